@@ -1,0 +1,33 @@
+"""CPU oracle for blockwise-scaled FP8 GEMM (1x128 activation groups, 128x128 weight blocks).
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package. The
+product path (``block_scaled_fp8_bfp8_amd``) never imports it, and this package
+imports nothing from the product path: the two share no code, tables or helpers.
+
+What is computed, and where it is defined on the pages:
+
+* e4m3fn codec (``e4m3``): the OCP float8 e4m3 "fn" format named by the vLLM
+  test on page "prhub.com.cn ... vllm/pull/49932" (section "关键源码片段": the
+  ``torch.float8_e4m3fn`` dtype and its ``finfo`` max of 448).
+* bf16 rounding (``bf16``): the bf16 output dtype of the same test and of the
+  ``gemm_fp8_fp8_bf16_nt`` kernel named on page "vllm-project/vllm/pull/19085".
+* per-token-group quantizer (``quant``): ``per_token_group_quant_fp8(x, 128)``
+  of the vLLM test and ``per_token_cast_to_fp8`` (gran_k=128, fp32 scale
+  factors) on page "transformers/integrations/deepgemm.py"
+  (``_select_fp8_cast_kwargs``, ``deepgemm_fp8_fp4_linear``).
+* blockwise GEMM (``gemm``): C[m,n] = sum_kb (A_q[m,kb] . B_q[n,kb]) * As[m,kb] * Bs[n//128,kb],
+  the ``native_w8a8_block_matmul`` reference of the vLLM test, with the
+  1x128 / 128x128 block contract of its "实现拆解" list item 2.
+* M-grouped contiguous GEMM (``gemm.grouped_gemm_contiguous_ref``): page
+  "transformers/integrations/deepgemm.py", ``_build_deepgemm_contiguous_layout``
+  (per-row expert id, -1 on padding rows) and ``deepgemm_fp8_fp4_experts_forward``.
+
+Every function is pinned by tests under ``tests/test_oracle_*.py`` (library
+routines, brute force with exact rationals, closed forms and invariants); none
+is "parity unpinned".
+"""
+
+from . import bf16, e4m3, gemm, quant  # noqa: F401
+
+__all__ = ["bf16", "e4m3", "gemm", "quant"]
