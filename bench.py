@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise-scaled FP8 GEMM hot path on one MI355X.
+
+Workload: the N = K = 4096 sweep over M in {1, 8, 9, 16, 24, 32, 64, 128, 160, 192, 224,
+256, 512, 1024, 2048, 4096, 8192} (the M sweep of page "lmdeploy/pull/4830", section
+"Performance"). Inputs are seeded synthetic data with the distributions of the vLLM
+test on page "prhub.com.cn ... vllm/pull/49932": fp32 activations U(-448, 448) and
+e4m3 weights (U(-448, 448) clamped and cast) with 128x128 float32 block scales
+U(0, 1e-2).
+
+One step = for every M of the sweep: quantize the activations per 1x128 group
+(bfp8_quant_act) and run the blockwise GEMM (bfp8_gemm), i.e. one pass of the whole
+hot path per M. `value` is the sweep's total GEMM FLOPs (2 M N K summed over M)
+divided by the measured time per step (quantization included), in TFLOP/s.
+
+Cold mode (default) rotates among copies of the weights totalling more than twice
+the 256 MB last-level cache, so every GEMM reads its weights from HBM; warm mode
+reuses one copy (the pages' "identical preallocated inputs").
+
+Also reported (same JSON line):
+  * roofline: the dominant kernel (the M = 8192 GEMM) against the dense FP8 matrix
+    peak, timed with HIP events around its launches on the launch stream;
+  * per_m: per-shape GEMM latency (p50 of 5 trials), TFLOP/s and the fraction of
+    the HBM (M <= 256) or FP8 (M >= 512) roofline, plus the quantizer's GB/s;
+  * cpu_baseline: the CPU oracle on a bounded sample of the same sweep.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix throughput
+N = K = 4096
+SWEEP_M = (1, 8, 9, 16, 24, 32, 64, 128, 160, 192, 224, 256, 512, 1024, 2048, 4096, 8192)
+DOMINANT_M = 8192
+LLC_BYTES = 256 * 2**20
+KERNEL_SOURCES = ["api.hip", "quant_act.hip", "gemm_small.hip", "gemm_tiled.hip", "device_common.h", "launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def gemm_alg_bytes(m: int, n: int = N, k: int = K) -> int:
+    """A + As + B + Bs + C, each touched once."""
+    kb = k // 128
+    return n * k + (-(-n // 128)) * kb * 4 + m * k + m * kb * 4 + 2 * m * n
+
+
+def quant_alg_bytes(m: int, k: int = K, in_bytes: int = 4) -> int:
+    return m * k * in_bytes + m * k + m * (k // 128) * 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_scaled_fp8_bfp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(rows_cap: int = 4096):
+    """The oracle on a bounded sample of the sweep: every M, first min(M, rows_cap) rows."""
+    import numpy as np
+
+    import workloads
+    from oracle import gemm as ogemm
+    from oracle import quant as oquant
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    w = workloads.square_weight()
+    bq, bs = w.q.numpy(), w.s.numpy()
+    flops = 0.0
+    t0 = time.perf_counter()
+    for m in SWEEP_M:
+        rows = min(m, rows_cap)
+        x = workloads.square_act(m)[:rows].numpy()
+        q, s = oquant.quant_act_ref(x)
+        ogemm.gemm_ref(q, s, bq, bs)
+        flops += 2.0 * rows * N * K
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"N=K=4096 sweep, every M with rows capped at {rows_cap} "
+                  f"({flops / 1e9:.0f} GFLOP incl. quantization), float64 numpy/BLAS, {dt:.1f} s",
+        "cpu": platform.processor() or platform.machine(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
+    ap.add_argument("--no-table", action="store_true", help="skip the per-M latency table")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-m", type=int, default=0, help="profile helper: run only this M (steps of GEMM+quant)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 256 MiB device copy (for counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
+            "run with --gpus 1.")
+        return 2
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        log("bench.py runs as a single process on one GPU")
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_scaled_fp8_bfp8_amd as bfp8
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sweep = (args.only_m,) if args.only_m else SWEEP_M
+
+    # ---- inputs, resident in HBM before any timing -------------------------------------
+    w = workloads.square_weight()
+    copies = 1 if args.mode == "warm" else max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+    bq = [w.q.to(dev) for _ in range(copies)]
+    bsc = [w.s.to(dev) for _ in range(copies)]
+    xs = {m: workloads.square_act(m).to(dev) for m in sweep}
+    qs = {m: torch.empty((m, K), dtype=torch.uint8, device=dev) for m in sweep}
+    ss = {m: torch.empty((K // 128, m), dtype=torch.float32, device=dev).t() for m in sweep}
+    cs = {m: torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in sweep}
+    torch.cuda.synchronize()
+    log(f"inputs ready: {copies} weight copies ({copies * N * K / 2**20:.0f} MiB), mode={args.mode}")
+
+    rot = [0]
+
+    def step(dom_events=None):
+        for m in sweep:
+            bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
+            i = rot[0] % copies
+            rot[0] += 1
+            if dom_events is not None and m == DOMINANT_M:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
+                e1.record(stream)
+                dom_events.append((e0, e1))
+            else:
+                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
+
+    if args.copy_calibration:
+        src = torch.ones(256 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 256 MiB device-to-device copy done")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    dom_events = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(dom_events)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / max(args.steps, 1)
+    flops_per_step = sum(2.0 * m * N * K for m in sweep)
+    value = flops_per_step / (ms_per_step * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s (quantization included)")
+
+    roofline = None
+    if dom_events:
+        dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_events]))
+        achieved = 2.0 * DOMINANT_M * N * K / (dom_ms * 1e-3) / 1e12
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("source_hash") == kernel_source_hash() and tr.get("m") == DOMINANT_M:
+                traffic = tr.get("bytes_per_launch")
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                    "kernel": f"bfp8_gemm M={DOMINANT_M} N={N} K={K} schedule={bfp8.schedule_for(DOMINANT_M, N, K)}",
+                    "avg_launch_us": round(dom_ms * 1e3, 2), "launches": len(dom_events)}
+
+    # ---- per-M table (page 1's protocol, shortened: warmup, then 5 trials, p50) -----------
+    per_m = {}
+    if not args.no_table:
+        for m in sweep:
+            def gemm_once():
+                i = rot[0] % copies
+                rot[0] += 1
+                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
+
+            def quant_once():
+                bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
+
+            res = {}
+            for name, fn in (("gemm", gemm_once), ("quant", quant_once)):
+                # size a trial to ~10 ms of work
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per = max(e0.elapsed_time(e1) / 5, 1e-3)
+                reps = int(min(max(10.0 / per, 10), 2000))
+                trials = []
+                for _ in range(5):
+                    e0.record(stream)
+                    for _ in range(reps):
+                        fn()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    trials.append(e0.elapsed_time(e1) * 1e3 / reps)
+                res[name] = float(np.median(trials))
+            us = res["gemm"]
+            tflops = 2.0 * m * N * K / (us * 1e-6) / 1e12
+            gbs = gemm_alg_bytes(m) / (us * 1e-6) / 1e9
+            hbm_bound = m <= 256
+            frac = gbs / PEAK_HBM_GBS if hbm_bound else tflops / PEAK_FP8_TFLOPS
+            qgbs = quant_alg_bytes(m) / (res["quant"] * 1e-6) / 1e9
+            per_m[str(m)] = {"gemm_us": round(us, 2), "tflops": round(tflops, 1), "alg_gbs": round(gbs, 1),
+                             "bound": "hbm" if hbm_bound else "mfma", "frac": round(frac, 4),
+                             "schedule": bfp8.schedule_for(m, N, K), "quant_us": round(res["quant"], 2),
+                             "quant_gbs": round(qgbs, 1)}
+            log(f"M={m:5d}  gemm {us:8.2f} us  {tflops:8.1f} TFLOP/s  {gbs:7.1f} GB/s  "
+                f"{'HBM' if hbm_bound else 'FP8'} frac {frac:.3f}  [{per_m[str(m)]['schedule']}]   "
+                f"quant {res['quant']:7.2f} us {qgbs:7.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.only_m:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "blocked-FP8 GEMM µs + TFLOP/s, N=K=4096, M=1..8192; % HBM/MFMA roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded; fp32 activations U(-448,448), e4m3 weights, 128x128 fp32 scales U(0,1e-2))",
+        "config": {"workload": "blockwise FP8 GEMM sweep N=K=4096, M in {1..8192}; per-1x128 activation "
+                               "quantization + GEMM per M",
+                   "n": N, "k": K, "m": list(sweep), "mode": args.mode, "weight_copies": copies},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_m": per_m,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out, ensure_ascii=False), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

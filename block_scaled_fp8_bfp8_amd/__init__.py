@@ -1,0 +1,185 @@
+"""Blockwise-scaled FP8 GEMM for AMD MI355X (gfx950): Python binding of libbfp8.so.
+
+Thin layer over the C ABI in include/bfp8.h: it allocates outputs with torch on
+the current device and stream, passes pointers, sizes and the stream handle,
+and maps status codes to exceptions (ValueError for invalid or misaligned
+arguments, NotImplementedError for unsupported requests, RuntimeError for device
+and launch failures). Every step of the computation runs in the HIP kernels;
+there is no fallback path.
+
+    q, s = quant_act(x)                 # x: [M, K] fp32 or bf16 (cuda)
+    c = gemm(q, s, w_q, w_s)            # c: [M, N] bf16
+    c = grouped_gemm_contiguous(q, s, w_q, w_s, layout)
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import SCHEDULES, LibraryMissing  # noqa: F401
+
+__all__ = [
+    "quant_act", "gemm", "grouped_gemm_contiguous", "set_schedule", "get_schedule", "schedule_for",
+    "abi_version", "BfpError", "LibraryMissing",
+]
+
+
+class BfpError(RuntimeError):
+    pass
+
+
+def _raise(status: int, what: str):
+    lib = _native.lib()
+    msg = lib.bfp8_last_error_message().decode()
+    name = lib.bfp8_status_string(status).decode()
+    text = f"{what}: {name}: {msg}"
+    if status in (_native.BFP8_ERR_INVALID_ARGUMENT, _native.BFP8_ERR_MISALIGNED, _native.BFP8_ERR_WORKSPACE):
+        raise ValueError(text)
+    if status == _native.BFP8_ERR_UNSUPPORTED:
+        raise NotImplementedError(text)
+    raise BfpError(text)
+
+
+def _check(status: int, what: str):
+    if status != _native.BFP8_OK:
+        _raise(status, what)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype, dims: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must be {dims}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+
+
+def _as_u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    """FP8 codes may be passed as uint8 or float8_e4m3fn (same bytes)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    return t
+
+
+def abi_version() -> int:
+    return _native.lib().bfp8_abi_version()
+
+
+def quant_act(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Per-token-group FP8 quantization of x [M, K] (fp32 or bf16, row stride may exceed K).
+
+    Returns (q, s): q uint8 e4m3fn codes [M, K]; s float32 [M, K/128], stored group-major
+    (s.stride() == (1, M)), i.e. the "column-major" activation scales the GEMM reads.
+    """
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise NotImplementedError(f"quant_act takes float32 or bfloat16 input, got {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    if x.stride(1) != 1:
+        raise ValueError("x must be K-contiguous")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((k // 128 if k % 128 == 0 else -(-k // 128), m), dtype=torch.float32,
+                             device=x.device).t()
+    _require(q, "q", torch.uint8, 2)
+    _require(scales, "scales", torch.float32, 2)
+    if q.stride(1) != 1 or scales.stride(0) != 1:
+        raise ValueError("q must be K-contiguous and scales group-major (stride(0) == 1)")
+    dt = _native.BFP8_IN_F32 if x.dtype == torch.float32 else _native.BFP8_IN_BF16
+    st = _native.lib().bfp8_quant_act(x.data_ptr(), dt, m, k, x.stride(0), q.data_ptr(), q.stride(0),
+                                      scales.data_ptr(), scales.stride(1) if scales.dim() == 2 else m,
+                                      _stream(x.device))
+    _check(st, "bfp8_quant_act")
+    return q, scales
+
+
+def _scale_ld_as(a_s: torch.Tensor, m: int) -> int:
+    if a_s.stride(0) != 1 and m > 1:
+        raise ValueError("activation scales must be group-major: a_s.stride(0) == 1 (as quant_act returns)")
+    return a_s.stride(1) if a_s.size(1) > 1 else max(m, 1)
+
+
+def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] (bf16) = blockwise FP8 product of a_q [M, K] and b_q [N, K] with scales a_s [M, K/128]
+    (group-major) and b_s [ceil(N/128), K/128]."""
+    a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
+    _require(a_q, "a_q", torch.uint8, 2)
+    _require(b_q, "b_q", torch.uint8, 2)
+    _require(a_s, "a_s", torch.float32, 2)
+    _require(b_s, "b_s", torch.float32, 2)
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    if b_q.shape[1] != k:
+        raise ValueError(f"a_q and b_q disagree on K: {k} vs {b_q.shape[1]}")
+    if a_q.stride(1) != 1 or b_q.stride(1) != 1 or b_s.stride(1) != 1:
+        raise ValueError("a_q, b_q and b_s must be contiguous along K")
+    if tuple(a_s.shape) != (m, -(-k // 128)) or tuple(b_s.shape) != (-(-n // 128), -(-k // 128)):
+        raise ValueError(f"scale shapes {tuple(a_s.shape)}, {tuple(b_s.shape)} do not match M={m}, N={n}, K={k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    _require(out, "out", torch.bfloat16, 2)
+    if out.stride(1) != 1:
+        raise ValueError("out must be contiguous along N")
+    st = _native.lib().bfp8_gemm(a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m),
+                                 b_q.data_ptr(), b_q.stride(0), b_s.data_ptr(), b_s.stride(0),
+                                 out.data_ptr(), out.stride(0), m, n, k, None, 0, _stream(a_q.device))
+    _check(st, "bfp8_gemm")
+    return out
+
+
+def grouped_gemm_contiguous(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+                            layout: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """M-grouped contiguous product: row m uses expert layout[m] (int32; -1 = padding, not written).
+
+    a_q [M, K] (M % 128 == 0), a_s [M, K/128] group-major, b_q [G, N, K], b_s [G, ceil(N/128), K/128]."""
+    a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
+    _require(a_q, "a_q", torch.uint8, 2)
+    _require(b_q, "b_q", torch.uint8, 3)
+    _require(a_s, "a_s", torch.float32, 2)
+    _require(b_s, "b_s", torch.float32, 3)
+    _require(layout, "layout", torch.int32, 1)
+    m, k = a_q.shape
+    g, n, k2 = b_q.shape
+    if k2 != k or layout.shape[0] != m:
+        raise ValueError("shape mismatch between a_q, b_q and layout")
+    if not (b_q.is_contiguous() and b_s.is_contiguous() and layout.is_contiguous()):
+        raise ValueError("b_q, b_s and layout must be contiguous")
+    if tuple(b_s.shape) != (g, -(-n // 128), -(-k // 128)) or tuple(a_s.shape) != (m, -(-k // 128)):
+        raise ValueError("scale shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    _require(out, "out", torch.bfloat16, 2)
+    st = _native.lib().bfp8_grouped_gemm_contiguous(
+        a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m), b_q.data_ptr(), b_q.stride(1),
+        b_s.data_ptr(), b_s.stride(1), layout.data_ptr(), g, out.data_ptr(), out.stride(0), m, n, k, None, 0,
+        _stream(a_q.device))
+    _check(st, "bfp8_grouped_gemm_contiguous")
+    return out
+
+
+def set_schedule(name: str) -> None:
+    """Force a GEMM schedule ('small_m', 'tiled') or restore the automatic choice ('auto')."""
+    if name not in SCHEDULES:
+        raise ValueError(f"unknown schedule {name!r}; choose from {sorted(SCHEDULES)}")
+    _check(_native.lib().bfp8_set_schedule(SCHEDULES[name]), "bfp8_set_schedule")
+
+
+def get_schedule() -> str:
+    v = _native.lib().bfp8_get_schedule()
+    return {v_: k_ for k_, v_ in SCHEDULES.items()}[v]
+
+
+def schedule_for(m: int, n: int, k: int) -> str:
+    v = _native.lib().bfp8_gemm_schedule_for(m, n, k)
+    return {v_: k_ for k_, v_ in SCHEDULES.items()}[v]

@@ -1,0 +1,61 @@
+"""ctypes declarations of libbfp8.so's C ABI (include/bfp8.h). Loading only; no computation."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libbfp8.so")
+
+BFP8_OK = 0
+BFP8_ERR_INVALID_ARGUMENT = 1
+BFP8_ERR_UNSUPPORTED = 2
+BFP8_ERR_MISALIGNED = 3
+BFP8_ERR_WORKSPACE = 4
+BFP8_ERR_DEVICE = 5
+BFP8_ERR_LAUNCH = 6
+
+BFP8_IN_F32 = 0
+BFP8_IN_BF16 = 1
+
+SCHEDULES = {"auto": 0, "small_m": 1, "tiled": 2}
+
+# Every symbol include/bfp8.h declares: (name, restype, argtypes)
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = [
+    ("bfp8_abi_version", ctypes.c_int, []),
+    ("bfp8_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("bfp8_last_error_message", ctypes.c_char_p, []),
+    ("bfp8_quant_act", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    ("bfp8_gemm_workspace_bytes", _sz, [_i64, _i64, _i64]),
+    ("bfp8_gemm", ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_grouped_gemm_contiguous", ctypes.c_int,
+     [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_set_schedule", ctypes.c_int, [ctypes.c_int]),
+    ("bfp8_get_schedule", ctypes.c_int, []),
+    ("bfp8_gemm_schedule_for", ctypes.c_int, [_i64, _i64, _i64]),
+]
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libbfp8.so (raises LibraryMissing if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                f"{LIB_PATH} is missing: build it with `python -m block_scaled_fp8_bfp8_amd.build` "
+                "(there is no fallback implementation)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, restype, argtypes in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = restype
+            fn.argtypes = argtypes
+        _lib = handle
+    return _lib

@@ -1,0 +1,204 @@
+// C ABI of libbfp8 (declared in include/bfp8.h): argument validation, device
+// check, schedule choice and launch. No allocation, no host<->device copies.
+//
+// Validation happens entirely on the host before any HIP call, so a rejected
+// call touches no buffer; each rejection states its reason through
+// bfp8_last_error_message() (the "can_implement returns an explicit reason"
+// contract of page "prhub.com.cn ... vllm/pull/49932", section "实现拆解" item 2).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/bfp8.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_message;
+std::atomic<int> g_schedule{BFP8_SCHED_AUTO};
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bfp8_status_t fail(bfp8_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_message = buf;
+  return st;
+}
+
+bfp8_status_t ok() {
+  g_message.clear();
+  return BFP8_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel row index in int32
+
+// Device check: the current device must be a gfx950. Cached per device id.
+bfp8_status_t check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BFP8_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BFP8_ERR_DEVICE, "device id %d out of range", dev);
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(BFP8_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+    if (st == 2) return fail(BFP8_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
+                             prop.gcnArchName);
+  }
+  if (st == 2) return fail(BFP8_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  return BFP8_OK;
+}
+
+bfp8_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BFP8_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Shared checks of the dense and grouped GEMM arguments.
+bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
+                              int64_t ldb, const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes) {
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
+  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
+  if (K % bfp8::kBlock != 0)
+    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128 (only whole 128-wide scale blocks)",
+                (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(BFP8_ERR_UNSUPPORTED, "M, N and K must each be at most 2^30");
+  if (!b || !bs) return fail(BFP8_ERR_INVALID_ARGUMENT, "b and bs must not be NULL");
+  if (M > 0 && (!a || !as || !c)) return fail(BFP8_ERR_INVALID_ARGUMENT, "a, as and c must not be NULL when M > 0");
+  if (lda < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "lda = %lld < K = %lld", (long long)lda, (long long)K);
+  if (ldb < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldb = %lld < K = %lld", (long long)ldb, (long long)K);
+  if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
+  if (ld_bs < K / bfp8::kBlock)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_bs = %lld < K/128 = %lld", (long long)ld_bs,
+                (long long)(K / bfp8::kBlock));
+  if (ldc < N) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldc = %lld < N = %lld", (long long)ldc, (long long)N);
+  if (lda % 16 || ldb % 16) return fail(BFP8_ERR_MISALIGNED, "lda and ldb must be multiples of 16 bytes");
+  if (!aligned(a, 16) || !aligned(b, 16)) return fail(BFP8_ERR_MISALIGNED, "a and b must be 16-byte aligned");
+  if (!aligned(as, 4) || !aligned(bs, 4)) return fail(BFP8_ERR_MISALIGNED, "as and bs must be 4-byte aligned");
+  if (!aligned(c, 2)) return fail(BFP8_ERR_MISALIGNED, "c must be 2-byte aligned");
+  const size_t need = bfp8_gemm_workspace_bytes(M, N, K);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  return BFP8_OK;
+}
+
+int choose_schedule(int64_t M, int64_t /*N*/, int64_t /*K*/) {
+  const int forced = g_schedule.load(std::memory_order_relaxed);
+  if (forced != BFP8_SCHED_AUTO) return forced;
+  return M <= bfp8::kSmallMaxM ? BFP8_SCHED_SMALL_M : BFP8_SCHED_TILED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bfp8_abi_version(void) { return BFP8_ABI_VERSION; }
+
+const char* bfp8_status_string(bfp8_status_t status) {
+  switch (status) {
+    case BFP8_OK: return "BFP8_OK";
+    case BFP8_ERR_INVALID_ARGUMENT: return "BFP8_ERR_INVALID_ARGUMENT";
+    case BFP8_ERR_UNSUPPORTED: return "BFP8_ERR_UNSUPPORTED";
+    case BFP8_ERR_MISALIGNED: return "BFP8_ERR_MISALIGNED";
+    case BFP8_ERR_WORKSPACE: return "BFP8_ERR_WORKSPACE";
+    case BFP8_ERR_DEVICE: return "BFP8_ERR_DEVICE";
+    case BFP8_ERR_LAUNCH: return "BFP8_ERR_LAUNCH";
+  }
+  return "BFP8_UNKNOWN_STATUS";
+}
+
+const char* bfp8_last_error_message(void) { return g_message.c_str(); }
+
+bfp8_status_t bfp8_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* as, int64_t ld_as, void* stream) {
+  if (x_dtype != BFP8_IN_F32 && x_dtype != BFP8_IN_BF16)
+    return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is neither BFP8_IN_F32 nor BFP8_IN_BF16", x_dtype);
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
+  if (K % bfp8::kBlock != 0)
+    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128", (long long)K);
+  if (M > kMaxDim || K > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M and K must each be at most 2^30");
+  if (M == 0) return ok();
+  if (!x || !q || !as) return fail(BFP8_ERR_INVALID_ARGUMENT, "x, q and as must not be NULL");
+  if (ldx < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldq < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldq = %lld < K = %lld", (long long)ldq, (long long)K);
+  if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
+  const int64_t esize = x_dtype == BFP8_IN_F32 ? 4 : 2;
+  if ((ldx * esize) % 16 || ldq % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(BFP8_ERR_MISALIGNED, "x and q must be 16-byte aligned");
+  if (!aligned(as, 4)) return fail(BFP8_ERR_MISALIGNED, "as must be 4-byte aligned");
+  bfp8_status_t st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, (hipStream_t)stream),
+                  "quant_act");
+}
+
+size_t bfp8_gemm_workspace_bytes(int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) { return 0; }
+
+bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b, int64_t ldb,
+                        const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
+                                     workspace_bytes);
+  if (st != BFP8_OK) return st;
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  const bfp8::GemmArgs args{a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, (int)M, (int)N, (int)K, nullptr, 1};
+  const int sched = choose_schedule(M, N, K);
+  if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_small(args, (hipStream_t)stream), "gemm_small");
+  return launched(bfp8::launch_gemm_tiled(args, (hipStream_t)stream), "gemm_tiled");
+}
+
+bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                                           const int32_t* grouped_layout, int32_t G, uint16_t* c, int64_t ldc,
+                                           int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
+                                     workspace_bytes);
+  if (st != BFP8_OK) return st;
+  if (G < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "G = %d must be >= 1", (int)G);
+  if (M % bfp8::kBlock != 0)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is not a multiple of the 128-row group alignment",
+                (long long)M);
+  if (M > 0 && !grouped_layout) return fail(BFP8_ERR_INVALID_ARGUMENT, "grouped_layout must not be NULL");
+  if (!aligned(grouped_layout, 4)) return fail(BFP8_ERR_MISALIGNED, "grouped_layout must be 4-byte aligned");
+  if ((int64_t)G * N * ldb > ((int64_t)1 << 40)) return fail(BFP8_ERR_UNSUPPORTED, "G * N * ldb too large");
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  const bfp8::GemmArgs args{a,   lda, as,     ld_as,  b,      ldb,           bs, ld_bs,
+                            c,   ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G};
+  return launched(bfp8::launch_grouped_tiled(args, (hipStream_t)stream), "grouped_gemm_tiled");
+}
+
+bfp8_status_t bfp8_set_schedule(int schedule) {
+  if (schedule < BFP8_SCHED_AUTO || schedule >= BFP8_SCHED_COUNT_)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "unknown schedule %d", schedule);
+  g_schedule.store(schedule, std::memory_order_relaxed);
+  return ok();
+}
+
+int bfp8_get_schedule(void) { return g_schedule.load(std::memory_order_relaxed); }
+
+int bfp8_gemm_schedule_for(int64_t M, int64_t N, int64_t K) { return choose_schedule(M, N, K); }
+
+}  // extern "C"

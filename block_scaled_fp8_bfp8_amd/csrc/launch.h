@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (internal to libbfp8; arguments are
+// validated by the C-ABI layer before any of these is called).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bfp8 {
+
+constexpr int kBlock = 128;  // K block of the scale grid, also the N block of the weight scales
+
+constexpr int kInF32 = 0;
+constexpr int kInBf16 = 1;
+
+struct GemmArgs {
+  const uint8_t* a;  // [M][lda] e4m3 activations
+  int64_t lda;
+  const float* as;  // [K/128][ld_as] activation scales (group-major)
+  int64_t ld_as;
+  const uint8_t* b;  // [G][N][ldb] e4m3 weights (G = 1 for the dense GEMM)
+  int64_t ldb;
+  const float* bs;  // [G][ceil(N/128)][ld_bs] weight block scales
+  int64_t ld_bs;
+  uint16_t* c;  // [M][ldc] bf16 output
+  int64_t ldc;
+  int M, N, K;
+  const int32_t* layout;  // grouped GEMM only: [M] group id per row, -1 = padding
+  int G;
+};
+
+hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                            int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
+
+// Largest M the small-M schedule covers in one pass over the weights.
+constexpr int kSmallMaxM = 64;
+
+hipError_t launch_gemm_small(const GemmArgs& args, hipStream_t stream);
+hipError_t launch_gemm_tiled(const GemmArgs& args, hipStream_t stream);
+hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream);
+
+}  // namespace bfp8

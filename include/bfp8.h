@@ -1,0 +1,197 @@
+/*
+ * bfp8 — blockwise-scaled FP8 GEMM for AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * C ABI of libbfp8.so. Every entry point takes plain device pointers, sizes and
+ * a HIP stream (passed as void*, NULL = the null stream); no PyTorch or C++
+ * types cross this boundary and no exception leaves it.
+ *
+ * The method (DeepSeek-style blockwise FP8 "W8A8"):
+ *   C[m, n] = sum_kb (A_q[m, kb-block] . B_q[n, kb-block]) * As[m, kb] * Bs[n/128, kb]
+ * with e4m3fn operands, 1x128 per-token-group activation scales, 128x128 weight
+ * block scales, FP32 accumulation and bf16 output. Sources:
+ *   - page "prhub.com.cn ... vllm/pull/49932" (torch._scaled_mm block-scale
+ *     backend): section "实现拆解" items 2-3 fix the 1x128 activation group and the
+ *     128x128 weight block, the column-major (M-major) activation scales and the
+ *     call shape _scaled_mm(A, B.t(), scale_a=As, scale_b=Bs.t()); its test
+ *     source (section "关键源码片段") fixes e4m3fn operands, fp32 scales of shapes
+ *     [M, ceil(K/128)] and [ceil(N/128), ceil(K/128)], bf16 output and the
+ *     acceptance metric mean|C - ref| / mean|ref| < 1e-3.
+ *   - page "vllm-project/vllm/pull/19085": the dense kernel gemm_fp8_fp8_bf16_nt
+ *     ("NT": both operands K-contiguous).
+ *   - page "transformers/integrations/deepgemm.py": per_token_cast_to_fp8 with
+ *     gran_k = 128 and float32 scale factors (_select_fp8_cast_kwargs), the
+ *     caller-allocated output of deepgemm_fp8_fp4_linear, and the M-grouped
+ *     contiguous layout (_build_deepgemm_contiguous_layout: 128-row alignment,
+ *     one int32 expert id per row, -1 on padding rows).
+ *   - page "lmdeploy/pull/4830" (Gluon blocked FP8 GEMM), section "Kernel
+ *     design": the schedule is chosen by M (small / mid / large M).
+ *
+ * Conventions shared by all entry points
+ *   - Ownership: the caller allocates and owns every buffer (inputs, outputs,
+ *     workspace). The library never allocates, frees or copies between host
+ *     and device; it keeps only per-device cached properties.
+ *   - Asynchrony: work is enqueued on `stream`; BFP8_OK means "enqueued".
+ *     Errors in the arguments are found on the host before any HIP call and
+ *     leave every buffer untouched.
+ *   - M == 0 is a valid no-op (BFP8_OK, nothing launched).
+ *   - Alignment: every uint8 operand pointer and every row stride in bytes is
+ *     a multiple of 16; float pointers are 4-byte aligned; bf16 output
+ *     pointers are 2-byte aligned. Violations return BFP8_ERR_MISALIGNED.
+ *   - K must be a positive multiple of 128 (the scale grid's K blocks are then
+ *     whole); other K return BFP8_ERR_UNSUPPORTED.
+ *   - Only gfx950 devices are supported (BFP8_ERR_UNSUPPORTED otherwise).
+ *   - Determinism: for fixed inputs and sizes every result is bitwise identical
+ *     from run to run (fixed reduction orders, no floating-point atomics).
+ *   - Thread safety: calls may be made from several host threads; the message
+ *     returned by bfp8_last_error_message() is per host thread.
+ */
+#ifndef BFP8_H_
+#define BFP8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BFP8_ABI_VERSION 1
+
+typedef enum bfp8_status {
+  BFP8_OK = 0,
+  BFP8_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative or inconsistent size or stride */
+  BFP8_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement (K % 128, arch, dtype) */
+  BFP8_ERR_MISALIGNED = 3,       /* pointer or stride alignment (see conventions) */
+  BFP8_ERR_WORKSPACE = 4,        /* workspace smaller than bfp8_gemm_workspace_bytes() */
+  BFP8_ERR_DEVICE = 5,           /* HIP runtime query failed */
+  BFP8_ERR_LAUNCH = 6            /* kernel launch failed (message holds hipGetErrorString) */
+} bfp8_status_t;
+
+/* Activation dtypes accepted by bfp8_quant_act. */
+typedef enum bfp8_in_dtype {
+  BFP8_IN_F32 = 0,
+  BFP8_IN_BF16 = 1
+} bfp8_in_dtype_t;
+
+/* GEMM schedules (page "lmdeploy/pull/4830", section "Kernel design": one schedule
+ * per M range). AUTO picks by M and shape; the others force one schedule at any M
+ * (for tests and benchmarks). Each schedule is deterministic on its own; the
+ * schedules sum the K blocks in different orders, so they agree to FP32
+ * rounding, not bitwise. */
+typedef enum bfp8_schedule {
+  BFP8_SCHED_AUTO = 0,
+  BFP8_SCHED_SMALL_M = 1, /* weight-streaming, K split across the waves of a workgroup */
+  BFP8_SCHED_TILED = 2,   /* LDS-tiled MFMA kernel, one output tile per workgroup */
+  BFP8_SCHED_COUNT_ = 3
+} bfp8_schedule_t;
+
+/* Returns BFP8_ABI_VERSION of the loaded library. */
+int bfp8_abi_version(void);
+
+/* Static string naming a status code (never NULL). */
+const char* bfp8_status_string(bfp8_status_t status);
+
+/* Why the calling thread's last failing call failed ("" after success). The
+ * pointer stays valid until the thread's next bfp8 call. */
+const char* bfp8_last_error_message(void);
+
+/*
+ * Per-token-group FP8 quantization of activations.
+ * Source: page "prhub.com.cn ... vllm/pull/49932", test source
+ * (per_token_group_quant_fp8(A, 128, column_major_scales=True)); page
+ * "transformers/integrations/deepgemm.py", per_token_cast_to_fp8 with gran_k=128
+ * and float32 scale factors.
+ *
+ * For every row m and group g (columns 128g .. 128g+127):
+ *   s        = fl32(max(max_k |x[m,k]|, 1e-10) / 448)      (correctly rounded divide)
+ *   q[m,k]   = e4m3fn_RNE(clamp(fl32(x[m,k] / s), -448, 448))
+ *   as[g*ld_as + m] = s
+ * x is widened to float32 first (exact for bf16).
+ *
+ *   x       device, [M][ldx] elements of x_dtype, row-major; read only
+ *   x_dtype BFP8_IN_F32 or BFP8_IN_BF16
+ *   M, K    M >= 0, K > 0 and K % 128 == 0
+ *   ldx     >= K, elements; ldx * sizeof(element) % 16 == 0; x 16-byte aligned
+ *   q       device, [M][ldq] bytes (e4m3fn codes); ldq >= K, ldq % 16 == 0; written
+ *   as      device, [K/128][ld_as] float32, group-major ("column-major" scales:
+ *           scale of row m, group g at as[g*ld_as + m]); ld_as >= M; written
+ *   stream  hipStream_t or NULL
+ * x may not overlap q or as.
+ */
+bfp8_status_t bfp8_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* as, int64_t ld_as, void* stream);
+
+/* Bytes of workspace bfp8_gemm and bfp8_grouped_gemm_contiguous need for this
+ * shape (0 for every shape in this version; the argument is kept so that a
+ * schedule needing scratch can be added without an ABI change). */
+size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Dense blockwise-scaled FP8 GEMM, NT layout, bf16 output.
+ * Source: page "prhub.com.cn ... vllm/pull/49932", section "实现拆解" items 2-3 and
+ * the test source (native_w8a8_block_matmul as reference); page
+ * "vllm-project/vllm/pull/19085" (gemm_fp8_fp8_bf16_nt); page
+ * "transformers/integrations/deepgemm.py" (fp8_fp4_gemm_nt((a, sfa), (b, sfb), out)).
+ *
+ *   C[m, n] = bf16_RNE( sum_{kb < K/128} P_kb[m,n] * as[kb*ld_as + m] * bs[(n/128)*ld_bs + kb] )
+ *   P_kb[m, n] = sum_{k = 128 kb}^{128 kb + 127} e4m3(a[m*lda + k]) * e4m3(b[n*ldb + k])
+ * Each P_kb is accumulated in FP32 by the matrix cores and promoted into an FP32
+ * accumulator with the product of the two scales.
+ *
+ *   a      device, [M][lda] e4m3fn codes (activations), lda >= K, 16-byte aligned rows
+ *   as     device, [K/128][ld_as] float32 activation scales (group-major), ld_as >= M
+ *   b      device, [N][ldb] e4m3fn codes (weights, K-contiguous), ldb >= K, 16-byte aligned rows
+ *   bs     device, [ceil(N/128)][ld_bs] float32 weight block scales, ld_bs >= K/128
+ *   c      device, [M][ldc] bf16 bit patterns, ldc >= N; written (only columns < N)
+ *   M >= 0, N >= 1, K > 0 with K % 128 == 0
+ *   workspace / workspace_bytes: device scratch of at least
+ *          bfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0)
+ *   stream hipStream_t or NULL
+ * Inputs are read only; c may not overlap any input.
+ */
+bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                        const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * M-grouped contiguous blockwise FP8 GEMM (mixture-of-experts layers).
+ * Source: page "transformers/integrations/deepgemm.py": _build_deepgemm_contiguous_layout
+ * (rows of each expert padded to a multiple of 128; per-row int32 expert id, -1 on
+ * padding rows), deepgemm_fp8_fp4_experts_forward (m_grouped_fp8_fp4_gemm_nt_contiguous)
+ * and DeepGEMM.m_alignment (128).
+ *
+ * For every row m with g = grouped_layout[m] >= 0:
+ *   C[m, n] = the dense product above with b + g*N*ldb and bs + g*ceil(N/128)*ld_bs
+ * Rows with grouped_layout[m] == -1 are padding: their A, As and C contents are
+ * never used and C rows are not written.
+ *
+ *   a, as, c, lda, ld_as, ldc  as in bfp8_gemm, with M rows (M % 128 == 0)
+ *   b      device, [G][N][ldb] e4m3fn expert weights
+ *   bs     device, [G][ceil(N/128)][ld_bs] float32 block scales
+ *   grouped_layout device, int32 [M]; contract (not checked on the host: device
+ *          data): values in [-1, G), and all non-negative ids within one 128-row
+ *          block are equal. A block whose ids are all -1 is skipped; a block whose
+ *          largest id is >= G is skipped too (its rows are not written).
+ *   G >= 1
+ */
+bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                                           const int32_t* grouped_layout, int32_t G,
+                                           uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Process-wide schedule override for bfp8_gemm (tests and benchmarks):
+ * BFP8_SCHED_AUTO restores the automatic choice. Returns BFP8_ERR_INVALID_ARGUMENT
+ * for an unknown value. The grouped GEMM always uses the tiled schedule. */
+bfp8_status_t bfp8_set_schedule(int schedule);
+int bfp8_get_schedule(void);
+
+/* The schedule bfp8_gemm would run for this shape under the current override. */
+int bfp8_gemm_schedule_for(int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFP8_H_ */

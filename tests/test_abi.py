@@ -1,0 +1,179 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and rejects
+invalid arguments on the host before any HIP call (fake pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from block_scaled_fp8_bfp8_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bfp8.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bfp8_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _native.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    bound = {n for n, _, _ in _native.SIGNATURES}
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+        assert n in bound, f"{n} has no ctypes signature"
+    assert bound == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bfp8_abi_version() == 1
+    for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
+                       (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
+                       (6, b"BFP8_ERR_LAUNCH")]:
+        assert lib.bfp8_status_string(code) == name
+    assert lib.bfp8_status_string(99) == b"BFP8_UNKNOWN_STATUS"
+    assert lib.bfp8_gemm_workspace_bytes(4096, 4096, 4096) == 0
+
+
+A = 0x10000000  # fake, 256-byte aligned device addresses: validation never dereferences them
+AS = 0x20000000
+B = 0x30000000
+BS = 0x40000000
+C = 0x50000000
+
+
+def _gemm(lib, a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=2, c=C, ldc=64, M=8, N=64, K=256,
+          ws=None, wsb=0):
+    return lib.bfp8_gemm(a, lda, as_, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(N=0), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=200, lda=256, ldb=256), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(M=1 << 31), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(a=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(b=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(bs=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(c=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(lda=128), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ldb=255), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ld_as=7), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ld_bs=1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ldc=63), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(lda=264), _native.BFP8_ERR_MISALIGNED),
+    (dict(ldb=260), _native.BFP8_ERR_MISALIGNED),
+    (dict(a=A + 8), _native.BFP8_ERR_MISALIGNED),
+    (dict(b=B + 1), _native.BFP8_ERR_MISALIGNED),
+    (dict(as_=AS + 2), _native.BFP8_ERR_MISALIGNED),
+    (dict(bs=BS + 1), _native.BFP8_ERR_MISALIGNED),
+    (dict(c=C + 1), _native.BFP8_ERR_MISALIGNED),
+])
+def test_gemm_rejections(lib, kw, status):
+    st = _gemm(lib, **kw)
+    assert st == status, lib.bfp8_last_error_message()
+    assert len(lib.bfp8_last_error_message()) > 0
+
+
+def test_m_zero_is_ok_without_device(lib):
+    # M = 0 returns before any HIP call; a, as and c may be NULL
+    assert _gemm(lib, M=0, a=None, as_=None, c=None, ld_as=0) == _native.BFP8_OK
+    assert lib.bfp8_last_error_message() == b""
+
+
+def _quant(lib, x=A, dt=0, M=4, K=256, ldx=256, q=B, ldq=256, as_=AS, ld_as=4):
+    return lib.bfp8_quant_act(x, dt, M, K, ldx, q, ldq, as_, ld_as, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(M=-3), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=130, ldx=256, ldq=256), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(x=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ldx=255), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ldq=128), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ld_as=3), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ldx=258, dt=1), _native.BFP8_ERR_MISALIGNED),
+    (dict(ldq=264), _native.BFP8_ERR_MISALIGNED),
+    (dict(x=A + 4), _native.BFP8_ERR_MISALIGNED),
+    (dict(q=B + 8), _native.BFP8_ERR_MISALIGNED),
+    (dict(as_=AS + 1), _native.BFP8_ERR_MISALIGNED),
+])
+def test_quant_rejections(lib, kw, status):
+    assert _quant(lib, **kw) == status, lib.bfp8_last_error_message()
+
+
+def test_quant_m_zero_ok(lib):
+    assert _quant(lib, M=0, x=None, q=None, as_=None) == _native.BFP8_OK
+
+
+def _grouped(lib, a=A, lda=256, as_=AS, ld_as=128, b=B, ldb=256, bs=BS, ld_bs=2, lay=0x60000000, G=2, c=C,
+             ldc=64, M=128, N=64, K=256):
+    return lib.bfp8_grouped_gemm_contiguous(a, lda, as_, ld_as, b, ldb, bs, ld_bs, lay, G, c, ldc, M, N, K, None, 0,
+                                            None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=100, ld_as=128), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(G=0), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(lay=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(lay=0x60000002), _native.BFP8_ERR_MISALIGNED),
+    (dict(K=192), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(ldc=32), _native.BFP8_ERR_INVALID_ARGUMENT),
+])
+def test_grouped_rejections(lib, kw, status):
+    assert _grouped(lib, **kw) == status, lib.bfp8_last_error_message()
+
+
+def test_schedule_override(lib):
+    try:
+        assert lib.bfp8_set_schedule(7) == _native.BFP8_ERR_INVALID_ARGUMENT
+        assert lib.bfp8_get_schedule() == 0
+        assert lib.bfp8_gemm_schedule_for(1, 4096, 4096) == 1
+        assert lib.bfp8_gemm_schedule_for(4096, 4096, 4096) == 2
+        assert lib.bfp8_set_schedule(2) == 0
+        assert lib.bfp8_gemm_schedule_for(1, 4096, 4096) == 2
+    finally:
+        lib.bfp8_set_schedule(0)
+
+
+def _gpu_count():
+    import torch
+
+    return torch.cuda.device_count()
+
+
+@pytest.mark.skipif(_gpu_count() > 0, reason="a GPU is visible: a valid call with fake pointers would launch")
+def test_valid_call_without_gpu_reports_device_error(lib):
+    st = _gemm(lib)
+    assert st in (_native.BFP8_ERR_DEVICE, _native.BFP8_ERR_UNSUPPORTED), lib.bfp8_last_error_message()
+    assert b"hip" in lib.bfp8_last_error_message().lower() or b"device" in lib.bfp8_last_error_message().lower()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import block_scaled_fp8_bfp8_amd._native as n; n.LIB_PATH = '/nonexistent/libbfp8.so'\n"
+            "try:\n    n.lib()\nexcept n.LibraryMissing as e:\n    print('missing:', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert "missing:" in out.stdout and "no fallback" in out.stdout
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "block_scaled_fp8_bfp8_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

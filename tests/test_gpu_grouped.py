@@ -1,0 +1,114 @@
+"""GPU parity of bfp8_grouped_gemm_contiguous against the oracle (M-grouped contiguous MoE GEMM)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_bfp8_amd as bfp8
+import workloads
+from tests import tolerance
+from tests.gpu_util import announce, bits, quant_gpu_checked
+
+pytestmark = pytest.mark.gpu
+
+_moe = {}
+
+
+def _moe_on(dev):
+    if "case" not in _moe:
+        case = workloads.moe_case()
+        bq = torch.stack([w.q for w in case.weights])
+        bs = torch.stack([w.s for w in case.weights])
+        _moe["case"] = (case, bq, bs, bq.to(dev), bs.to(dev))
+    return _moe["case"]
+
+
+def _grouped(q, s, bq, bs, layout, what, out=None):
+    announce("grouped_gemm", what, tuple(q.shape), tuple(bq.shape))
+    c = bfp8.grouped_gemm_contiguous(q, s, bq, bs, layout, out=out)
+    torch.cuda.synchronize()
+    return c
+
+
+def _check_rows(c_bits, q_ref, s_ref, bq, bs, layout, rows_per_group, cols, what):
+    rng = np.random.default_rng(17)
+    k = q_ref.shape[1]
+    for g in np.unique(layout[layout >= 0]):
+        rows = np.nonzero(layout == g)[0]
+        rows = np.unique(np.concatenate([rows[:1], rows[-1:], rng.choice(rows, min(rows_per_group, rows.size),
+                                                                          replace=False)]))
+        _, _, ref_bits, mag = tolerance.reference(q_ref, s_ref, bq[g], bs[g], rows=rows, cols=cols)
+        tolerance.compare(c_bits[np.ix_(rows, cols)], ref_bits, mag, k, f"{what} expert {g}")
+
+
+def test_moe_config(gpu):
+    """16 experts, N=4096, K=7168, 4096 tokens with Dirichlet(1) counts, 128-row padding."""
+    case, bq, bs, bq_d, bs_d = _moe_on(gpu)
+    q, s, q_ref, s_ref = quant_gpu_checked(case.act, gpu, "moe activations")
+    layout = case.layout.numpy()
+    lay_d = case.layout.to(gpu)
+    sentinel = torch.full((layout.size, 4096), 1536.0, dtype=torch.bfloat16, device=gpu)
+    c = _grouped(q, s, bq_d, bs_d, lay_d, "moe config", out=sentinel)
+    cb = bits(c)
+    rng = np.random.default_rng(5)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(4032, 4096), rng.choice(4096, 400, replace=False)]))
+    _check_rows(cb, q_ref, s_ref, bq.numpy(), bs.numpy(), layout, 6, cols, "moe")
+    # padding rows are not written
+    pad = layout < 0
+    assert (c[torch.from_numpy(pad).to(gpu)].float().cpu() == 1536.0).all()
+
+
+def test_poisoned_padding_rows_and_empty_blocks(gpu):
+    """Padding rows full of NaN codes and NaN scales, plus a trailing all-padding block: valid rows
+    are bitwise unchanged and no padding row is written."""
+    g_count, n, k = 3, 384, 512
+    counts = np.array([130, 0, 45])
+    layout = workloads.moe_layout(counts)
+    layout = np.concatenate([layout, np.full(128, -1, np.int32)])  # a block of padding only
+    m = layout.size
+    ws = [workloads.weight(n, k, seed=900 + g) for g in range(g_count)]
+    bq = torch.stack([w.q for w in ws])
+    bs = torch.stack([w.s for w in ws])
+    x = workloads.act_normal_bf16(m, k, seed=77)
+    q, s, q_ref, s_ref = quant_gpu_checked(x, gpu, "grouped small")
+    bq_d, bs_d, lay_d = bq.to(gpu), bs.to(gpu), torch.from_numpy(layout).to(gpu)
+    c_clean = _grouped(q, s, bq_d, bs_d, lay_d, "clean").clone()
+    pad = torch.from_numpy(layout < 0).to(gpu)
+    q_p = q.clone()
+    q_p[pad] = 0x7F
+    s_p = s.clone()
+    s_p[pad] = float("nan")
+    out = torch.full((m, n), -3.0, dtype=torch.bfloat16, device=gpu)
+    c_p = _grouped(q_p, s_p, bq_d, bs_d, lay_d, "poisoned", out=out)
+    valid = ~pad
+    assert torch.equal(c_p[valid].view(torch.int16), c_clean[valid].view(torch.int16))
+    assert (c_p[pad].float() == -3.0).all()
+    _check_rows(bits(c_clean), q_ref, s_ref, bq.numpy(), bs.numpy(), layout, 200, np.arange(n), "grouped small")
+
+
+def test_single_group_equals_dense_tiled(gpu):
+    """G = 1 with no padding is the dense product; both run the tiled schedule, so bitwise equal."""
+    w = workloads.weight(640, 1024, seed=31)
+    x = workloads.act_normal_bf16(256, 1024, seed=32)
+    q, s, _, _ = quant_gpu_checked(x, gpu, "single group")
+    bq_d, bs_d = w.q.to(gpu), w.s.to(gpu)
+    lay = torch.zeros(256, dtype=torch.int32, device=gpu)
+    c_g = _grouped(q, s, bq_d[None], bs_d[None], lay, "G=1")
+    bfp8.set_schedule("tiled")
+    try:
+        c_d = bfp8.gemm(q, s, bq_d, bs_d)
+        torch.cuda.synchronize()
+    finally:
+        bfp8.set_schedule("auto")
+    assert torch.equal(c_g.view(torch.int16), c_d.view(torch.int16))
+
+
+def test_grouped_rejections(gpu):
+    q = torch.zeros(100, 256, dtype=torch.uint8, device=gpu)
+    s = torch.ones(2, 100, dtype=torch.float32, device=gpu).t()
+    bq = torch.zeros(2, 128, 256, dtype=torch.uint8, device=gpu)
+    bs = torch.ones(2, 1, 2, dtype=torch.float32, device=gpu)
+    lay = torch.zeros(100, dtype=torch.int32, device=gpu)
+    with pytest.raises(ValueError):  # M % 128 != 0
+        bfp8.grouped_gemm_contiguous(q, s, bq, bs, lay)
+
