@@ -27,6 +27,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # never emit packed-FP32 instructions (v_pk_add/mul/fma_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the per-block promotion FMAs read them directly and
+    # independent MFMAs do not serialize on one accumulator register quad
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 
 ]
 

@@ -13,7 +13,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/bfp8.h"
+#include "bfp8.h"
 #include "launch.h"
 
 namespace {

@@ -9,6 +9,8 @@
 namespace bfp8 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // One 16x16x128 FP8 (e4m3 x e4m3) matrix-core product with a zero accumulator input.
@@ -50,12 +52,9 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* c, int n, int N, bool vec
 
 // 32 bytes from global memory (16-byte aligned) as an MFMA operand.
 __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
+  const v4i lo = *reinterpret_cast<const v4i*>(p);
+  const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 }  // namespace bfp8

@@ -5,24 +5,32 @@
 // design", and the M-grouped contiguous kernel of page
 // "transformers/integrations/deepgemm.py" (m_grouped_fp8_fp4_gemm_nt_contiguous,
 // _build_deepgemm_contiguous_layout), re-derived for CDNA4:
-//   * one workgroup computes a BN x BM tile of C^T = B . A^T (weights on the
-//     MFMA's first operand, activations on its second), split over WGN x WGM
-//     waves of WN x WM each; one 16x16x128 FP8 MFMA covers one 128-wide K block of
-//     a 16x16 sub-tile, so the "block accumulator" of the method is just the MFMA
-//     result of that K block;
-//   * per K block the B and A tiles (BN and BM rows of 128 bytes) are copied
-//     HBM -> registers -> LDS with 16-byte coalesced loads, double buffered: the
-//     loads of block kb+1 are in flight while block kb is multiplied, and one
-//     barrier per K block separates the two LDS buffers' uses. 16-byte chunks of
-//     each 128-byte LDS row are XOR-swizzled by (row mod 8) so that the 16 lanes
-//     reading one fragment column spread over the LDS banks;
-//   * promotion: acc += P * (As[kb][m] * Bs[n/128][kb]) with one FMA per element;
-//     each lane holds one activation row m per M sub-tile (one scale product per
-//     sub-tile) and each wave's N range lies inside one 128-row weight-scale strip
-//     (one weight scale per K block, loaded once per wave);
+//   * a workgroup computes a BN x BM tile of C^T = B . A^T (weight rows on the MFMA's
+//     first operand, activation rows on its second) with WGN x WGM waves of WN x WM;
+//     one 16x16x128 FP8 MFMA covers one 128-wide K block of a 16x16 sub-tile, so the
+//     per-block FP32 accumulator of the method is simply that MFMA's result;
+//   * promotion: acc += P * (As[kb][m] * Bs[n/128][kb]), one FMA per element per K
+//     block; every lane holds one activation row m per M sub-tile (one scale product
+//     per sub-tile) and each wave's weight rows lie in one 128-row scale strip;
+//   * both operand tiles of a K block (BN + BM rows of 128 bytes) and the block's BM
+//     activation scales are copied HBM -> LDS by the gfx950 direct-to-LDS loads
+//     (global_load_lds_dwordx4 / _dword), which need no staging registers and no LDS
+//     write instructions. The copy of block kb + 1 runs while block kb is multiplied
+//     out of the other LDS stage. The loads are issued from inline assembly and their
+//     completion is awaited explicitly (the compiler would otherwise drain them before
+//     every LDS read); the weight scales come through scalar loads. The 16-byte chunks
+//     of each 128-byte LDS row are XOR-swizzled by (row mod 8), which the copy realizes
+//     by choosing each lane's source chunk: the 16 lanes that read one fragment column
+//     then hit different LDS banks;
+//   * workgroups are mapped to tiles XCD by XCD: the hardware deals consecutive
+//     workgroups round-robin to the 8 XCDs, so each XCD is given a contiguous run of
+//     tiles in an M-grouped order, and the workgroups resident on one XCD at a time
+//     share activation and weight rows in that XCD's L2;
 //   * grouped: a workgroup's BM rows lie in one 128-row block; its expert id is the
-//     largest id among those rows (padding rows carry -1), a block of padding only
+//     largest id among those rows (padding rows carry -1); a block of padding only
 //     exits at once, and rows whose id is -1 are not stored.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,20 +38,83 @@ namespace bfp8 {
 
 namespace {
 
-template <int BN, int BM, int WGN, int WGM, bool kGrouped>
+// LDS-only workgroup barrier: orders LDS accesses across the barrier without
+// waiting for outstanding global loads (unlike a full __syncthreads()).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Direct global -> LDS copies: lane l's 16 (or 4) bytes from sbase + voff land at LDS
+// byte address lds + 16 * l (or 4 * l); completion is awaited with wait_copies(). They are
+// issued from inline assembly because the compiler, which cannot tell the copies into one
+// LDS stage from reads of the other, would otherwise drain every copy in flight before
+// each LDS read. The LDS address travels in M0, which the compiler reserves: it is saved
+// and restored inside the same statement.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %2, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(sbase), "v"(voff), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %2, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(sbase), "v"(voff), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent copies have landed.
+template <int N>
+__device__ __forceinline__ void wait_copies_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Tile of workgroup `bid`: each XCD (bid % 8) owns a contiguous run of the tiles,
+// ordered in groups of `group_m` M-tiles with the M-tile index fastest.
+__device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int group_m, int& tn, int& tm) {
+  const int total = n_tiles * m_tiles;
+  int t = bid;
+  if (total % 8 == 0) t = (bid % 8) * (total / 8) + bid / 8;
+  const int band = group_m * n_tiles;
+  const int first_m = (t / band) * group_m;
+  const int gm = min(m_tiles - first_m, group_m);
+  const int r = t - (t / band) * band;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+template <int BN, int BM, int WGN, int WGM, int STAGES, bool kGrouped>
 __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs args) {
-  constexpr int kThreads = WGN * WGM * 64;
+  constexpr int kWaves = WGN * WGM;
   constexpr int WN = BN / WGN, WM = BM / WGM;
   constexpr int TN = WN / 16, TM = WM / 16;
-  constexpr int kRows = BN + BM;  // 128-byte LDS rows per stage
-  constexpr int kLoads = kRows * 8 / kThreads;
-  static_assert(kRows * 8 % kThreads == 0, "tile copy must split evenly over the threads");
-  static_assert(kThreads % 8 == 0 && BN % (kThreads / 8) == 0, "each copy step must stay inside B or A rows");
+  constexpr int kRows = BN + BM;             // 128-byte LDS rows per stage: weights, then activations
+  constexpr int kStage = kRows * kBlock;     // bytes per stage
+  constexpr int kCopies = kRows / 8 / kWaves;  // 1 KB (8-row) copies per wave per K block
+  static_assert(kRows % (8 * kWaves) == 0, "each wave copies whole 8-row groups");
+  static_assert(BM % 64 == 0 && BM / 64 <= kWaves, "activation scales: one 64-lane copy per 64 rows");
   static_assert(WN % 16 == 0 && WM % 16 == 0, "wave tiles are made of 16x16 MFMA tiles");
   static_assert(kBlock % WN == 0 && BN % WN == 0, "a wave's N range must lie inside one weight-scale strip");
   static_assert(!kGrouped || kBlock % BM == 0, "grouped: a workgroup's rows must lie in one 128-row block");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kRows * kBlock];
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 pipeline stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES][kStage];
+  __shared__ __attribute__((aligned(16))) float as_lds[STAGES][BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -53,8 +124,9 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   const int KB = args.K / kBlock;
 
   const int n_tiles = (N + BN - 1) / BN;
-  const int tile_n = blockIdx.x % n_tiles;
-  const int tile_m = blockIdx.x / n_tiles;
+  const int m_tiles = (M + BM - 1) / BM;
+  int tile_n, tile_m;
+  map_tile(blockIdx.x, n_tiles, m_tiles, 8, tile_n, tile_m);
   const int n0 = tile_n * BN, m0 = tile_m * BM;
 
   const uint8_t* bmat = args.b;
@@ -72,29 +144,47 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
     bsmat += (int64_t)gid * ((N + kBlock - 1) / kBlock) * args.ld_bs;
   }
 
-  // Copy assignment: chunk c = tid + j * kThreads of the stage, row c / 8, 16-byte column c % 8.
-  const uint8_t* gsrc[kLoads];
-  int ldst[kLoads];
+  // Copy plan. Wave w copies stage rows [w * 8 * kCopies, ...) in 8-row pieces; lane l of
+  // piece j lands at stage row prow_base + j*8 + l/8, physical 16-byte column l%8, so it
+  // loads the logical column (l%8) ^ (row%8) = (l%8) ^ (l/8) of that row. A piece is all
+  // weight rows or all activation rows (BN is a multiple of 8). Rows past M or N are
+  // clamped to the last row (their results are never stored).
+  const int prow_base = w * 8 * kCopies;
+  const int lrow = lane >> 3, lcol = (lane & 7) ^ (lane >> 3);
+  uint32_t coff[kCopies];
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int c = tid + j * kThreads;
-    const int row = c >> 3, col = c & 7;
-    if (row < BN) {
-      const int n = min(n0 + row, N - 1);
-      gsrc[j] = bmat + (int64_t)n * args.ldb + col * 16;
-    } else {
-      const int m = min(m0 + row - BN, M - 1);
-      gsrc[j] = args.a + (int64_t)m * args.lda + col * 16;
-    }
-    ldst[j] = row * kBlock + ((col ^ (row & 7)) << 4);
+  for (int j = 0; j < kCopies; ++j) {
+    const int prow = prow_base + j * 8;  // uniform
+    const int row = prow < BN ? min(n0 + prow + lrow, N - 1) : min(m0 + prow - BN + lrow, M - 1);
+    const int64_t ld = prow < BN ? args.ldb : args.lda;
+    coff[j] = (uint32_t)((int64_t)row * ld + lcol * 16);
   }
+  // Activation scales of a K block: waves 0 .. BM/64-1 copy 64 of them each (clamped rows).
+  const bool copies_as = w < BM / 64;
+  const uint32_t as_voff = (uint32_t)min(m0 + (copies_as ? w : 0) * 64 + lane, M - 1) * 4u;
 
-  // Scale pointers: one activation row per lane per M sub-tile, one weight strip per wave.
-  const int r = lane & 15, kc = lane >> 4;
-  const float* asp[TM];
+  uint32_t stage_lds[STAGES], as_lds_addr[STAGES];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) asp[tm] = args.as + min(m0 + wm * WM + tm * 16 + r, M - 1);
-  const float* bsp = bsmat + (int64_t)(min(n0 + wn * WN, N - 1) / kBlock) * args.ld_bs;
+  for (int i = 0; i < STAGES; ++i) {
+    stage_lds[i] = lds_addr(&smem[i][0]);
+    as_lds_addr[i] = lds_addr(&as_lds[i][0]);
+  }
+  auto issue_copies = [&](int buf, int kb) __attribute__((always_inline)) {
+    const uint8_t* bsrc = bmat + (int64_t)kb * kBlock;
+    const uint8_t* asrc = args.a + (int64_t)kb * kBlock;
+    const uint32_t dst = stage_lds[buf] + (uint32_t)(prow_base * kBlock);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j)
+      copy16_to_lds(prow_base + j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
+    if (copies_as)
+      copy4_to_lds(args.as + (int64_t)kb * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
+  };
+
+  const int r = lane & 15, kc = lane >> 4;
+  // Weight scale of this wave's strip, through the scalar cache (constant address space).
+  const __attribute__((address_space(4))) float* bsp =
+      (const __attribute__((address_space(4))) float*)(bsmat +
+                                                       (int64_t)(min(n0 + wn * WN, N - 1) / kBlock) * args.ld_bs);
 
   float acc[TN][TM][4];
 #pragma unroll
@@ -104,70 +194,95 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[tn][tm][e] = 0.f;
 
-  uint4 stage[kLoads];
-  float as_next[TM], as_cur[TM];
-  float bs_next, bs_cur;
-
-  auto load_global = [&](int kb) {
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) stage[j] = *reinterpret_cast<const uint4*>(gsrc[j] + (int64_t)kb * kBlock);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) as_next[tm] = asp[tm][(int64_t)kb * args.ld_as];
-    bs_next = bsp[kb];
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) *reinterpret_cast<uint4*>(&smem[buf][ldst[j]]) = stage[j];
-  };
-  auto lds_frag = [&](int buf, int row) -> v8i {
+  auto lds_frag = [&](int buf, int row) __attribute__((always_inline)) -> v8i {
     const uint8_t* base = &smem[buf][row * kBlock];
     const int sw = row & 7;
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * kc) ^ sw) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * kc + 1) ^ sw) << 4));
-    v8i f;
-    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
-    return f;
+    const v4i lo = *reinterpret_cast<const v4i*>(base + (((2 * kc) ^ sw) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(base + (((2 * kc + 1) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
-  load_global(0);
-  store_lds(0);
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) as_cur[tm] = as_next[tm];
-  bs_cur = bs_next;
-  __syncthreads();
+  // Copies issued per wave per K block; the wait for the oldest block in flight counts the
+  // copies of the STAGES - 2 blocks issued after it (waits need immediate counts).
+  auto wait_for_next_block = [&](bool steady) __attribute__((always_inline)) {
+    if (!steady || STAGES == 2) {
+      wait_copies();
+    } else if (copies_as) {
+      wait_copies_upto<(STAGES - 2) * (kCopies + 1)>();
+    } else {
+      wait_copies_upto<(STAGES - 2) * kCopies>();
+    }
+  };
 
-  for (int kb = 0; kb < KB; ++kb) {
-    const int cur = kb & 1;
-    const bool more = kb + 1 < KB;
-    if (more) load_global(kb + 1);
-
+  auto iter = [&](int kb, auto buf_c) __attribute__((always_inline)) {
+    constexpr int s = decltype(buf_c)::value;  // kb % STAGES
+    // Copy block kb + STAGES - 1 into the stage consumed in iteration kb - 1 (which ended
+    // with a barrier) while block kb is multiplied. Near the end no copy is issued and the
+    // wait below drains everything.
+    const bool steady = kb + STAGES - 1 < KB;
+    if (steady) issue_copies((s + STAGES - 1) % STAGES, kb + STAGES - 1);
+    const float bs_kb = bsp[kb];
+    // Hand-scheduled multiply: step t issues the MFMA of sub-tile t and the promotion FMAs
+    // of sub-tile t - 2, whose result is then at least one whole MFMA old (promoting t - 1
+    // would stall on the MFMA latency); a scheduling barrier per step keeps the compiler
+    // from hoisting all MFMAs ahead of their promotions, which would hold every block
+    // result live at once.
     v8i af[TM];
     float sc[TM];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      af[tm] = lds_frag(cur, BN + wm * WM + tm * 16 + r);
-      sc[tm] = as_cur[tm] * bs_cur;
+      af[tm] = lds_frag(s, BN + wm * WM + tm * 16 + r);
+      sc[tm] = as_lds[s][wm * WM + tm * 16 + r] * bs_kb;
     }
+    v8i bf = lds_frag(s, wn * WN + r);
+    v8i bf_next = bf;
+    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;  // results of sub-tiles t - 1 and t - 2
+    auto promote = [&](int u, const v4f& pu) __attribute__((always_inline)) {
+      const int un = u / TM, um = u % TM;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const v8i bf = lds_frag(cur, wn * WN + tn * 16 + r);
+      for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], sc[um], acc[un][um][e]);
+      // Pin the promotion here: otherwise the FMAs are sunk past the loop's branch,
+      // since their results are only read in the next K block.
+      asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
+    };
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const v4f p = mfma_block(bf, af[tm]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[tn][tm][e] = fmaf(p[e], sc[tm], acc[tn][tm][e]);
-      }
+    for (int t = 0; t < TN * TM; ++t) {
+      const int tn = t / TM, tm = t % TM;
+      if (tm == 0 && tn + 1 < TN) bf_next = lds_frag(s, wn * WN + (tn + 1) * 16 + r);
+      const v4f p = mfma_block(bf, af[tm]);
+      if (t >= 2) promote(t - 2, p2);
+      __builtin_amdgcn_sched_barrier(0);
+      p2 = p1;
+      p1 = p;
+      if (tm == TM - 1) bf = bf_next;
     }
+    promote(TN * TM - 2, p2);
+    promote(TN * TM - 1, p1);
+    // Block kb + 1 is in LDS once every wave's copies of it have landed.
+    wait_for_next_block(steady);
+    lds_barrier();
+  };
 
-    if (more) {
-      store_lds(cur ^ 1);
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) as_cur[tm] = as_next[tm];
-      bs_cur = bs_next;
-    }
-    __syncthreads();
+  for (int i = 0; i < STAGES - 1; ++i) issue_copies(i, min(i, KB - 1));
+  // block 0 has landed once the copies of blocks 1 .. STAGES-2 are the only ones left
+  wait_for_next_block(STAGES - 1 <= KB);
+  lds_barrier();
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2 % STAGES>;
+  using S3 = std::integral_constant<int, 3 % STAGES>;
+  int kb = 0;
+  for (; kb + STAGES <= KB; kb += STAGES) {
+    iter(kb, S0{});
+    iter(kb + 1, S1{});
+    if constexpr (STAGES > 2) iter(kb + 2, S2{});
+    if constexpr (STAGES > 3) iter(kb + 3, S3{});
   }
+  if (kb < KB) iter(kb++, S0{});
+  if (kb < KB) iter(kb++, S1{});
+  if constexpr (STAGES > 2)
+    if (kb < KB) iter(kb++, S2{});
 
   const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
 #pragma unroll
@@ -186,24 +301,33 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   }
 }
 
-constexpr int kTileBN = 128, kTileBM = 128, kTileWGN = 2, kTileWGM = 2;
-
-}  // namespace
-
-hipError_t launch_gemm_tiled(const GemmArgs& args, hipStream_t stream) {
-  const int n_tiles = (args.N + kTileBN - 1) / kTileBN;
-  const int m_tiles = (args.M + kTileBM - 1) / kTileBM;
-  hipLaunchKernelGGL((gemm_tiled_kernel<kTileBN, kTileBM, kTileWGN, kTileWGM, false>),
-                     dim3((unsigned)(n_tiles * m_tiles)), dim3(kTileWGN * kTileWGM * 64), 0, stream, args);
+template <int BN, int BM, int WGN, int WGM, int STAGES, bool G>
+hipError_t launch_tiled_cfg(const GemmArgs& args, hipStream_t stream) {
+  const int n_tiles = (args.N + BN - 1) / BN;
+  const int m_tiles = (args.M + BM - 1) / BM;
+  hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, G>), dim3((unsigned)(n_tiles * m_tiles)),
+                     dim3(WGN * WGM * 64), 0, stream, args);
   return hipGetLastError();
 }
 
+}  // namespace
+
+// Dense: the largest tile that still gives every CU (256 on MI355X) a workgroup, which
+// trades LDS traffic per MFMA (lower with big tiles) against parallelism (measured on the
+// N = K = 4096 sweep: 256x256 wins from M = 4096, 256x128 at M = 2048, 128x128 at 1024,
+// 128x64 below). Tiles with smaller stages get deeper copy pipelines.
+hipError_t launch_gemm_tiled(const GemmArgs& args, hipStream_t stream) {
+  auto tiles = [&](int bn, int bm) { return (int64_t)((args.N + bn - 1) / bn) * ((args.M + bm - 1) / bm); };
+  constexpr int64_t kFill = 256;
+  if (tiles(256, 256) >= kFill) return launch_tiled_cfg<256, 256, 2, 4, 2, false>(args, stream);
+  if (tiles(256, 128) >= kFill) return launch_tiled_cfg<256, 128, 4, 2, 3, false>(args, stream);
+  if (tiles(128, 128) >= kFill) return launch_tiled_cfg<128, 128, 2, 2, 3, false>(args, stream);
+  return launch_tiled_cfg<128, 64, 2, 1, 3, false>(args, stream);
+}
+
+// Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream) {
-  const int n_tiles = (args.N + kTileBN - 1) / kTileBN;
-  const int m_tiles = args.M / kTileBM;  // M % 128 == 0 (checked by the caller)
-  hipLaunchKernelGGL((gemm_tiled_kernel<kTileBN, kTileBM, kTileWGN, kTileWGM, true>),
-                     dim3((unsigned)(n_tiles * m_tiles)), dim3(kTileWGN * kTileWGM * 64), 0, stream, args);
-  return hipGetLastError();
+  return launch_tiled_cfg<256, 128, 4, 2, 3, true>(args, stream);
 }
 
 }  // namespace bfp8
