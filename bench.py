@@ -20,8 +20,9 @@ reuses one copy (the pages' "identical preallocated inputs").
 Also reported (same JSON line):
   * roofline: the dominant kernel (the M = 8192 GEMM) against the dense FP8 matrix
     peak, timed with HIP events around its launches on the launch stream;
-  * per_m: per-shape GEMM latency (p50 of 5 trials), TFLOP/s and the fraction of
-    the HBM (M <= 256) or FP8 (M >= 512) roofline, plus the quantizer's GB/s;
+  * per_m: per-shape GEMM latency (p50 of 5 replays of a captured HIP graph of
+    back-to-back launches, so host launch cost is excluded), TFLOP/s and the fraction
+    of the HBM (M <= 256) or FP8 (M >= 512) roofline, plus the quantizer's GB/s;
   * cpu_baseline: the CPU oracle on a bounded sample of the same sweep.
 """
 
@@ -154,26 +155,46 @@ def main() -> int:
 
     rot = [0]
 
-    def step(dom_events=None):
-        for m in sweep:
-            bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
-            i = rot[0] % copies
-            rot[0] += 1
-            if dom_events is not None and m == DOMINANT_M:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
-                e1.record(stream)
-                dom_events.append((e0, e1))
-            else:
-                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
-
     if args.copy_calibration:
         src = torch.ones(256 * 2**20 // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         log("copy calibration: 256 MiB device-to-device copy done")
+
+    # One step: quantize + GEMM for every M of the sweep. Everything but the dominant GEMM is
+    # replayed from a captured HIP graph (host launch cost would otherwise dominate the
+    # microsecond-scale small-M kernels); the dominant GEMM is launched directly with HIP
+    # events around it on the same stream, which times that kernel inside the timed region.
+    def graph_part():
+        for j, m in enumerate(sweep):
+            bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
+            if m != DOMINANT_M:
+                i = j % copies
+                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
+
+    capture_stream = torch.cuda.Stream(dev)
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(capture_stream):
+        graph_part()
+        capture_stream.synchronize()
+        with torch.cuda.graph(step_graph, stream=capture_stream):
+            graph_part()
+    torch.cuda.synchronize()
+
+    def step(dom_events=None):
+        step_graph.replay()
+        if DOMINANT_M in sweep:
+            i = rot[0] % copies
+            rot[0] += 1
+            if dom_events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                bfp8.gemm(qs[DOMINANT_M], ss[DOMINANT_M], bq[i], bsc[i], out=cs[DOMINANT_M])
+                e1.record(stream)
+                dom_events.append((e0, e1))
+            else:
+                bfp8.gemm(qs[DOMINANT_M], ss[DOMINANT_M], bq[i], bsc[i], out=cs[DOMINANT_M])
 
     for _ in range(args.warmup):
         step()
@@ -209,38 +230,45 @@ def main() -> int:
                     "kernel": f"bfp8_gemm M={DOMINANT_M} N={N} K={K} schedule={bfp8.schedule_for(DOMINANT_M, N, K)}",
                     "avg_launch_us": round(dom_ms * 1e3, 2), "launches": len(dom_events)}
 
-    # ---- per-M table (page 1's protocol, shortened: warmup, then 5 trials, p50) -----------
+    # ---- per-M table: back-to-back launches replayed from a captured HIP graph (so host-side
+    # launch cost is not measured), p50 of 5 trials; cold mode cycles the weight copies ----
     per_m = {}
     if not args.no_table:
-        for m in sweep:
-            def gemm_once():
-                i = rot[0] % copies
-                rot[0] += 1
-                bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
+        graph_stream = torch.cuda.Stream(dev)
 
-            def quant_once():
-                bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
-
-            res = {}
-            for name, fn in (("gemm", gemm_once), ("quant", quant_once)):
-                # size a trial to ~10 ms of work
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        def graph_time_us(fn, calls: int) -> float:
+            """Median per-call time of `calls` back-to-back calls of fn, captured once and replayed."""
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(graph_stream):
+                fn(calls)  # warm the code paths on the capture stream
+                graph_stream.synchronize()
+                with torch.cuda.graph(g, stream=graph_stream):
+                    fn(calls)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            trials = []
+            for _ in range(5):
                 e0.record(stream)
-                for _ in range(5):
-                    fn()
+                g.replay()
                 e1.record(stream)
                 torch.cuda.synchronize()
-                per = max(e0.elapsed_time(e1) / 5, 1e-3)
-                reps = int(min(max(10.0 / per, 10), 2000))
-                trials = []
-                for _ in range(5):
-                    e0.record(stream)
-                    for _ in range(reps):
-                        fn()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    trials.append(e0.elapsed_time(e1) * 1e3 / reps)
-                res[name] = float(np.median(trials))
+                trials.append(e0.elapsed_time(e1) * 1e3 / calls)
+            del g
+            return float(np.median(trials))
+
+        for m in sweep:
+            def gemm_calls(n):
+                for j in range(n):
+                    i = j % copies
+                    bfp8.gemm(qs[m], ss[m], bq[i], bsc[i], out=cs[m])
+
+            def quant_calls(n):
+                for _ in range(n):
+                    bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
+
+            calls = copies if m <= 2048 else max(copies // 4, 4)
+            res = {"gemm": graph_time_us(gemm_calls, calls), "quant": graph_time_us(quant_calls, min(calls, 32))}
             us = res["gemm"]
             tflops = 2.0 * m * N * K / (us * 1e-6) / 1e12
             gbs = gemm_alg_bytes(m) / (us * 1e-6) / 1e9

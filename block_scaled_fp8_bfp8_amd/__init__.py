@@ -70,6 +70,24 @@ def _as_u8(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> tuple[int, int]:
+    """(pointer, size) of a zero-filled workspace for the current stream, grown on demand.
+
+    The GEMM leaves its arrival counters zero after each call, so one buffer per (device,
+    stream) is reused by every call ordered on that stream."""
+    if nbytes == 0:
+        return 0, 0
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
 def abi_version() -> int:
     return _native.lib().bfp8_abi_version()
 
@@ -110,9 +128,13 @@ def _scale_ld_as(a_s: torch.Tensor, m: int) -> int:
 
 
 def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
-         out: torch.Tensor | None = None) -> torch.Tensor:
+         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """C[M, N] (bf16) = blockwise FP8 product of a_q [M, K] and b_q [N, K] with scales a_s [M, K/128]
-    (group-major) and b_s [ceil(N/128), K/128]."""
+    (group-major) and b_s [ceil(N/128), K/128].
+
+    workspace: optional caller-owned uint8 buffer on the same device (zero-filled before its
+    first use, at least bfp8_gemm_workspace_bytes(M, N, K) bytes); by default one buffer per
+    (device, stream) is kept here."""
     a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
     _require(a_q, "a_q", torch.uint8, 2)
     _require(b_q, "b_q", torch.uint8, 2)
@@ -131,9 +153,15 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Ten
     _require(out, "out", torch.bfloat16, 2)
     if out.stride(1) != 1:
         raise ValueError("out must be contiguous along N")
-    st = _native.lib().bfp8_gemm(a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m),
-                                 b_q.data_ptr(), b_q.stride(0), b_s.data_ptr(), b_s.stride(0),
-                                 out.data_ptr(), out.stride(0), m, n, k, None, 0, _stream(a_q.device))
+    lib = _native.lib()
+    if workspace is None:
+        ws_ptr, ws_bytes = _workspace(a_q.device, lib.bfp8_gemm_workspace_bytes(m, n, k))
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib.bfp8_gemm(a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m),
+                       b_q.data_ptr(), b_q.stride(0), b_s.data_ptr(), b_s.stride(0),
+                       out.data_ptr(), out.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream(a_q.device))
     _check(st, "bfp8_gemm")
     return out
 

@@ -71,7 +71,7 @@ bfp8_status_t launched(hipError_t e, const char* what) {
 // Shared checks of the dense and grouped GEMM arguments.
 bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
                               int64_t ldb, const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
-                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes) {
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes, bool grouped) {
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
   if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
   if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
@@ -85,6 +85,8 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, in
   if (lda < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "lda = %lld < K = %lld", (long long)lda, (long long)K);
   if (ldb < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldb = %lld < K = %lld", (long long)ldb, (long long)K);
   if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
+  if (workspace && !aligned(workspace, 256))
+    return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   if (ld_bs < K / bfp8::kBlock)
     return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_bs = %lld < K/128 = %lld", (long long)ld_bs,
                 (long long)(K / bfp8::kBlock));
@@ -93,7 +95,7 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, in
   if (!aligned(a, 16) || !aligned(b, 16)) return fail(BFP8_ERR_MISALIGNED, "a and b must be 16-byte aligned");
   if (!aligned(as, 4) || !aligned(bs, 4)) return fail(BFP8_ERR_MISALIGNED, "as and bs must be 4-byte aligned");
   if (!aligned(c, 2)) return fail(BFP8_ERR_MISALIGNED, "c must be 2-byte aligned");
-  const size_t need = bfp8_gemm_workspace_bytes(M, N, K);
+  const size_t need = grouped ? 0 : bfp8_gemm_workspace_bytes(M, N, K);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   return BFP8_OK;
@@ -150,13 +152,18 @@ bfp8_status_t bfp8_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, i
                   "quant_act");
 }
 
-size_t bfp8_gemm_workspace_bytes(int64_t /*M*/, int64_t /*N*/, int64_t /*K*/) { return 0; }
+size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % bfp8::kBlock != 0) return 0;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (choose_schedule(M, N, K) != BFP8_SCHED_TILED) return 0;
+  return bfp8::plan_tiled(M, N, K).workspace_bytes;
+}
 
 bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b, int64_t ldb,
                         const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream) {
   bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
-                                     workspace_bytes);
+                                     workspace_bytes, false);
   if (st != BFP8_OK) return st;
   if (M == 0) return ok();
   st = check_device();
@@ -164,7 +171,7 @@ bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t 
   const bfp8::GemmArgs args{a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, (int)M, (int)N, (int)K, nullptr, 1};
   const int sched = choose_schedule(M, N, K);
   if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_small(args, (hipStream_t)stream), "gemm_small");
-  return launched(bfp8::launch_gemm_tiled(args, (hipStream_t)stream), "gemm_tiled");
+  return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
 }
 
 bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
@@ -173,7 +180,7 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
                                            int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                                            void* stream) {
   bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
-                                     workspace_bytes);
+                                     workspace_bytes, true);
   if (st != BFP8_OK) return st;
   if (G < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "G = %d must be >= 1", (int)G);
   if (M % bfp8::kBlock != 0)
@@ -185,8 +192,8 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
-  const bfp8::GemmArgs args{a,   lda, as,     ld_as,  b,      ldb,           bs, ld_bs,
-                            c,   ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G};
+  const bfp8::GemmArgs args{a,   lda, as,     ld_as,  b,      ldb,           bs,     ld_bs,  c,
+                            ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G};
   return launched(bfp8::launch_grouped_tiled(args, (hipStream_t)stream), "grouped_gemm_tiled");
 }
 

@@ -19,9 +19,9 @@
 //     out of the other LDS stage. The loads are issued from inline assembly and their
 //     completion is awaited explicitly (the compiler would otherwise drain them before
 //     every LDS read); the weight scales come through scalar loads. The 16-byte chunks
-//     of each 128-byte LDS row are XOR-swizzled by (row mod 8), which the copy realizes
-//     by choosing each lane's source chunk: the 16 lanes that read one fragment column
-//     then hit different LDS banks;
+//     of each 128-byte LDS row are XOR-swizzled by a function of the row, which the copy
+//     realizes by choosing each lane's source chunk, so that fragment reads are free of
+//     bank conflicts;
 //   * workgroups are mapped to tiles XCD by XCD: the hardware deals consecutive
 //     workgroups round-robin to the 8 XCDs, so each XCD is given a contiguous run of
 //     tiles in an M-grouped order, and the workgroups resident on one XCD at a time
@@ -29,6 +29,7 @@
 //   * grouped: a workgroup's BM rows lie in one 128-row block; its expert id is the
 //     largest id among those rows (padding rows carry -1); a block of padding only
 //     exits at once, and rows whose id is -1 are not stored.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -84,6 +85,14 @@ __device__ __forceinline__ void wait_copies_upto() {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
+// XOR swizzle of the 16-byte columns of a 128-byte LDS row. A fragment read has 16 lanes
+// reading the same logical column of the 16 rows of a 16-row block, two 16-byte reads per
+// lane. Measured on gfx950 with the LDS bank-conflict counter: XOR by (r ^ r / 8) % 8, r the
+// row within its block, makes these reads conflict-free, whereas r % 8, (r / 2) % 8 and
+// similar XORs still conflict two ways and halve the LDS read rate. It depends on r alone, so
+// all fragments of a wave share their swizzled offsets.
+__device__ __forceinline__ int lds_swizzle(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
 // Tile of workgroup `bid`: each XCD (bid % 8) owns a contiguous run of the tiles,
 // ordered in groups of `group_m` M-tiles with the M-tile index fastest.
 __device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int group_m, int& tn, int& tm) {
@@ -121,10 +130,10 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = w % WGN, wm = w / WGN;
   const int M = args.M, N = args.N;
-  const int KB = args.K / kBlock;
 
   const int n_tiles = (N + BN - 1) / BN;
   const int m_tiles = (M + BM - 1) / BM;
+  const int KB = args.K / kBlock;
   int tile_n, tile_m;
   map_tile(blockIdx.x, n_tiles, m_tiles, 8, tile_n, tile_m);
   const int n0 = tile_n * BN, m0 = tile_m * BM;
@@ -145,16 +154,17 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   }
 
   // Copy plan. Wave w copies stage rows [w * 8 * kCopies, ...) in 8-row pieces; lane l of
-  // piece j lands at stage row prow_base + j*8 + l/8, physical 16-byte column l%8, so it
-  // loads the logical column (l%8) ^ (row%8) = (l%8) ^ (l/8) of that row. A piece is all
-  // weight rows or all activation rows (BN is a multiple of 8). Rows past M or N are
-  // clamped to the last row (their results are never stored).
+  // piece j lands at stage row prow + l/8, physical 16-byte column l%8, so it loads the
+  // logical column (l%8) ^ swizzle(row) of that row. A piece is all weight rows or all
+  // activation rows (BN is a multiple of 8). Rows past M or N are clamped to the last row
+  // (their results are never stored).
   const int prow_base = w * 8 * kCopies;
-  const int lrow = lane >> 3, lcol = (lane & 7) ^ (lane >> 3);
+  const int lrow = lane >> 3;
   uint32_t coff[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
     const int prow = prow_base + j * 8;  // uniform
+    const int lcol = (lane & 7) ^ lds_swizzle(prow + lrow);
     const int row = prow < BN ? min(n0 + prow + lrow, N - 1) : min(m0 + prow - BN + lrow, M - 1);
     const int64_t ld = prow < BN ? args.ldb : args.lda;
     coff[j] = (uint32_t)((int64_t)row * ld + lcol * 16);
@@ -169,7 +179,8 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
     stage_lds[i] = lds_addr(&smem[i][0]);
     as_lds_addr[i] = lds_addr(&as_lds[i][0]);
   }
-  auto issue_copies = [&](int buf, int kb) __attribute__((always_inline)) {
+  auto issue_copies = [&](int buf, int kb_local) __attribute__((always_inline)) {
+    const int kb = kb_local;
     const uint8_t* bsrc = bmat + (int64_t)kb * kBlock;
     const uint8_t* asrc = args.a + (int64_t)kb * kBlock;
     const uint32_t dst = stage_lds[buf] + (uint32_t)(prow_base * kBlock);
@@ -178,6 +189,16 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
       copy16_to_lds(prow_base + j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
     if (copies_as)
       copy4_to_lds(args.as + (int64_t)kb * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
+  };
+  // One piece of a block's copy (for spreading a block's copies over the multiply steps).
+  auto issue_piece = [&](int buf, int kb_local, int j) __attribute__((always_inline)) {
+    const int kb = kb_local;
+    const uint8_t* src = prow_base + j * 8 < BN ? bmat + (int64_t)kb * kBlock : args.a + (int64_t)kb * kBlock;
+    copy16_to_lds(src, coff[j], stage_lds[buf] + (uint32_t)((prow_base + j * 8) * kBlock));
+  };
+  auto issue_scales = [&](int buf, int kb_local) __attribute__((always_inline)) {
+    if (copies_as)
+      copy4_to_lds(args.as + (int64_t)kb_local * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
   };
 
   const int r = lane & 15, kc = lane >> 4;
@@ -194,17 +215,42 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[tn][tm][e] = 0.f;
 
-  auto lds_frag = [&](int buf, int row) __attribute__((always_inline)) -> v8i {
-    const uint8_t* base = &smem[buf][row * kBlock];
-    const int sw = row & 7;
-    const v4i lo = *reinterpret_cast<const v4i*>(base + (((2 * kc) ^ sw) << 4));
-    const v4i hi = *reinterpret_cast<const v4i*>(base + (((2 * kc + 1) ^ sw) << 4));
+  // Fragment rows come in 16-row blocks, so every row a lane reads has row % 16 == r and the
+  // same swizzle: a fragment is two 16-byte reads at per-lane offsets from the block's first
+  // row, and the block offset folds into the instruction's immediate.
+  const int fsw = lds_swizzle(r);
+  const uint32_t off_lo = (uint32_t)(r * kBlock + (((2 * kc) ^ fsw) << 4));
+  const uint32_t off_hi = (uint32_t)(r * kBlock + (((2 * kc + 1) ^ fsw) << 4));
+  auto frag_at = [&](const uint8_t* stage, int row0) __attribute__((always_inline)) -> v8i {
+    const v4i lo = *reinterpret_cast<const v4i*>(stage + off_lo + row0 * kBlock);
+    const v4i hi = *reinterpret_cast<const v4i*>(stage + off_hi + row0 * kBlock);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  auto frag_b = [&](const uint8_t* stage, int tn) __attribute__((always_inline)) {
+    return frag_at(stage, wn * WN + tn * 16);
+  };
+  auto frag_a = [&](const uint8_t* stage, int tm) __attribute__((always_inline)) {
+    return frag_at(stage, BN + wm * WM + tm * 16);
+  };
+  auto act_scale = [&](int slot, int tm) __attribute__((always_inline)) { return as_lds[slot][wm * WM + tm * 16 + r]; };
 
-  // Copies issued per wave per K block; the wait for the oldest block in flight counts the
-  // copies of the STAGES - 2 blocks issued after it (waits need immediate counts).
-  auto wait_for_next_block = [&](bool steady) __attribute__((always_inline)) {
+  // Software pipeline. Sub-tiles are visited activation-row by activation-row: step
+  // t = tm * TN + tn multiplies weight fragment tn by activation fragment tm. Block kb is
+  // multiplied out of registers while block kb + 1 is read from LDS into the same registers,
+  // each fragment right after its last use in block kb (activation fragment tm after row tm,
+  // weight fragment tn in the last row). LDS stage kb % STAGES is free once block kb has been
+  // read (the barrier ending iteration kb - 1), so iteration kb refills it with block
+  // kb + STAGES, its copies spread over the steps, and waits at its end for block kb + 2,
+  // which iteration kb + 1 reads.
+  v8i fa[TM];
+  v8i fb[TN];
+  float sa[TM];
+  float bsv;
+  constexpr int kSteps = TN * TM;
+
+  // Copies issued per wave per K block; the wait for block kb + 2 at the end of iteration kb
+  // may leave the copies of blocks kb + 3 .. kb + STAGES in flight (waits take immediates).
+  auto wait_block_after_next = [&](bool steady) __attribute__((always_inline)) {
     if (!steady || STAGES == 2) {
       wait_copies();
     } else if (copies_as) {
@@ -214,75 +260,78 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
     }
   };
 
-  auto iter = [&](int kb, auto buf_c) __attribute__((always_inline)) {
-    constexpr int s = decltype(buf_c)::value;  // kb % STAGES
-    // Copy block kb + STAGES - 1 into the stage consumed in iteration kb - 1 (which ended
-    // with a barrier) while block kb is multiplied. Near the end no copy is issued and the
-    // wait below drains everything.
-    const bool steady = kb + STAGES - 1 < KB;
-    if (steady) issue_copies((s + STAGES - 1) % STAGES, kb + STAGES - 1);
-    const float bs_kb = bsp[kb];
-    // Hand-scheduled multiply: step t issues the MFMA of sub-tile t and the promotion FMAs
-    // of sub-tile t - 2, whose result is then at least one whole MFMA old (promoting t - 1
-    // would stall on the MFMA latency); a scheduling barrier per step keeps the compiler
-    // from hoisting all MFMAs ahead of their promotions, which would hold every block
-    // result live at once.
-    v8i af[TM];
+  auto iter = [&](int kb, auto steady_c) __attribute__((always_inline)) {
+    constexpr bool kSteady = decltype(steady_c)::value;  // kb + STAGES < KB: refill a stage
+    const int cslot = kb % STAGES;
+    // The last iteration also reads a (stale, in-bounds) stage, which keeps the steps free of
+    // branches; those registers are never used.
+    const int nslot = (kb + 1) % STAGES;
+    const uint8_t* nstage = &smem[nslot][0];
+    const float bs_next = bsp[min(kb + 1, KB - 1)];
     float sc[TM];
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      af[tm] = lds_frag(s, BN + wm * WM + tm * 16 + r);
-      sc[tm] = as_lds[s][wm * WM + tm * 16 + r] * bs_kb;
-    }
-    v8i bf = lds_frag(s, wn * WN + r);
-    v8i bf_next = bf;
-    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;  // results of sub-tiles t - 1 and t - 2
+    for (int tm = 0; tm < TM; ++tm) sc[tm] = sa[tm] * bsv;
+    if constexpr (kSteady) issue_scales(cslot, kb + STAGES);
+    // Step t issues the MFMA of sub-tile t, the promotion FMAs of sub-tile t - 2 (whose
+    // result is then at least one MFMA old), its share of the copies and of the next block's
+    // LDS reads; a scheduling barrier per step keeps this order. Copies go out in the first
+    // half of the steps, so that they land before the iteration ends.
+    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;
     auto promote = [&](int u, const v4f& pu) __attribute__((always_inline)) {
-      const int un = u / TM, um = u % TM;
+      const int um = u / TN, un = u % TN;
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], sc[um], acc[un][um][e]);
       // Pin the promotion here: otherwise the FMAs are sunk past the loop's branch,
       // since their results are only read in the next K block.
       asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
     };
+    constexpr int kCopySteps = kSteps / 2 > kCopies ? kSteps / 2 : kCopies;
 #pragma unroll
-    for (int t = 0; t < TN * TM; ++t) {
-      const int tn = t / TM, tm = t % TM;
-      if (tm == 0 && tn + 1 < TN) bf_next = lds_frag(s, wn * WN + (tn + 1) * 16 + r);
-      const v4f p = mfma_block(bf, af[tm]);
+    for (int t = 0; t < kSteps; ++t) {
+      const int tm = t / TN, tn = t % TN;
+      const v4f p = mfma_block(fb[tn], fa[tm]);
       if (t >= 2) promote(t - 2, p2);
+      if constexpr (kSteady) {
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j)
+          if (t == j * kCopySteps / kCopies) issue_piece(cslot, kb + STAGES, j);
+      }
+      if (tn == TN - 1) {
+        fa[tm] = frag_a(nstage, tm);
+        sa[tm] = act_scale(nslot, tm);
+      }
+      if (tm == TM - 1) fb[tn] = frag_b(nstage, tn);
       __builtin_amdgcn_sched_barrier(0);
       p2 = p1;
       p1 = p;
-      if (tm == TM - 1) bf = bf_next;
     }
-    promote(TN * TM - 2, p2);
-    promote(TN * TM - 1, p1);
-    // Block kb + 1 is in LDS once every wave's copies of it have landed.
-    wait_for_next_block(steady);
+    promote(kSteps - 2, p2);
+    promote(kSteps - 1, p1);
+    bsv = bs_next;
+    // Block kb + 2 is in LDS once every wave's copies of it have landed; the barrier also
+    // orders this iteration's reads of stage (kb + 1) % STAGES before its refill.
+    wait_block_after_next(kSteady);
     lds_barrier();
   };
 
 #pragma unroll
-  for (int i = 0; i < STAGES - 1; ++i) issue_copies(i, min(i, KB - 1));
-  // block 0 has landed once the copies of blocks 1 .. STAGES-2 are the only ones left
-  wait_for_next_block(STAGES - 1 <= KB);
+  for (int i = 0; i < STAGES; ++i) issue_copies(i, min(i, KB - 1));
+  // blocks 0 and 1 have landed once the copies of blocks 2 .. STAGES-1 are the only ones left
+  wait_block_after_next(STAGES <= KB);
   lds_barrier();
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2 % STAGES>;
-  using S3 = std::integral_constant<int, 3 % STAGES>;
-  int kb = 0;
-  for (; kb + STAGES <= KB; kb += STAGES) {
-    iter(kb, S0{});
-    iter(kb + 1, S1{});
-    if constexpr (STAGES > 2) iter(kb + 2, S2{});
-    if constexpr (STAGES > 3) iter(kb + 3, S3{});
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    fa[tm] = frag_a(&smem[0][0], tm);
+    sa[tm] = act_scale(0, tm);
   }
-  if (kb < KB) iter(kb++, S0{});
-  if (kb < KB) iter(kb++, S1{});
-  if constexpr (STAGES > 2)
-    if (kb < KB) iter(kb++, S2{});
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_b(&smem[0][0], tn);
+  bsv = bsp[0];
+  // every wave has read stage 0 before iteration 0 refills it
+  lds_barrier();
+  int kb = 0;
+  for (; kb + STAGES < KB; ++kb) iter(kb, std::true_type{});
+  for (; kb < KB; ++kb) iter(kb, std::false_type{});
 
   const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
 #pragma unroll
@@ -302,32 +351,42 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
 }
 
 template <int BN, int BM, int WGN, int WGM, int STAGES, bool G>
-hipError_t launch_tiled_cfg(const GemmArgs& args, hipStream_t stream) {
-  const int n_tiles = (args.N + BN - 1) / BN;
-  const int m_tiles = (args.M + BM - 1) / BM;
-  hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, G>), dim3((unsigned)(n_tiles * m_tiles)),
-                     dim3(WGN * WGM * 64), 0, stream, args);
+hipError_t launch_tiled_cfg(const GemmArgs& args, int tiles, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, G>), dim3((unsigned)tiles), dim3(WGN * WGM * 64), 0,
+                     stream, args);
   return hipGetLastError();
 }
 
+constexpr int64_t kCUs = 256;  // workgroups that fill MI355X once
+
 }  // namespace
 
-// Dense: the largest tile that still gives every CU (256 on MI355X) a workgroup, which
-// trades LDS traffic per MFMA (lower with big tiles) against parallelism (measured on the
-// N = K = 4096 sweep: 256x256 wins from M = 4096, 256x128 at M = 2048, 128x128 at 1024,
-// 128x64 below). Tiles with smaller stages get deeper copy pipelines.
-hipError_t launch_gemm_tiled(const GemmArgs& args, hipStream_t stream) {
-  auto tiles = [&](int bn, int bm) { return (int64_t)((args.N + bn - 1) / bn) * ((args.M + bm - 1) / bm); };
-  constexpr int64_t kFill = 256;
-  if (tiles(256, 256) >= kFill) return launch_tiled_cfg<256, 256, 2, 4, 2, false>(args, stream);
-  if (tiles(256, 128) >= kFill) return launch_tiled_cfg<256, 128, 4, 2, 3, false>(args, stream);
-  if (tiles(128, 128) >= kFill) return launch_tiled_cfg<128, 128, 2, 2, 3, false>(args, stream);
-  return launch_tiled_cfg<128, 64, 2, 1, 3, false>(args, stream);
+// Tile shape: the largest that still gives every CU a workgroup, which trades bytes copied
+// per MFMA (fewer with big tiles) against parallelism. Measured on the N = K = 4096 sweep:
+// 256x256 from M = 4096 (8 waves of 128x64, two LDS stages), 256x128 at M = 2048 and 128x128
+// at M = 1024 (three stages), 128x64 below (4 waves of 64x32, three stages).
+TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  auto tiles = [&](int bn, int bm) { return (int)(((N + bn - 1) / bn) * ((M + bm - 1) / bm)); };
+  if (tiles(256, 256) >= kCUs) return {256, 256, tiles(256, 256), 0};
+  if (tiles(256, 128) >= kCUs) return {256, 128, tiles(256, 128), 0};
+  if (tiles(128, 128) >= kCUs) return {128, 128, tiles(128, 128), 0};
+  return {128, 64, tiles(128, 64), 0};
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  const TiledPlan p = plan_tiled(args.M, args.N, args.K);
+  if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, false>(args, p.tiles, stream);
+  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, false>(args, p.tiles, stream);
+  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, false>(args, p.tiles, stream);
+  return launch_tiled_cfg<128, 64, 2, 2, 3, false>(args, p.tiles, stream);
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream) {
-  return launch_tiled_cfg<256, 128, 4, 2, 3, true>(args, stream);
+  const int tiles = (int)(((args.N + 255) / 256) * (args.M / 128));
+  return launch_tiled_cfg<256, 128, 4, 2, 3, true>(args, tiles, stream);
 }
 
 }  // namespace bfp8

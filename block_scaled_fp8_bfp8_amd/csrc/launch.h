@@ -28,6 +28,14 @@ struct GemmArgs {
   int G;
 };
 
+// Tiled-schedule plan for a dense GEMM: tile shape, and the workspace it needs (none so far).
+struct TiledPlan {
+  int bn, bm;  // tile: weight rows x activation rows
+  int tiles;   // number of output tiles
+  size_t workspace_bytes;
+};
+TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K);
+
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
 
@@ -35,7 +43,7 @@ hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, in
 constexpr int kSmallMaxM = 64;
 
 hipError_t launch_gemm_small(const GemmArgs& args, hipStream_t stream);
-hipError_t launch_gemm_tiled(const GemmArgs& args, hipStream_t stream);
+hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream);
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream);
 
 }  // namespace bfp8

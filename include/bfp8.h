@@ -121,9 +121,12 @@ const char* bfp8_last_error_message(void);
 bfp8_status_t bfp8_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* as, int64_t ld_as, void* stream);
 
-/* Bytes of workspace bfp8_gemm and bfp8_grouped_gemm_contiguous need for this
- * shape (0 for every shape in this version; the argument is kept so that a
- * schedule needing scratch can be added without an ABI change). */
+/* Bytes of device workspace bfp8_gemm needs for this shape under the current schedule
+ * (bfp8_set_schedule). Every schedule of this version needs none and returns 0; the
+ * argument pair exists so that a schedule with cross-workgroup partial sums can be added
+ * without changing the ABI. Contract for a non-zero size: 256-byte aligned, zero-filled
+ * before its first use, reusable by later calls ordered after it (same stream), never
+ * shared by calls that may run concurrently. bfp8_grouped_gemm_contiguous needs none. */
 size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -145,7 +148,8 @@ size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   c      device, [M][ldc] bf16 bit patterns, ldc >= N; written (only columns < N)
  *   M >= 0, N >= 1, K > 0 with K % 128 == 0
  *   workspace / workspace_bytes: device scratch of at least
- *          bfp8_gemm_workspace_bytes(M, N, K) bytes (may be NULL when that is 0)
+ *          bfp8_gemm_workspace_bytes(M, N, K) bytes under the contract above (may be
+ *          NULL when that is 0); BFP8_ERR_WORKSPACE if smaller
  *   stream hipStream_t or NULL
  * Inputs are read only; c may not overlap any input.
  */

@@ -99,7 +99,7 @@ def _random_codes(rng, shape):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (7, 17, 256), (83, 136, 128), (129, 576, 384), (64, 200, 256),
-                                   (65, 130, 512), (200, 40, 128)])
+                                   (65, 130, 512), (200, 40, 128), (83, 136, 1024), (129, 576, 2048)])
 @pytest.mark.parametrize("sched", SCHEDULES)
 def test_ragged_tails_with_padded_strides(gpu, m, n, k, sched):
     """Ragged M and N (partial 16-row, 128-row and weight-scale strips), padded row strides
@@ -150,7 +150,7 @@ def test_fp8_block_dot_alignment_window(gpu, sched):
     print(sched, "row0:", float(got[0, 0]), "exact:", exact)
 
 
-@pytest.mark.parametrize("m,sched", [(9, "auto"), (256, "small_m"), (512, "tiled"), (2048, "auto")])
+@pytest.mark.parametrize("m,sched", [(9, "auto"), (256, "small_m"), (128, "auto"), (512, "tiled"), (2048, "auto")])
 def test_run_to_run_bitwise_determinism(gpu, m, sched):
     w, bq, bs = _weight_on(gpu, "square", workloads.square_weight)
     q, s, _, _ = quant_gpu_checked(workloads.square_act(m), gpu, f"square M={m}")
@@ -171,3 +171,21 @@ def test_m_zero_and_rejections(gpu):
     q2 = torch.zeros(4, 200, dtype=torch.uint8, device=gpu)
     with pytest.raises(ValueError):
         bfp8.gemm(q2, s1, bq, bs)
+
+
+def test_tile_plans_back_to_back_with_caller_workspace(gpu):
+    """Tiled GEMMs whose plans differ (128x64, 128x128, 256x128 and 256x256 tiles, ragged M)
+    run back to back with one caller-owned workspace; each must match the oracle."""
+    w, bq, bs = _weight_on(gpu, "square", workloads.square_weight)
+    sizes = [128, 160, 96, 600, 1024, 130, 2048, 4096, 128]
+    need = max(bfp8._native.lib().bfp8_gemm_workspace_bytes(m, 4096, 4096) for m in sizes)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=gpu)
+    bfp8.set_schedule("tiled")
+    for m in sizes:
+        q, s, q_ref, s_ref = quant_gpu_checked(workloads.square_act(m), gpu, f"square M={m}")
+        announce("gemm", f"caller workspace M={m}")
+        c = bfp8.gemm(q, s, bq, bs, workspace=ws)
+        torch.cuda.synchronize()
+        rows = _sample_rows(m, 16, seed=m + 1)
+        _, _, ref_bits, mag = tolerance.reference(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows=rows)
+        tolerance.compare(bits(c)[rows], ref_bits, mag, 4096, f"caller workspace M={m}")

@@ -87,12 +87,16 @@ def test_poisoned_padding_rows_and_empty_blocks(gpu):
 
 
 def test_single_group_equals_dense_tiled(gpu):
-    """G = 1 with no padding is the dense product; both run the tiled schedule, so bitwise equal."""
-    w = workloads.weight(640, 1024, seed=31)
-    x = workloads.act_normal_bf16(256, 1024, seed=32)
-    q, s, _, _ = quant_gpu_checked(x, gpu, "single group")
+    """G = 1 with no padding is the dense product. At 2048 x 2048 the dense tiled plan fills the
+    chip without splitting K, so both sum every output block by block in the same order and
+    must agree bitwise (a split-K plan adds its partial sums in another order)."""
+    m, n, k = 2048, 2048, 1024
+    assert bfp8.schedule_for(m, n, k) == "tiled" and bfp8._native.lib().bfp8_gemm_workspace_bytes(m, n, k) == 0
+    w = workloads.weight(n, k, seed=31)
+    x = workloads.act_normal_bf16(m, k, seed=32)
+    q, s, q_ref, s_ref = quant_gpu_checked(x, gpu, "single group")
     bq_d, bs_d = w.q.to(gpu), w.s.to(gpu)
-    lay = torch.zeros(256, dtype=torch.int32, device=gpu)
+    lay = torch.zeros(m, dtype=torch.int32, device=gpu)
     c_g = _grouped(q, s, bq_d[None], bs_d[None], lay, "G=1")
     bfp8.set_schedule("tiled")
     try:
@@ -101,6 +105,8 @@ def test_single_group_equals_dense_tiled(gpu):
     finally:
         bfp8.set_schedule("auto")
     assert torch.equal(c_g.view(torch.int16), c_d.view(torch.int16))
+    _check_rows(bits(c_g), q_ref, s_ref, w.q.numpy()[None], w.s.numpy()[None], np.zeros(m, np.int32), 24,
+                np.arange(n), "single group")
 
 
 def test_grouped_rejections(gpu):
