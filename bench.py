@@ -46,7 +46,7 @@ N = K = 4096
 SWEEP_M = (1, 8, 9, 16, 24, 32, 64, 128, 160, 192, 224, 256, 512, 1024, 2048, 4096, 8192)
 DOMINANT_M = 8192
 LLC_BYTES = 256 * 2**20
-KERNEL_SOURCES = ["api.hip", "quant_act.hip", "gemm_small.hip", "gemm_tiled.hip", "device_common.h", "launch.h"]
+KERNEL_SOURCES = ["api.hip", "gemm_tiled.hip", "device_common.h", "launch.h"]  # the dominant GEMM's code
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

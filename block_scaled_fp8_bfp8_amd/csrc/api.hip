@@ -170,7 +170,7 @@ bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t 
   if (st != BFP8_OK) return st;
   const bfp8::GemmArgs args{a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, (int)M, (int)N, (int)K, nullptr, 1};
   const int sched = choose_schedule(M, N, K);
-  if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_small(args, (hipStream_t)stream), "gemm_small");
+  if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_ksplit(args, (hipStream_t)stream), "gemm_ksplit");
   return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
 }
 

@@ -57,4 +57,58 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// LDS-only workgroup barrier: orders LDS accesses across the barrier without
+// waiting for outstanding global loads (unlike a full __syncthreads()).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Direct global -> LDS copies: lane l's 16 (or 4) bytes from sbase + voff land at LDS
+// byte address lds + 16 * l (or 4 * l); completion is awaited with wait_copies(). They are
+// issued from inline assembly because the compiler, which cannot tell the copies into one
+// LDS stage from reads of the other, would otherwise drain every copy in flight before
+// each LDS read. The LDS address travels in M0, which the compiler reserves: it is saved
+// and restored inside the same statement.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %2, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(sbase), "v"(voff), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %2, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(sbase), "v"(voff), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent copies have landed.
+template <int N>
+__device__ __forceinline__ void wait_copies_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// XOR swizzle of the 16-byte columns of a 128-byte LDS row. A fragment read has 16 lanes
+// reading the same logical column of the 16 rows of a 16-row block, two 16-byte reads per
+// lane. Measured on gfx950 with the LDS bank-conflict counter: XOR by (r ^ r / 8) % 8, r the
+// row within its block, makes these reads conflict-free, whereas r % 8, (r / 2) % 8 and
+// similar XORs still conflict two ways and halve the LDS read rate. It depends on r alone, so
+// all fragments of a wave share their swizzled offsets.
+__device__ __forceinline__ int lds_swizzle(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
 }  // namespace bfp8

@@ -1,0 +1,199 @@
+// K-split blockwise FP8 GEMM schedule for gfx950 (small and mid M, memory bound).
+//
+// Role: the small-M "single-partition" and mid-M schedules of page "lmdeploy/pull/4830",
+// section "Kernel design", re-derived for CDNA4. At small and mid M the cost is moving the
+// weight matrix B (N*K bytes, from HBM) and the activation rows (from L2) into the CUs; the
+// math is small. So:
+//   * the problem is computed transposed, C^T = B . A^T: the 16 rows of an MFMA's first
+//     operand are weight rows and its 16 columns activation rows; one 16x16x128 FP8 MFMA
+//     covers one 128-wide K block of a 16x16 sub-tile;
+//   * a workgroup owns a BN x BM tile of C^T (BN weight rows, BM activation rows), small
+//     enough that the grid has a workgroup for every CU; its WAVES waves split the tile's
+//     K blocks round-robin (kb = w, w + WAVES, ...), each wave accumulating the whole tile
+//     over its own blocks, so waves never wait for one another inside the K loop;
+//   * each wave copies its K blocks (BN + BM rows of 128 bytes, and the block's BM
+//     activation scales) with the gfx950 direct-to-LDS loads into SLOTS private LDS slots.
+//     These copies read whole 128-byte rows with 8 lanes each, several times the rate of
+//     loading MFMA operands straight from memory (4 rows per lane quad). The wave reads a
+//     block's fragments into registers, refills the slot with its next block and multiplies
+//     while that copy is in flight; the 16-byte columns of each LDS row are XOR-swizzled so
+//     that the fragment reads are free of bank conflicts;
+//   * promotion per K block: acc += P * (As[kb][m] * Bs[n/128][kb]) with one FMA per
+//     element (BN is at most 128 and tiles are BN-aligned, so a wave's weight rows share
+//     one scale strip);
+//   * the waves' partial tiles are summed through LDS in a fixed wave order, which keeps
+//     results bitwise reproducible without atomics or a global workspace, and each sum is
+//     rounded once to bf16.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bfp8 {
+
+namespace {
+
+template <int TN, int TM, int WAVES, int SLOTS>
+__global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) {
+  constexpr int BN = 16 * TN, BM = 16 * TM;
+  constexpr int kRows = BN + BM;
+  constexpr int kSlot = kRows * kBlock;           // bytes per slot
+  constexpr int kPieces = kRows / 8;              // 1 KB (8-row) copies per K block
+  constexpr int kAsCopies = (BM + 63) / 64;       // 64-lane scale copies per K block
+  constexpr int kPerBlock = kPieces + kAsCopies;  // copies issued per K block
+  constexpr int kTileFloats = BN * BM;
+  static_assert(kBlock % BN == 0, "a wave's weight rows must share one scale strip");
+  static_assert(kTileFloats * 4 <= SLOTS * kSlot, "the reduction reuses the wave's slots");
+  static_assert(SLOTS >= 1 && SLOTS <= 3 && (SLOTS - 1) * kPerBlock < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t slots[WAVES][SLOTS][kSlot];
+  __shared__ __attribute__((aligned(16))) float as_slots[WAVES][SLOTS][kAsCopies * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, kc = lane >> 4;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int M = args.M, N = args.N;
+  const int KB = args.K / kBlock;
+  const int nkb = KB > w ? (KB - w + WAVES - 1) / WAVES : 0;  // this wave's blocks: w + i * WAVES
+
+  // Copy plan: piece j is slot rows [8j, 8j + 8); lane l lands at row 8j + l/8, physical
+  // 16-byte column l%8, so it loads logical column (l%8) ^ swizzle(row) of that row. Rows
+  // past N or M are clamped to the last row (their results are never stored).
+  uint32_t coff[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    const int row = j * 8 + (lane >> 3);
+    const int lcol = (lane & 7) ^ lds_swizzle(row);
+    const bool is_b = j * 8 < BN;  // uniform: BN is a multiple of 16
+    const int src_row = is_b ? min(n0 + row, N - 1) : min(m0 + row - BN, M - 1);
+    coff[j] = (uint32_t)((int64_t)src_row * (is_b ? args.ldb : args.lda) + lcol * 16);
+  }
+  uint32_t as_voff[kAsCopies];
+#pragma unroll
+  for (int c = 0; c < kAsCopies; ++c) as_voff[c] = (uint32_t)min(m0 + c * 64 + lane, M - 1) * 4u;
+
+  auto issue = [&](int slot, int kb) __attribute__((always_inline)) {
+    const uint8_t* bsrc = args.b + (int64_t)kb * kBlock;
+    const uint8_t* asrc = args.a + (int64_t)kb * kBlock;
+    const uint32_t dst = lds_addr(&slots[w][slot][0]);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) copy16_to_lds(j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
+#pragma unroll
+    for (int c = 0; c < kAsCopies; ++c)
+      copy4_to_lds(args.as + (int64_t)kb * args.ld_as, as_voff[c], lds_addr(&as_slots[w][slot][c * 64]));
+  };
+
+  // Fragment rows come in 16-row blocks, so every row a lane reads has row % 16 == r.
+  const int fsw = lds_swizzle(r);
+  const uint32_t off_lo = (uint32_t)(r * kBlock + (((2 * kc) ^ fsw) << 4));
+  const uint32_t off_hi = (uint32_t)(r * kBlock + (((2 * kc + 1) ^ fsw) << 4));
+  auto frag_at = [&](const uint8_t* slot, int row0) __attribute__((always_inline)) -> v8i {
+    const v4i lo = *reinterpret_cast<const v4i*>(slot + off_lo + row0 * kBlock);
+    const v4i hi = *reinterpret_cast<const v4i*>(slot + off_hi + row0 * kBlock);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // Weight scale strip of the tile (scalar loads through the constant address space).
+  const __attribute__((address_space(4))) float* bsp =
+      (const __attribute__((address_space(4))) float*)(args.bs + (int64_t)(min(n0, N - 1) / kBlock) * args.ld_bs);
+
+  float acc[TN][TM][4];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[tn][tm][e] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s)
+    if (s < nkb) issue(s, w + s * WAVES);
+
+  for (int i = 0; i < nkb; ++i) {
+    const int kb = w + i * WAVES;
+    const int slot = i % SLOTS;
+    // Block i has landed once only the copies of the SLOTS - 1 blocks issued after it remain.
+    if (i + SLOTS - 1 < nkb) {
+      wait_copies_upto<(SLOTS - 1) * kPerBlock>();
+    } else {
+      wait_copies();
+    }
+    const uint8_t* sl = &slots[w][slot][0];
+    v8i fb[TN], fa[TM];
+    float sc[TM];
+    const float bs_kb = bsp[kb];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_at(sl, tn * 16);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      fa[tm] = frag_at(sl, BN + tm * 16);
+      sc[tm] = as_slots[w][slot][tm * 16 + r] * bs_kb;
+    }
+    // The slot is refilled only after this wave's reads of it have returned.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (i + SLOTS < nkb) issue(slot, kb + SLOTS * WAVES);
+    // Multiply, promoting sub-tile t - 2 after issuing the MFMA of sub-tile t (the result
+    // is then at least one MFMA old); a scheduling barrier per step keeps this order.
+    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;
+    auto promote = [&](int u, const v4f& pu) __attribute__((always_inline)) {
+      const int un = u / TM, um = u % TM;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], sc[um], acc[un][um][e]);
+      asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
+    };
+#pragma unroll
+    for (int t = 0; t < TN * TM; ++t) {
+      const v4f p = mfma_block(fb[t / TM], fa[t % TM]);
+      if (t >= 2) promote(t - 2, p2);
+      __builtin_amdgcn_sched_barrier(0);
+      p2 = p1;
+      p1 = p;
+    }
+    if constexpr (TN * TM >= 2) promote(TN * TM - 2, p2);
+    promote(TN * TM - 1, p1);
+  }
+
+  // Fixed-order reduction of the waves' partial tiles through LDS. Wave w's partial goes to
+  // its own slots, which no other wave touches and in which none of its copies is pending.
+  float* red = reinterpret_cast<float*>(&slots[w][0][0]);
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      *reinterpret_cast<v4f*>(red + ((tn * TM + tm) * 64 + lane) * 4) =
+          v4f{acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
+  __syncthreads();
+
+  const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
+  for (int q = threadIdx.x; q < TN * TM * 64; q += WAVES * 64) {
+    const int ln = q & 63, tile = q >> 6;  // tile = tn * TM + tm
+    v4f v = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(&slots[0][0][0]) + q * 4);
+    for (int ww = 1; ww < WAVES; ++ww)
+      v += *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(&slots[ww][0][0]) + q * 4);
+    const int m = m0 + (tile % TM) * 16 + (ln & 15);
+    const int n = n0 + (tile / TM) * 16 + 4 * (ln >> 4);
+    if (m < M && n < N) store_bf16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <int TN, int TM, int WAVES, int SLOTS>
+hipError_t launch_ksplit_cfg(const GemmArgs& args, hipStream_t stream) {
+  const dim3 grid((unsigned)((args.N + 16 * TN - 1) / (16 * TN)), (unsigned)((args.M + 16 * TM - 1) / (16 * TM)));
+  hipLaunchKernelGGL((gemm_ksplit_kernel<TN, TM, WAVES, SLOTS>), grid, dim3(WAVES * 64), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile per M, measured on the N = K = 4096 sweep (cold weights): 16x16 up to M = 16 (two
+// slots per wave), 16x32 and 32x32 up to 32 and 64, then 64x32 and 64x64 (one slot per
+// wave). Every choice gives 256 or more workgroups at N = 4096.
+hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream) {
+  if (args.M <= 16) return launch_ksplit_cfg<1, 1, 8, 2>(args, stream);
+  if (args.M <= 32) return launch_ksplit_cfg<1, 2, 8, 2>(args, stream);
+  if (args.M <= 64) return launch_ksplit_cfg<2, 2, 8, 2>(args, stream);
+  if (args.M <= 128) return launch_ksplit_cfg<4, 2, 8, 1>(args, stream);
+  return launch_ksplit_cfg<4, 4, 8, 1>(args, stream);
+}
+
+}  // namespace bfp8

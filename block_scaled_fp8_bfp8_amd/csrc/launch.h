@@ -39,10 +39,11 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K);
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
 
-// Largest M the small-M schedule covers in one pass over the weights.
-constexpr int kSmallMaxM = 64;
+// Largest M the automatic choice gives to the K-split schedule (BFP8_SCHED_SMALL_M); the
+// tiled schedule takes larger M.
+constexpr int kSmallMaxM = 256;
 
-hipError_t launch_gemm_small(const GemmArgs& args, hipStream_t stream);
+hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream);
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream);
 

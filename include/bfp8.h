@@ -74,13 +74,13 @@ typedef enum bfp8_in_dtype {
 } bfp8_in_dtype_t;
 
 /* GEMM schedules (page "lmdeploy/pull/4830", section "Kernel design": one schedule
- * per M range). AUTO picks by M and shape; the others force one schedule at any M
- * (for tests and benchmarks). Each schedule is deterministic on its own; the
- * schedules sum the K blocks in different orders, so they agree to FP32
+ * per M range). AUTO gives M <= 256 to SMALL_M and larger M to TILED; the others force
+ * one schedule at any M (for tests and benchmarks). Each schedule is deterministic on
+ * its own; the schedules sum the K blocks in different orders, so they agree to FP32
  * rounding, not bitwise. */
 typedef enum bfp8_schedule {
   BFP8_SCHED_AUTO = 0,
-  BFP8_SCHED_SMALL_M = 1, /* weight-streaming, K split across the waves of a workgroup */
+  BFP8_SCHED_SMALL_M = 1, /* small/mid M: K blocks split across the waves of a workgroup */
   BFP8_SCHED_TILED = 2,   /* LDS-tiled MFMA kernel, one output tile per workgroup */
   BFP8_SCHED_COUNT_ = 3
 } bfp8_schedule_t;
