@@ -42,6 +42,7 @@ bfp8_status_t ok() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel row index in int32
+constexpr int64_t kMaxOperandSpan = ((int64_t)1 << 32) - 1;  // in-kernel copy offsets are 32-bit
 
 // Device check: the current device must be a gfx950. Cached per device id.
 bfp8_status_t check_device() {
@@ -95,6 +96,10 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, in
   if (!aligned(a, 16) || !aligned(b, 16)) return fail(BFP8_ERR_MISALIGNED, "a and b must be 16-byte aligned");
   if (!aligned(as, 4) || !aligned(bs, 4)) return fail(BFP8_ERR_MISALIGNED, "as and bs must be 4-byte aligned");
   if (!aligned(c, 2)) return fail(BFP8_ERR_MISALIGNED, "c must be 2-byte aligned");
+  // The kernels address a row inside A, and inside one weight matrix of B, with a 32-bit
+  // byte offset from the operand's base.
+  if ((N - 1) * ldb + K > kMaxOperandSpan || (M > 0 && (M - 1) * lda + K > kMaxOperandSpan))
+    return fail(BFP8_ERR_UNSUPPORTED, "A (M x lda) and each weight matrix (N x ldb) must span less than 4 GiB");
   const size_t need = grouped ? 0 : bfp8_gemm_workspace_bytes(M, N, K);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);

@@ -21,6 +21,8 @@
 //   * promotion per K block: acc += P * (As[kb][m] * Bs[n/128][kb]) with one FMA per
 //     element (BN is at most 128 and tiles are BN-aligned, so a wave's weight rows share
 //     one scale strip);
+//   * the workgroups that share weight rows walk their K blocks from different starting
+//     points, so that they do not all wait on the same HBM reads;
 //   * the waves' partial tiles are summed through LDS in a fixed wave order, which keeps
 //     results bitwise reproducible without atomics or a global workspace, and each sum is
 //     rounded once to bf16.
@@ -105,12 +107,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[tn][tm][e] = 0.f;
 
+  // The workgroups of one weight strip (blockIdx.y = 0 .. gridDim.y - 1) start at different
+  // points of their K loops, so that at any time they request different weight blocks: the
+  // first to touch a block fetches it from HBM while the others, later, find it in L2,
+  // rather than all waiting on the same HBM reads. A wave still visits each of its blocks
+  // once, in a cyclically shifted order.
+  const int rot = nkb > 0 ? (int)((int64_t)blockIdx.y * nkb / gridDim.y) : 0;
+  auto block_of = [&](int i) __attribute__((always_inline)) {
+    const int j = i + rot < nkb ? i + rot : i + rot - nkb;
+    return w + j * WAVES;
+  };
+
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s)
-    if (s < nkb) issue(s, w + s * WAVES);
+    if (s < nkb) issue(s, block_of(s));
 
   for (int i = 0; i < nkb; ++i) {
-    const int kb = w + i * WAVES;
+    const int kb = block_of(i);
     const int slot = i % SLOTS;
     // Block i has landed once only the copies of the SLOTS - 1 blocks issued after it remain.
     if (i + SLOTS - 1 < nkb) {
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     }
     // The slot is refilled only after this wave's reads of it have returned.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (i + SLOTS < nkb) issue(slot, kb + SLOTS * WAVES);
+    if (i + SLOTS < nkb) issue(slot, block_of(i + SLOTS));
     // Multiply, promoting sub-tile t - 2 after issuing the MFMA of sub-tile t (the result
     // is then at least one MFMA old); a scheduling barrier per step keeps this order.
     v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;

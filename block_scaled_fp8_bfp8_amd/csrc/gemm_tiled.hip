@@ -53,9 +53,9 @@ __device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int 
   tn = r / gm;
 }
 
-template <int BN, int BM, int WGN, int WGM, int STAGES, bool kGrouped>
-__global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs args) {
-  constexpr int kWaves = WGN * WGM;
+template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped>
+__global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs args) {
+  constexpr int kWaves = WGN * WGM;  // waves per K group
   constexpr int WN = BN / WGN, WM = BM / WGM;
   constexpr int TN = WN / 16, TM = WM / 16;
   constexpr int kRows = BN + BM;             // 128-byte LDS rows per stage: weights, then activations
@@ -67,19 +67,24 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   static_assert(kBlock % WN == 0 && BN % WN == 0, "a wave's N range must lie inside one weight-scale strip");
   static_assert(!kGrouped || kBlock % BM == 0, "grouped: a workgroup's rows must lie in one 128-row block");
 
-  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 pipeline stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES][kStage];
-  __shared__ __attribute__((aligned(16))) float as_lds[STAGES][BM];
+  static_assert(STAGES >= 2 && STAGES <= 8, "2 to 8 pipeline stages");
+  static_assert(KG == 1 || KG == 2, "one or two K groups");
+  static_assert(KG == 1 || BN * BM * 4 <= KG * STAGES * kStage, "the K-group sum reuses the stages");
+  // K groups: KG sets of WGN x WGM waves; group g multiplies the K blocks kb = g, g + KG, ...
+  // through its own LDS ring, and the groups' tiles are summed in group order at the end.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[KG][STAGES][kStage];
+  __shared__ __attribute__((aligned(16))) float as_lds[KG][STAGES][BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wg / kWaves, w = wg % kWaves;  // K group, wave within the group
   const int wn = w % WGN, wm = w / WGN;
   const int M = args.M, N = args.N;
 
   const int n_tiles = (N + BN - 1) / BN;
   const int m_tiles = (M + BM - 1) / BM;
-  const int KB = args.K / kBlock;
+  const int KB = args.K / kBlock / KG;  // K blocks per group (the plan makes K / 128 a multiple of KG)
   int tile_n, tile_m;
   map_tile(blockIdx.x, n_tiles, m_tiles, 8, tile_n, tile_m);
   const int n0 = tile_n * BN, m0 = tile_m * BM;
@@ -122,11 +127,13 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   uint32_t stage_lds[STAGES], as_lds_addr[STAGES];
 #pragma unroll
   for (int i = 0; i < STAGES; ++i) {
-    stage_lds[i] = lds_addr(&smem[i][0]);
-    as_lds_addr[i] = lds_addr(&as_lds[i][0]);
+    stage_lds[i] = lds_addr(&smem[g][i][0]);
+    as_lds_addr[i] = lds_addr(&as_lds[g][i][0]);
   }
+  // Block index in K of this group's local block i.
+  auto gkb = [&](int i) __attribute__((always_inline)) { return i * KG + g; };
   auto issue_copies = [&](int buf, int kb_local) __attribute__((always_inline)) {
-    const int kb = kb_local;
+    const int kb = gkb(kb_local);
     const uint8_t* bsrc = bmat + (int64_t)kb * kBlock;
     const uint8_t* asrc = args.a + (int64_t)kb * kBlock;
     const uint32_t dst = stage_lds[buf] + (uint32_t)(prow_base * kBlock);
@@ -138,13 +145,13 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   };
   // One piece of a block's copy (for spreading a block's copies over the multiply steps).
   auto issue_piece = [&](int buf, int kb_local, int j) __attribute__((always_inline)) {
-    const int kb = kb_local;
+    const int kb = gkb(kb_local);
     const uint8_t* src = prow_base + j * 8 < BN ? bmat + (int64_t)kb * kBlock : args.a + (int64_t)kb * kBlock;
     copy16_to_lds(src, coff[j], stage_lds[buf] + (uint32_t)((prow_base + j * 8) * kBlock));
   };
   auto issue_scales = [&](int buf, int kb_local) __attribute__((always_inline)) {
     if (copies_as)
-      copy4_to_lds(args.as + (int64_t)kb_local * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
+      copy4_to_lds(args.as + (int64_t)gkb(kb_local) * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
   };
 
   const int r = lane & 15, kc = lane >> 4;
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   auto frag_a = [&](const uint8_t* stage, int tm) __attribute__((always_inline)) {
     return frag_at(stage, BN + wm * WM + tm * 16);
   };
-  auto act_scale = [&](int slot, int tm) __attribute__((always_inline)) { return as_lds[slot][wm * WM + tm * 16 + r]; };
+  auto act_scale = [&](int slot, int tm) __attribute__((always_inline)) { return as_lds[g][slot][wm * WM + tm * 16 + r]; };
 
   // Software pipeline. Sub-tiles are visited activation-row by activation-row: step
   // t = tm * TN + tn multiplies weight fragment tn by activation fragment tm. Block kb is
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   // each fragment right after its last use in block kb (activation fragment tm after row tm,
   // weight fragment tn in the last row). LDS stage kb % STAGES is free once block kb has been
   // read (the barrier ending iteration kb - 1), so iteration kb refills it with block
-  // kb + STAGES, its copies spread over the steps, and waits at its end for block kb + 2,
+  // kb + STAGES, one copy per step, and waits at its end for block kb + 2,
   // which iteration kb + 1 reads.
   v8i fa[TM];
   v8i fb[TN];
@@ -212,16 +219,16 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
     // The last iteration also reads a (stale, in-bounds) stage, which keeps the steps free of
     // branches; those registers are never used.
     const int nslot = (kb + 1) % STAGES;
-    const uint8_t* nstage = &smem[nslot][0];
-    const float bs_next = bsp[min(kb + 1, KB - 1)];
+    const uint8_t* nstage = &smem[g][nslot][0];
+    const float bs_next = bsp[gkb(min(kb + 1, KB - 1))];
     float sc[TM];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) sc[tm] = sa[tm] * bsv;
     if constexpr (kSteady) issue_scales(cslot, kb + STAGES);
     // Step t issues the MFMA of sub-tile t, the promotion FMAs of sub-tile t - 2 (whose
     // result is then at least one MFMA old), its share of the copies and of the next block's
-    // LDS reads; a scheduling barrier per step keeps this order. Copies go out in the first
-    // half of the steps, so that they land before the iteration ends.
+    // LDS reads; a scheduling barrier per step keeps this order. Copies go out one per step
+    // from the first, so that they have most of the iteration to land.
     v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;
     auto promote = [&](int u, const v4f& pu) __attribute__((always_inline)) {
       const int um = u / TN, un = u % TN;
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
       // since their results are only read in the next K block.
       asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
     };
-    constexpr int kCopySteps = kSteps / 2 > kCopies ? kSteps / 2 : kCopies;
+    constexpr int kCopySteps = kCopies;  // one copy per step from the first (kCopies <= kSteps)
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
       const int tm = t / TN, tn = t % TN;
@@ -267,17 +274,37 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   lds_barrier();
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    fa[tm] = frag_a(&smem[0][0], tm);
+    fa[tm] = frag_a(&smem[g][0][0], tm);
     sa[tm] = act_scale(0, tm);
   }
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_b(&smem[0][0], tn);
-  bsv = bsp[0];
+  for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_b(&smem[g][0][0], tn);
+  bsv = bsp[g];
   // every wave has read stage 0 before iteration 0 refills it
   lds_barrier();
   int kb = 0;
   for (; kb + STAGES < KB; ++kb) iter(kb, std::true_type{});
   for (; kb < KB; ++kb) iter(kb, std::false_type{});
+
+  if constexpr (KG == 2) {
+    // Sum of the two groups' tiles, group 0 + group 1: group 1 parks its tile in the stages
+    // (every wave has finished with them at the last barrier), group 0 adds and stores.
+    float* red = reinterpret_cast<float*>(&smem[0][0][0]);
+    if (g == 1) {
+#pragma unroll
+      for (int t = 0; t < TN * TM; ++t)
+        *reinterpret_cast<v4f*>(red + ((w * TN * TM + t) * 64 + lane) * 4) =
+            v4f{acc[t / TM][t % TM][0], acc[t / TM][t % TM][1], acc[t / TM][t % TM][2], acc[t / TM][t % TM][3]};
+    }
+    lds_barrier();
+    if (g == 1) return;
+#pragma unroll
+    for (int t = 0; t < TN * TM; ++t) {
+      const v4f o = *reinterpret_cast<const v4f*>(red + ((w * TN * TM + t) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t / TM][t % TM][e] += o[e];
+    }
+  }
 
   const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
 #pragma unroll
@@ -296,10 +323,10 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs arg
   }
 }
 
-template <int BN, int BM, int WGN, int WGM, int STAGES, bool G>
+template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool G>
 hipError_t launch_tiled_cfg(const GemmArgs& args, int tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, G>), dim3((unsigned)tiles), dim3(WGN * WGM * 64), 0,
-                     stream, args);
+  hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G>), dim3((unsigned)tiles),
+                     dim3(KG * WGN * WGM * 64), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -323,16 +350,16 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
   (void)workspace;
   const TiledPlan p = plan_tiled(args.M, args.N, args.K);
-  if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, false>(args, p.tiles, stream);
-  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, false>(args, p.tiles, stream);
-  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, false>(args, p.tiles, stream);
-  return launch_tiled_cfg<128, 64, 2, 2, 3, false>(args, p.tiles, stream);
+  if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, 1, false>(args, p.tiles, stream);
+  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false>(args, p.tiles, stream);
+  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false>(args, p.tiles, stream);
+  return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false>(args, p.tiles, stream);
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream) {
   const int tiles = (int)(((args.N + 255) / 256) * (args.M / 128));
-  return launch_tiled_cfg<256, 128, 4, 2, 3, true>(args, tiles, stream);
+  return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true>(args, tiles, stream);
 }
 
 }  // namespace bfp8

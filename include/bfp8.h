@@ -40,6 +40,9 @@
  *   - K must be a positive multiple of 128 (the scale grid's K blocks are then
  *     whole); other K return BFP8_ERR_UNSUPPORTED.
  *   - Only gfx950 devices are supported (BFP8_ERR_UNSUPPORTED otherwise).
+ *   - Size: M, N, K are at most 2^30, and the activation matrix ((M - 1) * lda + K
+ *     bytes) and each weight matrix ((N - 1) * ldb + K bytes) span less than 4 GiB;
+ *     larger requests return BFP8_ERR_UNSUPPORTED.
  *   - Determinism: for fixed inputs and sizes every result is bitwise identical
  *     from run to run (fixed reduction orders, no floating-point atomics).
  *   - Thread safety: calls may be made from several host threads; the message

@@ -80,6 +80,8 @@ def _gemm(lib, a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=2, c=C,
     (dict(as_=AS + 2), _native.BFP8_ERR_MISALIGNED),
     (dict(bs=BS + 1), _native.BFP8_ERR_MISALIGNED),
     (dict(c=C + 1), _native.BFP8_ERR_MISALIGNED),
+    (dict(N=(1 << 24) + 1, ldb=256, ldc=(1 << 24) + 1), _native.BFP8_ERR_UNSUPPORTED),  # B spans 4 GiB + 256 B
+    (dict(M=(1 << 24) + 1, lda=256, ld_as=(1 << 24) + 1), _native.BFP8_ERR_UNSUPPORTED),  # A likewise
 ])
 def test_gemm_rejections(lib, kw, status):
     st = _gemm(lib, **kw)
