@@ -39,6 +39,13 @@ namespace bfp8 {
 
 namespace {
 
+// Largest divisor of n that is at most cap (0 if cap < 1).
+constexpr int largest_divisor_upto(int n, int cap) {
+  for (int d = cap < n ? cap : n; d >= 1; --d)
+    if (n % d == 0) return d;
+  return 0;
+}
+
 // Tile of workgroup `bid`: each XCD (bid % 8) owns a contiguous run of the tiles,
 // ordered in groups of `group_m` M-tiles with the M-tile index fastest.
 __device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int group_m, int& tn, int& tm) {
@@ -304,6 +311,66 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[t / TM][t % TM][e] += o[e];
     }
+  }
+
+  // Output. When C rows allow 16-byte stores, each wave stages its tile in LDS as bf16 rows
+  // (padded by 16 bytes, which keeps the transposing writes free of bank conflicts) and then
+  // stores whole row segments, WN * 2 contiguous bytes per row; storing straight from the
+  // MFMA layout writes 16 rows x 32 bytes per instruction and reaches memory as partial
+  // lines. Each wave uses its own part of the stages (after the K-group sum's area), in
+  // chunks of 16-row blocks that fit.
+  const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
+  if (vec16) {
+    constexpr int kRowBytes = WN * 2 + 16;
+    constexpr int kBase = KG == 2 ? BN * BM * 4 : 0;
+    constexpr int kFitRows = (KG * STAGES * kStage - kBase) / (kWaves * kRowBytes);
+    constexpr int kChunkTM = largest_divisor_upto(TM, kFitRows / 16);
+    static_assert(kChunkTM >= 1 && TM % kChunkTM == 0, "output staging must fit the LDS stages");
+    constexpr int kLanesPerRow = WN / 8;  // 16 bytes (8 outputs) per lane
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
+    static_assert(64 % kLanesPerRow == 0 && (kChunkTM * 16) % kRowsPerPass == 0, "whole passes");
+    uint8_t* out_lds = &smem[0][0][0] + kBase + w * (kChunkTM * 16 * kRowBytes);
+#pragma unroll
+    for (int c0 = 0; c0 < TM; c0 += kChunkTM) {
+#pragma unroll
+      for (int tm = c0; tm < c0 + kChunkTM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          uint2 pk;
+          pk.x = f32_to_bf16_rne(acc[tn][tm][0]) | (f32_to_bf16_rne(acc[tn][tm][1]) << 16);
+          pk.y = f32_to_bf16_rne(acc[tn][tm][2]) | (f32_to_bf16_rne(acc[tn][tm][3]) << 16);
+          *reinterpret_cast<uint2*>(out_lds + ((tm - c0) * 16 + r) * kRowBytes + (tn * 16 + 4 * kc) * 2) = pk;
+        }
+      // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
+      // wave's accesses in order, and this keeps the compiler from reordering them.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int pass = 0; pass < kChunkTM * 16 / kRowsPerPass; ++pass) {
+        const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+        const int seg = lane % kLanesPerRow;
+        const v4i v = *reinterpret_cast<const v4i*>(out_lds + row * kRowBytes + seg * 16);
+        const int m = m0 + wm * WM + c0 * 16 + row;
+        const int n = n0 + wn * WN + seg * 8;
+        bool row_ok = m < M;
+        if constexpr (kGrouped) row_ok = row_ok && args.layout[m] >= 0;
+        if (row_ok && n < N) {
+          uint16_t* cp = args.c + (int64_t)m * args.ldc + n;
+          if (n + 8 <= N) {
+            *reinterpret_cast<v4i*>(cp) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) cp[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+    return;
   }
 
   const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
