@@ -10,6 +10,7 @@ there is no fallback path.
     q, s = quant_act(x)                 # x: [M, K] fp32 or bf16 (cuda)
     c = gemm(q, s, w_q, w_s)            # c: [M, N] bf16
     c = grouped_gemm_contiguous(q, s, w_q, w_s, layout)
+    y = linear(x_bf16, w_q, w_s, bias)  # quantize + GEMM (+ bias), bf16 out
 """
 
 from __future__ import annotations
@@ -22,7 +23,7 @@ from . import _native
 from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
-    "quant_act", "gemm", "grouped_gemm_contiguous", "set_schedule", "get_schedule", "schedule_for",
+    "quant_act", "gemm", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
 
@@ -74,10 +75,11 @@ _workspaces: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> tuple[int, int]:
-    """(pointer, size) of a zero-filled workspace for the current stream, grown on demand.
+    """(pointer, size) of a workspace for the current stream, grown on demand.
 
-    The GEMM leaves its arrival counters zero after each call, so one buffer per (device,
-    stream) is reused by every call ordered on that stream."""
+    Its contents do not persist between calls (the linear layer's quantized activations are
+    written and read within one call), so one buffer per (device, stream) serves every call
+    ordered on that stream."""
     if nbytes == 0:
         return 0, 0
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
@@ -194,6 +196,54 @@ def grouped_gemm_contiguous(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Ten
         _stream(a_q.device))
     _check(st, "bfp8_grouped_gemm_contiguous")
     return out
+
+
+def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Tensor | None = None,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """FP8 linear layer, bf16 in and out: per-1x128-group quantization of x [M, K] (bf16), the
+    blockwise FP8 product with w_q [N, K] / w_s [ceil(N/128), K/128], then bf16(out + bias).
+
+    workspace: optional uint8 buffer of at least bfp8_linear_workspace_bytes(M, N, K) bytes
+    (holds the quantized activations); by default one buffer per (device, stream) is kept."""
+    if x.dtype != torch.bfloat16:
+        raise NotImplementedError(f"linear takes bfloat16 activations (bf16 output), got {x.dtype}")
+    _require(x, "x", torch.bfloat16, 2)
+    w_q = _as_u8(w_q, "w_q")
+    _require(w_q, "w_q", torch.uint8, 2)
+    _require(w_s, "w_s", torch.float32, 2)
+    if x.stride(1) != 1 or w_q.stride(1) != 1 or w_s.stride(1) != 1:
+        raise ValueError("x, w_q and w_s must be contiguous along K")
+    m, k = x.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError(f"x and w_q disagree on K: {k} vs {w_q.shape[1]}")
+    if tuple(w_s.shape) != (-(-n // 128), -(-k // 128)):
+        raise ValueError(f"w_s shape {tuple(w_s.shape)} does not match N={n}, K={k}")
+    if bias is not None:
+        _require(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != n or bias.stride(0) != 1:
+            raise ValueError("bias must be a contiguous bf16 vector of length N")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _require(out, "out", torch.bfloat16, 2)
+    if out.stride(1) != 1:
+        raise ValueError("out must be contiguous along N")
+    lib = _native.lib()
+    if workspace is None:
+        ws_ptr, ws_bytes = _workspace(x.device, lib.bfp8_linear_workspace_bytes(m, n, k))
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib.bfp8_linear(x.data_ptr(), _native.BFP8_IN_BF16, m, k, x.stride(0), w_q.data_ptr(), w_q.stride(0),
+                         w_s.data_ptr(), w_s.stride(0), bias.data_ptr() if bias is not None else None,
+                         out.data_ptr(), out.stride(0), n, ws_ptr or None, ws_bytes, _stream(x.device))
+    _check(st, "bfp8_linear")
+    return out
+
+
+def linear_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Bytes of device workspace that linear() needs for an [m, k] x [n, k] layer."""
+    return _native.lib().bfp8_linear_workspace_bytes(m, n, k)
 
 
 def set_schedule(name: str) -> None:

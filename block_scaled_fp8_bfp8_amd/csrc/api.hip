@@ -106,6 +106,35 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, in
   return BFP8_OK;
 }
 
+// Arguments of the activation quantizer (no device access).
+bfp8_status_t check_quant_args(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* q,
+                               int64_t ldq, const float* as, int64_t ld_as) {
+  if (x_dtype != BFP8_IN_F32 && x_dtype != BFP8_IN_BF16)
+    return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is neither BFP8_IN_F32 nor BFP8_IN_BF16", x_dtype);
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
+  if (K % bfp8::kBlock != 0)
+    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128", (long long)K);
+  if (M > kMaxDim || K > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M and K must each be at most 2^30");
+  if (M == 0) return ok();
+  if (!x || !q || !as) return fail(BFP8_ERR_INVALID_ARGUMENT, "x, q and as must not be NULL");
+  if (ldx < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldq < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldq = %lld < K = %lld", (long long)ldq, (long long)K);
+  if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
+  const int64_t esize = x_dtype == BFP8_IN_F32 ? 4 : 2;
+  if ((ldx * esize) % 16 || ldq % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(BFP8_ERR_MISALIGNED, "x and q must be 16-byte aligned");
+  if (!aligned(as, 4)) return fail(BFP8_ERR_MISALIGNED, "as must be 4-byte aligned");
+  return ok();
+}
+
+// Workspace of the linear layer: the codes q [M][K] at offset 0, the scales As [K/128][M]
+// after them, then the GEMM's own workspace; each part 256-byte aligned.
+struct LinearLayout {
+  size_t as_off, gemm_off, total;
+};
+LinearLayout linear_layout(int64_t M, int64_t N, int64_t K);
+
 int choose_schedule(int64_t M, int64_t /*N*/, int64_t /*K*/) {
   const int forced = g_schedule.load(std::memory_order_relaxed);
   if (forced != BFP8_SCHED_AUTO) return forced;
@@ -135,23 +164,9 @@ const char* bfp8_last_error_message(void) { return g_message.c_str(); }
 
 bfp8_status_t bfp8_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                              float* as, int64_t ld_as, void* stream) {
-  if (x_dtype != BFP8_IN_F32 && x_dtype != BFP8_IN_BF16)
-    return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is neither BFP8_IN_F32 nor BFP8_IN_BF16", x_dtype);
-  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
-  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
-  if (K % bfp8::kBlock != 0)
-    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128", (long long)K);
-  if (M > kMaxDim || K > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M and K must each be at most 2^30");
-  if (M == 0) return ok();
-  if (!x || !q || !as) return fail(BFP8_ERR_INVALID_ARGUMENT, "x, q and as must not be NULL");
-  if (ldx < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
-  if (ldq < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldq = %lld < K = %lld", (long long)ldq, (long long)K);
-  if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
-  const int64_t esize = x_dtype == BFP8_IN_F32 ? 4 : 2;
-  if ((ldx * esize) % 16 || ldq % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
-  if (!aligned(x, 16) || !aligned(q, 16)) return fail(BFP8_ERR_MISALIGNED, "x and q must be 16-byte aligned");
-  if (!aligned(as, 4)) return fail(BFP8_ERR_MISALIGNED, "as must be 4-byte aligned");
-  bfp8_status_t st = check_device();
+  bfp8_status_t st = check_quant_args(x, x_dtype, M, K, ldx, q, ldq, as, ld_as);
+  if (st != BFP8_OK || M == 0) return st;
+  st = check_device();
   if (st != BFP8_OK) return st;
   return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, (hipStream_t)stream),
                   "quant_act");
@@ -164,6 +179,34 @@ size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return bfp8::plan_tiled(M, N, K).workspace_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Launch the dense GEMM (arguments already validated) with the schedule for this shape.
+bfp8_status_t launch_dense(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
+                           int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace, void* stream) {
+  const bfp8::GemmArgs args{a,      lda,    as,     ld_as,   b, ldb, bs, ld_bs, c,
+                            ldc,    (int)M, (int)N, (int)K,  nullptr, 1, bias};
+  const int sched = choose_schedule(M, N, K);
+  if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_ksplit(args, (hipStream_t)stream), "gemm_ksplit");
+  return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
+}
+
+LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  LinearLayout L;
+  L.as_off = up((size_t)M * (size_t)K);
+  L.gemm_off = L.as_off + up((size_t)4 * (size_t)M * (size_t)(K / bfp8::kBlock));
+  L.total = L.gemm_off + bfp8_gemm_workspace_bytes(M, N, K);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
 bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b, int64_t ldb,
                         const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream) {
@@ -173,10 +216,7 @@ bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t 
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
-  const bfp8::GemmArgs args{a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, (int)M, (int)N, (int)K, nullptr, 1};
-  const int sched = choose_schedule(M, N, K);
-  if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_ksplit(args, (hipStream_t)stream), "gemm_ksplit");
-  return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
+  return launch_dense(a, lda, as, ld_as, b, ldb, bs, ld_bs, nullptr, c, ldc, M, N, K, workspace, stream);
 }
 
 bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
@@ -200,6 +240,49 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
   const bfp8::GemmArgs args{a,   lda, as,     ld_as,  b,      ldb,           bs,     ld_bs,  c,
                             ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G};
   return launched(bfp8::launch_grouped_tiled(args, (hipStream_t)stream), "grouped_gemm_tiled");
+}
+
+size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % bfp8::kBlock != 0) return 0;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  return linear_layout(M, N, K).total;
+}
+
+bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
+                          int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
+                          int64_t ldc, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x_dtype != BFP8_IN_BF16)
+    return fail(BFP8_ERR_UNSUPPORTED, "the linear layer takes bf16 activations (its output is bf16), got x_dtype %d",
+                x_dtype);
+  if (!aligned(bias, 2)) return fail(BFP8_ERR_MISALIGNED, "bias must be 2-byte aligned");
+  if (workspace && !aligned(workspace, 256)) return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  // Shapes first (a negative or oversized size must not reach the workspace arithmetic).
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
+  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
+  if (K % bfp8::kBlock != 0) return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128", (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(BFP8_ERR_UNSUPPORTED, "M, N and K must each be at most 2^30");
+  const size_t need = bfp8_linear_workspace_bytes(M, N, K);
+  if (M > 0 && (!workspace || workspace_bytes < need))
+    return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  bfp8_status_t st = BFP8_OK;
+  const LinearLayout L = linear_layout(M, N, K);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* q = M > 0 ? ws : nullptr;
+  float* as = M > 0 ? reinterpret_cast<float*>(ws + L.as_off) : nullptr;
+  void* gws = M > 0 ? static_cast<void*>(ws + L.gemm_off) : nullptr;
+  const size_t gws_bytes = M > 0 ? workspace_bytes - L.gemm_off : 0;
+  st = check_quant_args(x, x_dtype, M, K, ldx, q, K, as, M);
+  if (st != BFP8_OK) return st;
+  st = check_gemm_args(q, K, as, M, b, ldb, bs, ld_bs, c, ldc, M, N, K, gws, gws_bytes, false);
+  if (st != BFP8_OK) return st;
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, K, as, M, (hipStream_t)stream), "quant_act");
+  if (st != BFP8_OK) return st;
+  return launch_dense(q, K, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream);
 }
 
 bfp8_status_t bfp8_set_schedule(int schedule) {

@@ -32,11 +32,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// Store 4 consecutive bf16 outputs c[0..3] of one row, with column tail masking.
+// Output element n as bf16 bits: the FP32 result rounded to bf16, then, with a bias, the
+// bf16 sum bf16(float(c) + float(bias[n])) (the result is formed in the output's dtype and
+// the bias added to it, as the linear layer of page "transformers/integrations/deepgemm.py",
+// deepgemm_fp8_fp4_linear, does with output.add_(bias)).
+__device__ __forceinline__ uint32_t bf16_out(float acc, const uint16_t* bias, int n) {
+  uint32_t b = f32_to_bf16_rne(acc);
+  if (bias != nullptr) b = f32_to_bf16_rne(__uint_as_float(b << 16) + __uint_as_float((uint32_t)bias[n] << 16));
+  return b;
+}
+
+// Store 4 consecutive bf16 outputs c[0..3] of one row (columns n .. n+3), with column tail
+// masking and an optional bias.
 __device__ __forceinline__ void store_bf16x4(uint16_t* c, int n, int N, bool vec_ok, float v0, float v1,
-                                             float v2, float v3) {
-  const uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1);
-  const uint32_t b2 = f32_to_bf16_rne(v2), b3 = f32_to_bf16_rne(v3);
+                                             float v2, float v3, const uint16_t* bias) {
+  const uint32_t b0 = bf16_out(v0, bias, min(n, N - 1)), b1 = bf16_out(v1, bias, min(n + 1, N - 1));
+  const uint32_t b2 = bf16_out(v2, bias, min(n + 2, N - 1)), b3 = bf16_out(v3, bias, min(n + 3, N - 1));
   if (vec_ok && n + 3 < N) {
     uint2 pk;
     pk.x = b0 | (b1 << 16);

@@ -26,6 +26,7 @@ struct GemmArgs {
   int M, N, K;
   const int32_t* layout;  // grouped GEMM only: [M] group id per row, -1 = padding
   int G;
+  const uint16_t* bias;  // optional bf16 [N], added to the bf16 output (nullptr = none)
 };
 
 // Tiled-schedule plan for a dense GEMM: tile shape, and the workspace it needs (none so far).

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 1
+#define BFP8_ABI_VERSION 2
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -187,6 +187,34 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
                                            const int32_t* grouped_layout, int32_t G,
                                            uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace bfp8_linear needs (0 when M == 0): the quantized activations
+ * (M * K bytes), their scales (4 * M * K / 128 bytes) and the GEMM's workspace, each part
+ * 256-byte aligned. The workspace contract of bfp8_gemm applies. */
+size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * End-to-end FP8 linear layer, bf16 in and out (page "transformers/integrations/deepgemm.py",
+ * deepgemm_fp8_fp4_linear): the activations are quantized per 1x128 group exactly as
+ * bfp8_quant_act does, multiplied with the FP8 weight as bfp8_gemm does into a bf16 result,
+ * and, when a bias is given, the bias is added to that bf16 result:
+ *   out[m, n] = bf16(float(bf16(C[m, n])) + float(bias[n]))   (bias NULL: out = bf16(C)),
+ * which is the page's output.add_(bias) on a bf16 output.
+ *   x      [M][ldx] bf16 activations (x_dtype must be BFP8_IN_BF16; the page's output dtype
+ *          follows the input, and this library writes bf16 only)
+ *   b, bs  as for bfp8_gemm (weights [N][ldb] e4m3, scales [ceil(N/128)][ld_bs])
+ *   bias   NULL or bf16 [N], 2-byte aligned
+ *   c      [M][ldc] bf16 output
+ *   workspace / workspace_bytes: at least bfp8_linear_workspace_bytes(M, N, K) bytes,
+ *          256-byte aligned (BFP8_ERR_WORKSPACE if smaller); it holds the quantized
+ *          activations, which the call overwrites.
+ * Two kernels are enqueued on stream: the quantizer, then the GEMM with the bias in its
+ * output conversion. Validation, ownership and errors as for bfp8_quant_act and bfp8_gemm.
+ */
+bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                          const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                          const uint16_t* bias, uint16_t* c, int64_t ldc, int64_t N,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Process-wide schedule override for bfp8_gemm (tests and benchmarks):
  * BFP8_SCHED_AUTO restores the automatic choice. Returns BFP8_ERR_INVALID_ARGUMENT

@@ -22,12 +22,14 @@ What is computed, and where it is defined on the pages:
 * M-grouped contiguous GEMM (``gemm.grouped_gemm_contiguous_ref``): page
   "transformers/integrations/deepgemm.py", ``_build_deepgemm_contiguous_layout``
   (per-row expert id, -1 on padding rows) and ``deepgemm_fp8_fp4_experts_forward``.
+* FP8 linear layer (``linear.linear_ref``): page "transformers/integrations/deepgemm.py",
+  ``deepgemm_fp8_fp4_linear`` (quantize, GEMM into a bf16 output, then add the bias to it).
 
 Every function is pinned by tests under ``tests/test_oracle_*.py`` (library
 routines, brute force with exact rationals, closed forms and invariants); none
 is "parity unpinned".
 """
 
-from . import bf16, e4m3, gemm, quant  # noqa: F401
+from . import bf16, e4m3, gemm, linear, quant  # noqa: F401
 
-__all__ = ["bf16", "e4m3", "gemm", "quant"]
+__all__ = ["bf16", "e4m3", "gemm", "linear", "quant"]

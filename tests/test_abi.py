@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 1
+    assert lib.bfp8_abi_version() == 2
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -151,6 +151,45 @@ def test_schedule_override(lib):
         lib.bfp8_set_schedule(0)
 
 
+def _linear(lib, x=A, dt=1, M=8, K=256, ldx=256, b=B, ldb=256, bs=BS, ld_bs=2, bias=None, c=C, ldc=64, N=64,
+            ws=0x70000000, wsb=None):
+    if wsb is None:
+        wsb = lib.bfp8_linear_workspace_bytes(M, N, K) if M >= 0 else 0
+    return lib.bfp8_linear(x, dt, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, ws, wsb, None)
+
+
+def test_linear_workspace_size(lib):
+    # quantized codes (M x K bytes), then float32 scales (M x K/128), each region a whole number of
+    # 256-byte units; the GEMM itself needs none
+    assert lib.bfp8_linear_workspace_bytes(8, 64, 256) == 2048 + 256
+    assert lib.bfp8_linear_workspace_bytes(3, 64, 384) == 1280 + 256
+    assert lib.bfp8_linear_workspace_bytes(0, 64, 256) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=0), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(bias=0x80000001), _native.BFP8_ERR_MISALIGNED),
+    (dict(ws=0x70000010), _native.BFP8_ERR_MISALIGNED),
+    (dict(wsb=1024), _native.BFP8_ERR_WORKSPACE),
+    (dict(ws=None), _native.BFP8_ERR_WORKSPACE),
+    (dict(M=-1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=200, ldx=256), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(x=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(x=A + 2), _native.BFP8_ERR_MISALIGNED),
+    (dict(ldx=100), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ldc=32), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ld_bs=1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(b=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+])
+def test_linear_rejections(lib, kw, status):
+    assert _linear(lib, **kw) == status, lib.bfp8_last_error_message()
+    assert len(lib.bfp8_last_error_message()) > 0
+
+
+def test_linear_m_zero_ok_without_device(lib):
+    assert _linear(lib, M=0, x=None, ws=None, wsb=0) == _native.BFP8_OK
+
+
 def _gpu_count():
     import torch
 
@@ -158,8 +197,9 @@ def _gpu_count():
 
 
 @pytest.mark.skipif(_gpu_count() > 0, reason="a GPU is visible: a valid call with fake pointers would launch")
-def test_valid_call_without_gpu_reports_device_error(lib):
-    st = _gemm(lib)
+@pytest.mark.parametrize("call", ["gemm", "linear"])
+def test_valid_call_without_gpu_reports_device_error(lib, call):
+    st = _gemm(lib) if call == "gemm" else _linear(lib)
     assert st in (_native.BFP8_ERR_DEVICE, _native.BFP8_ERR_UNSUPPORTED), lib.bfp8_last_error_message()
     assert b"hip" in lib.bfp8_last_error_message().lower() or b"device" in lib.bfp8_last_error_message().lower()
 

@@ -101,3 +101,23 @@ def compare(got_bits, ref_bits, mag, k, what="", hw_block=None):
         raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {tuple(i)}: "
                              f"got {got[tuple(i)]!r} ref {ref[tuple(i)]!r} ({stats})")
     return stats
+
+
+def compare_linear(got_bits, ref_out_bits, ref_c_bits, mag, k, what=""):
+    """Linear layer: out = bf16(bf16(C) + bias). The GEMM's bound applies to C (at ref_c);
+    the bias addition then rounds once more, adding at most one bf16 ulp of the output."""
+    got = bf16.from_bits(got_bits)
+    ref = bf16.from_bits(ref_out_bits)
+    ref_c = bf16.from_bits(ref_c_bits)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    bound = 2 * bf16.ulp(ref_c) + 1e-3 * np.abs(ref_c) + (k / 128 + 130) * 2.0**-24 * mag + bf16.ulp(ref)
+    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
+    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3"
+    bad = d > bound
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r}")
+    return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_out_bits))}
