@@ -23,7 +23,8 @@ from . import _native
 from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
-    "quant_act", "gemm", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes", "set_schedule", "get_schedule", "schedule_for",
+    "quant_act", "gemm", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
+    "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
 
@@ -238,6 +239,143 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Te
                          w_s.data_ptr(), w_s.stride(0), bias.data_ptr() if bias is not None else None,
                          out.data_ptr(), out.stride(0), n, ws_ptr or None, ws_bytes, _stream(x.device))
     _check(st, "bfp8_linear")
+    return out
+
+
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    """UE8M0 scale codes as uint8 (float8_e8m0fnu tensors are viewed as their bytes)."""
+    if t.dtype == torch.float8_e8m0fnu:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise NotImplementedError(f"{name}: UE8M0 scale codes are uint8 or float8_e8m0fnu, got {t.dtype}")
+    return t
+
+
+def _check_padded_rows(t: torch.Tensor, name: str, ld: int, rows: int, cols: int):
+    """The UE8M0 kernels read codes four at a time: rows of ld bytes (a multiple of 4), all allocated."""
+    if ld % 4:
+        raise ValueError(f"{name}: rows of UE8M0 codes must be a multiple of 4 bytes apart (got {ld}); "
+                         "ue8m0_scales() and quant_act_ue8m0() lay them out so")
+    span = (rows - 1) * ld + (-(-cols // 4) * 4)
+    if t.untyped_storage().nbytes() - t.storage_offset() < span:
+        raise ValueError(f"{name}: the last row of UE8M0 codes must be padded to a multiple of 4 bytes")
+
+
+def ue8m0_scales(codes: torch.Tensor) -> torch.Tensor:
+    """UE8M0 scale codes [..., R, C] copied into rows padded to a multiple of 4 bytes, the layout
+    the UE8M0 GEMMs read (weights are prepared once); returns a view of the same shape."""
+    codes = _codes(codes, "codes")
+    *lead, r, c = codes.shape
+    buf = torch.zeros((*lead, r, -(-c // 4) * 4), dtype=torch.uint8, device=codes.device)
+    buf[..., :c] = codes
+    return buf[..., :c]
+
+
+def quant_act_ue8m0(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """quant_act with power-of-two scales: returns (q, e) with e the UE8M0 codes [M, K/128]
+    (uint8), stored group-major with a row of codes padded to a multiple of 4 bytes."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise NotImplementedError(f"quant_act_ue8m0 takes float32 or bfloat16 input, got {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    if x.stride(1) != 1:
+        raise ValueError("x must be K-contiguous")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        ld = max(-(-m // 4) * 4, 4)
+        scales = torch.empty((-(-k // 128), ld), dtype=torch.uint8, device=x.device)[:, :m].t()
+    scales = _codes(scales, "scales")
+    _require(q, "q", torch.uint8, 2)
+    _require(scales, "scales", torch.uint8, 2)
+    if q.stride(1) != 1 or (scales.stride(0) != 1 and m > 1):
+        raise ValueError("q must be K-contiguous and scales group-major (stride(0) == 1)")
+    dt = _native.BFP8_IN_F32 if x.dtype == torch.float32 else _native.BFP8_IN_BF16
+    st = _native.lib().bfp8_quant_act_ue8m0(x.data_ptr(), dt, m, k, x.stride(0), q.data_ptr(), q.stride(0),
+                                            scales.data_ptr(), scales.stride(1), _stream(x.device))
+    _check(st, "bfp8_quant_act_ue8m0")
+    return q, scales
+
+
+def gemm_ue8m0(a_q: torch.Tensor, a_e: torch.Tensor, b_q: torch.Tensor, b_e: torch.Tensor,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm with UE8M0 scale codes: a_e [M, K/128] group-major (as quant_act_ue8m0 returns) and
+    b_e [ceil(N/128), K/128] with rows padded to a multiple of 4 bytes (ue8m0_scales)."""
+    a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
+    a_e, b_e = _codes(a_e, "a_e"), _codes(b_e, "b_e")
+    _require(a_q, "a_q", torch.uint8, 2)
+    _require(b_q, "b_q", torch.uint8, 2)
+    _require(a_e, "a_e", torch.uint8, 2)
+    _require(b_e, "b_e", torch.uint8, 2)
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    kb = -(-k // 128)
+    if b_q.shape[1] != k:
+        raise ValueError(f"a_q and b_q disagree on K: {k} vs {b_q.shape[1]}")
+    if a_q.stride(1) != 1 or b_q.stride(1) != 1 or b_e.stride(1) != 1:
+        raise ValueError("a_q, b_q and b_e must be contiguous along K")
+    if tuple(a_e.shape) != (m, kb) or tuple(b_e.shape) != (-(-n // 128), kb):
+        raise ValueError(f"scale shapes {tuple(a_e.shape)}, {tuple(b_e.shape)} do not match M={m}, N={n}, K={k}")
+    if a_e.stride(0) != 1 and m > 1:
+        raise ValueError("a_e must be group-major: a_e.stride(0) == 1 (as quant_act_ue8m0 returns)")
+    ld_as = a_e.stride(1)
+    if m > 0:
+        _check_padded_rows(a_e, "a_e", ld_as, kb, m)
+    _check_padded_rows(b_e, "b_e", b_e.stride(0), b_e.shape[0], kb)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    _require(out, "out", torch.bfloat16, 2)
+    if out.stride(1) != 1:
+        raise ValueError("out must be contiguous along N")
+    lib = _native.lib()
+    if workspace is None:
+        ws_ptr, ws_bytes = _workspace(a_q.device, lib.bfp8_gemm_workspace_bytes(m, n, k))
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib.bfp8_gemm_ue8m0(a_q.data_ptr(), a_q.stride(0), a_e.data_ptr(), ld_as, b_q.data_ptr(), b_q.stride(0),
+                             b_e.data_ptr(), b_e.stride(0), out.data_ptr(), out.stride(0), m, n, k, ws_ptr or None,
+                             ws_bytes, _stream(a_q.device))
+    _check(st, "bfp8_gemm_ue8m0")
+    return out
+
+
+def grouped_gemm_contiguous_ue8m0(a_q: torch.Tensor, a_e: torch.Tensor, b_q: torch.Tensor, b_e: torch.Tensor,
+                                  layout: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """grouped_gemm_contiguous with UE8M0 scale codes: b_e [G, ceil(N/128), K/128] with rows padded
+    to a multiple of 4 bytes (ue8m0_scales), a_e as for gemm_ue8m0."""
+    a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
+    a_e, b_e = _codes(a_e, "a_e"), _codes(b_e, "b_e")
+    _require(a_q, "a_q", torch.uint8, 2)
+    _require(b_q, "b_q", torch.uint8, 3)
+    _require(a_e, "a_e", torch.uint8, 2)
+    _require(b_e, "b_e", torch.uint8, 3)
+    _require(layout, "layout", torch.int32, 1)
+    m, k = a_q.shape
+    g, n, k2 = b_q.shape
+    kb = -(-k // 128)
+    nb = -(-n // 128)
+    if k2 != k or layout.shape[0] != m:
+        raise ValueError("shape mismatch between a_q, b_q and layout")
+    if not (b_q.is_contiguous() and layout.is_contiguous()):
+        raise ValueError("b_q and layout must be contiguous")
+    if tuple(b_e.shape) != (g, nb, kb) or tuple(a_e.shape) != (m, kb):
+        raise ValueError("scale shapes do not match")
+    if b_e.stride(2) != 1 or b_e.stride(0) != nb * b_e.stride(1):
+        raise ValueError("b_e must be [G][ceil(N/128)][ld] with consecutive experts (ue8m0_scales)")
+    if a_e.stride(0) != 1 and m > 1:
+        raise ValueError("a_e must be group-major: a_e.stride(0) == 1 (as quant_act_ue8m0 returns)")
+    if m > 0:
+        _check_padded_rows(a_e, "a_e", a_e.stride(1), kb, m)
+    _check_padded_rows(b_e, "b_e", b_e.stride(1), g * nb, kb)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    _require(out, "out", torch.bfloat16, 2)
+    st = _native.lib().bfp8_grouped_gemm_contiguous_ue8m0(
+        a_q.data_ptr(), a_q.stride(0), a_e.data_ptr(), a_e.stride(1), b_q.data_ptr(), b_q.stride(1),
+        b_e.data_ptr(), b_e.stride(1), layout.data_ptr(), g, out.data_ptr(), out.stride(0), m, n, k, None, 0,
+        _stream(a_q.device))
+    _check(st, "bfp8_grouped_gemm_contiguous_ue8m0")
     return out
 
 

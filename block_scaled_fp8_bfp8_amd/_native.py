@@ -32,6 +32,11 @@ SIGNATURES = [
     ("bfp8_gemm", ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_grouped_gemm_contiguous", ctypes.c_int,
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_quant_act_ue8m0", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    ("bfp8_gemm_ue8m0", ctypes.c_int,
+     [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_grouped_gemm_contiguous_ue8m0", ctypes.c_int,
+     [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_linear_workspace_bytes", _sz, [_i64, _i64, _i64]),
     ("bfp8_linear", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),

@@ -69,10 +69,11 @@ bfp8_status_t launched(hipError_t e, const char* what) {
   return ok();
 }
 
-// Shared checks of the dense and grouped GEMM arguments.
-bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
-                              int64_t ldb, const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
-                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes, bool grouped) {
+// Shared checks of the dense and grouped GEMM arguments; e8: the scales are UE8M0 codes.
+bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const void* as, int64_t ld_as, const uint8_t* b,
+                              int64_t ldb, const void* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes, bool grouped,
+                              bool e8 = false) {
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
   if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
   if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
@@ -95,6 +96,8 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, in
   if (lda % 16 || ldb % 16) return fail(BFP8_ERR_MISALIGNED, "lda and ldb must be multiples of 16 bytes");
   if (!aligned(a, 16) || !aligned(b, 16)) return fail(BFP8_ERR_MISALIGNED, "a and b must be 16-byte aligned");
   if (!aligned(as, 4) || !aligned(bs, 4)) return fail(BFP8_ERR_MISALIGNED, "as and bs must be 4-byte aligned");
+  if (e8 && (ld_as % 4 || ld_bs % 4))
+    return fail(BFP8_ERR_MISALIGNED, "UE8M0 scale rows: ld_as and ld_bs must be multiples of 4 (codes are read as dwords)");
   if (!aligned(c, 2)) return fail(BFP8_ERR_MISALIGNED, "c must be 2-byte aligned");
   // The kernels address a row inside A, and inside one weight matrix of B, with a 32-bit
   // byte offset from the operand's base.
@@ -108,7 +111,7 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const float* as, in
 
 // Arguments of the activation quantizer (no device access).
 bfp8_status_t check_quant_args(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* q,
-                               int64_t ldq, const float* as, int64_t ld_as) {
+                               int64_t ldq, const void* as, int64_t ld_as, bool e8 = false) {
   if (x_dtype != BFP8_IN_F32 && x_dtype != BFP8_IN_BF16)
     return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is neither BFP8_IN_F32 nor BFP8_IN_BF16", x_dtype);
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
@@ -124,7 +127,7 @@ bfp8_status_t check_quant_args(const void* x, int x_dtype, int64_t M, int64_t K,
   const int64_t esize = x_dtype == BFP8_IN_F32 ? 4 : 2;
   if ((ldx * esize) % 16 || ldq % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
   if (!aligned(x, 16) || !aligned(q, 16)) return fail(BFP8_ERR_MISALIGNED, "x and q must be 16-byte aligned");
-  if (!aligned(as, 4)) return fail(BFP8_ERR_MISALIGNED, "as must be 4-byte aligned");
+  if (!e8 && !aligned(as, 4)) return fail(BFP8_ERR_MISALIGNED, "as must be 4-byte aligned");
   return ok();
 }
 
@@ -168,8 +171,18 @@ bfp8_status_t bfp8_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, i
   if (st != BFP8_OK || M == 0) return st;
   st = check_device();
   if (st != BFP8_OK) return st;
-  return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, (hipStream_t)stream),
+  return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, false, (hipStream_t)stream),
                   "quant_act");
+}
+
+bfp8_status_t bfp8_quant_act_ue8m0(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                   int64_t ldq, uint8_t* as, int64_t ld_as, void* stream) {
+  bfp8_status_t st = check_quant_args(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, true);
+  if (st != BFP8_OK || M == 0) return st;
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, true, (hipStream_t)stream),
+                  "quant_act_ue8m0");
 }
 
 size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -184,11 +197,12 @@ size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 namespace {
 
 // Launch the dense GEMM (arguments already validated) with the schedule for this shape.
-bfp8_status_t launch_dense(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
-                           int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
-                           int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace, void* stream) {
+bfp8_status_t launch_dense(const uint8_t* a, int64_t lda, const void* as, int64_t ld_as, const uint8_t* b,
+                           int64_t ldb, const void* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace, void* stream,
+                           bool e8 = false) {
   const bfp8::GemmArgs args{a,      lda,    as,     ld_as,   b, ldb, bs, ld_bs, c,
-                            ldc,    (int)M, (int)N, (int)K,  nullptr, 1, bias};
+                            ldc,    (int)M, (int)N, (int)K,  nullptr, 1, bias, e8};
   const int sched = choose_schedule(M, N, K);
   if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_ksplit(args, (hipStream_t)stream), "gemm_ksplit");
   return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
@@ -219,13 +233,28 @@ bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t 
   return launch_dense(a, lda, as, ld_as, b, ldb, bs, ld_bs, nullptr, c, ldc, M, N, K, workspace, stream);
 }
 
-bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
-                                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
-                                           const int32_t* grouped_layout, int32_t G, uint16_t* c, int64_t ldc,
-                                           int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
-                                           void* stream) {
+bfp8_status_t bfp8_gemm_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const uint8_t* b,
+                              int64_t ldb, const uint8_t* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
-                                     workspace_bytes, true);
+                                     workspace_bytes, false, true);
+  if (st != BFP8_OK) return st;
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launch_dense(a, lda, as, ld_as, b, ldb, bs, ld_bs, nullptr, c, ldc, M, N, K, workspace, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+bfp8_status_t grouped_gemm(const uint8_t* a, int64_t lda, const void* as, int64_t ld_as, const uint8_t* b,
+                           int64_t ldb, const void* bs, int64_t ld_bs, const int32_t* grouped_layout, int32_t G,
+                           uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream, bool e8) {
+  bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
+                                     workspace_bytes, true, e8);
   if (st != BFP8_OK) return st;
   if (G < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "G = %d must be >= 1", (int)G);
   if (M % bfp8::kBlock != 0)
@@ -237,9 +266,31 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
-  const bfp8::GemmArgs args{a,   lda, as,     ld_as,  b,      ldb,           bs,     ld_bs,  c,
-                            ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G};
+  const bfp8::GemmArgs args{a,   lda,    as,     ld_as,  b,              ldb,    bs,      ld_bs, c,
+                            ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G, nullptr, e8};
   return launched(bfp8::launch_grouped_tiled(args, (hipStream_t)stream), "grouped_gemm_tiled");
+}
+
+}  // namespace
+
+extern "C" {
+
+bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                                           const int32_t* grouped_layout, int32_t G, uint16_t* c, int64_t ldc,
+                                           int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  return grouped_gemm(a, lda, as, ld_as, b, ldb, bs, ld_bs, grouped_layout, G, c, ldc, M, N, K, workspace,
+                      workspace_bytes, stream, false);
+}
+
+bfp8_status_t bfp8_grouped_gemm_contiguous_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as,
+                                                 const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs,
+                                                 const int32_t* grouped_layout, int32_t G, uint16_t* c, int64_t ldc,
+                                                 int64_t M, int64_t N, int64_t K, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  return grouped_gemm(a, lda, as, ld_as, b, ldb, bs, ld_bs, grouped_layout, G, c, ldc, M, N, K, workspace,
+                      workspace_bytes, stream, true);
 }
 
 size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -280,7 +331,7 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
-  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, K, as, M, (hipStream_t)stream), "quant_act");
+  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, K, as, M, false, (hipStream_t)stream), "quant_act");
   if (st != BFP8_OK) return st;
   return launch_dense(q, K, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream);
 }

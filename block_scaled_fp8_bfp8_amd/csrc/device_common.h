@@ -24,6 +24,24 @@ __device__ __forceinline__ v4f mfma_block(const v8i& src0, const v8i& src1) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(src0, src1, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// The same product with UE8M0 block scales applied by the hardware and the result added to
+// `acc`: D = acc + sum_k (src0[i][k] 2^(e0 - 127)) (src1[j][k] 2^(e1 - 127)). Lane l gives
+// the scale code of row l % 16 of each operand in the low byte of e0 / e1 (the instruction
+// scales each 32-wide K slice by the code of the lane that holds it, and the four lanes of a
+// row carry the same code for a 128-wide block). The sum is formed in the matrix core's own
+// wide accumulation, not as IEEE float32 steps; its error against the exact result was
+// measured below 2^-19 of |acc| plus the block's absolute mass.
+__device__ __forceinline__ v4f mfma_block_e8(const v8i& src0, const v8i& src1, const v4f& acc, int e0, int e1) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(src0, src1, acc, 0, 0, 0, e0, 0, e1);
+}
+
+// UE8M0 code of block kb from a row of codes whose start is 4-byte aligned, read through the
+// scalar cache as the aligned dword that holds it (inside the row: its length is padded to a
+// multiple of 4).
+__device__ __forceinline__ int e8_code_scalar(const __attribute__((address_space(4))) uint32_t* row, int kb) {
+  return (int)((row[kb >> 2] >> ((kb & 3) * 8)) & 0xffu);
+}
+
 // float32 -> bf16 bit pattern, round to nearest, ties to even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -25,7 +25,9 @@
 //     points, so that they do not all wait on the same HBM reads;
 //   * the waves' partial tiles are summed through LDS in a fixed wave order, which keeps
 //     results bitwise reproducible without atomics or a global workspace, and each sum is
-//     rounded once to bf16.
+//     rounded once to bf16;
+//   * UE8M0 scales (kE8): the scale codes are copied like the float scales, and the scaled
+//     MFMA applies 2^(ea - 127) * 2^(eb - 127) and accumulates into the wave's tile itself.
 #include <type_traits>
 
 #include "device_common.h"
@@ -35,13 +37,17 @@ namespace bfp8 {
 
 namespace {
 
-template <int TN, int TM, int WAVES, int SLOTS>
+template <int TN, int TM, int WAVES, int SLOTS, bool kE8>
 __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) {
   constexpr int BN = 16 * TN, BM = 16 * TM;
   constexpr int kRows = BN + BM;
   constexpr int kSlot = kRows * kBlock;           // bytes per slot
   constexpr int kPieces = kRows / 8;              // 1 KB (8-row) copies per K block
-  constexpr int kAsCopies = (BM + 63) / 64;       // 64-lane scale copies per K block
+  // 64-lane scale copies per K block: 64 float scales each, or 256 UE8M0 codes (4 per lane).
+  constexpr int kAsCopies = kE8 ? 1 : (BM + 63) / 64;
+  constexpr int kScaleBytes = kE8 ? 1 : 4;
+  static_assert(!kE8 || BM <= 256, "one copy holds the codes of 256 activation rows");
+  using ScaleT = std::conditional_t<kE8, int, float>;
   constexpr int kPerBlock = kPieces + kAsCopies;  // copies issued per K block
   constexpr int kTileFloats = BN * BM;
   static_assert(kBlock % BN == 0, "a wave's weight rows must share one scale strip");
@@ -71,9 +77,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     const int src_row = is_b ? min(n0 + row, N - 1) : min(m0 + row - BN, M - 1);
     coff[j] = (uint32_t)((int64_t)src_row * (is_b ? args.ldb : args.lda) + lcol * 16);
   }
+  // Float scales: row m0 + 64 c + lane, clamped. UE8M0 codes: the dword of rows m0 + 4 lane ..,
+  // clamped to the one holding row M - 1 (inside the row of codes: its length is a multiple of 4).
   uint32_t as_voff[kAsCopies];
 #pragma unroll
-  for (int c = 0; c < kAsCopies; ++c) as_voff[c] = (uint32_t)min(m0 + c * 64 + lane, M - 1) * 4u;
+  for (int c = 0; c < kAsCopies; ++c)
+    as_voff[c] = kE8 ? (uint32_t)min(m0 + 4 * lane, (M - 1) & ~3) : (uint32_t)min(m0 + c * 64 + lane, M - 1) * 4u;
+  const uint8_t* asmat = static_cast<const uint8_t*>(args.as);
 
   auto issue = [&](int slot, int kb) __attribute__((always_inline)) {
     const uint8_t* bsrc = args.b + (int64_t)kb * kBlock;
@@ -83,7 +93,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     for (int j = 0; j < kPieces; ++j) copy16_to_lds(j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
 #pragma unroll
     for (int c = 0; c < kAsCopies; ++c)
-      copy4_to_lds(args.as + (int64_t)kb * args.ld_as, as_voff[c], lds_addr(&as_slots[w][slot][c * 64]));
+      copy4_to_lds(asmat + (int64_t)kb * args.ld_as * kScaleBytes, as_voff[c], lds_addr(&as_slots[w][slot][c * 64]));
   };
 
   // Fragment rows come in 16-row blocks, so every row a lane reads has row % 16 == r.
@@ -96,8 +106,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // Weight scale strip of the tile (scalar loads through the constant address space).
-  const __attribute__((address_space(4))) float* bsp =
-      (const __attribute__((address_space(4))) float*)(args.bs + (int64_t)(min(n0, N - 1) / kBlock) * args.ld_bs);
+  const uint8_t* bs_row =
+      static_cast<const uint8_t*>(args.bs) + (int64_t)(min(n0, N - 1) / kBlock) * args.ld_bs * kScaleBytes;
+  auto weight_scale = [&](int kb) __attribute__((always_inline)) -> ScaleT {
+    if constexpr (kE8) {
+      return e8_code_scalar((const __attribute__((address_space(4))) uint32_t*)bs_row, kb);
+    } else {
+      return ((const __attribute__((address_space(4))) float*)bs_row)[kb];
+    }
+  };
 
   float acc[TN][TM][4];
 #pragma unroll
@@ -134,13 +151,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     const uint8_t* sl = &slots[w][slot][0];
     v8i fb[TN], fa[TM];
     float sc[TM];
-    const float bs_kb = bsp[kb];
+    ScaleT ea[TM];
+    const ScaleT bs_kb = weight_scale(kb);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_at(sl, tn * 16);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       fa[tm] = frag_at(sl, BN + tm * 16);
-      sc[tm] = as_slots[w][slot][tm * 16 + r] * bs_kb;
+      if constexpr (kE8) {
+        ea[tm] = reinterpret_cast<const uint8_t*>(&as_slots[w][slot][0])[tm * 16 + r];
+      } else {
+        sc[tm] = as_slots[w][slot][tm * 16 + r] * bs_kb;
+      }
     }
     // The slot is refilled only after this wave's reads of it have returned.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -154,16 +176,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
       for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], sc[um], acc[un][um][e]);
       asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
     };
+    if constexpr (kE8) {
 #pragma unroll
-    for (int t = 0; t < TN * TM; ++t) {
-      const v4f p = mfma_block(fb[t / TM], fa[t % TM]);
-      if (t >= 2) promote(t - 2, p2);
-      __builtin_amdgcn_sched_barrier(0);
-      p2 = p1;
-      p1 = p;
+      for (int t = 0; t < TN * TM; ++t) {
+        const int tn = t / TM, tm = t % TM;
+        const v4f cur = {acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
+        const v4f nxt = mfma_block_e8(fb[tn], fa[tm], cur, bs_kb, ea[tm]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tn][tm][e] = nxt[e];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TN * TM; ++t) {
+        const v4f p = mfma_block(fb[t / TM], fa[t % TM]);
+        if (t >= 2) promote(t - 2, p2);
+        __builtin_amdgcn_sched_barrier(0);
+        p2 = p1;
+        p1 = p;
+      }
+      if constexpr (TN * TM >= 2) promote(TN * TM - 2, p2);
+      promote(TN * TM - 1, p1);
     }
-    if constexpr (TN * TM >= 2) promote(TN * TM - 2, p2);
-    promote(TN * TM - 1, p1);
   }
 
   // Fixed-order reduction of the waves' partial tiles through LDS. Wave w's partial goes to
@@ -192,7 +225,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
 template <int TN, int TM, int WAVES, int SLOTS>
 hipError_t launch_ksplit_cfg(const GemmArgs& args, hipStream_t stream) {
   const dim3 grid((unsigned)((args.N + 16 * TN - 1) / (16 * TN)), (unsigned)((args.M + 16 * TM - 1) / (16 * TM)));
-  hipLaunchKernelGGL((gemm_ksplit_kernel<TN, TM, WAVES, SLOTS>), grid, dim3(WAVES * 64), 0, stream, args);
+  if (args.e8) {
+    hipLaunchKernelGGL((gemm_ksplit_kernel<TN, TM, WAVES, SLOTS, true>), grid, dim3(WAVES * 64), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((gemm_ksplit_kernel<TN, TM, WAVES, SLOTS, false>), grid, dim3(WAVES * 64), 0, stream, args);
+  }
   return hipGetLastError();
 }
 

@@ -28,7 +28,11 @@
 //     share activation and weight rows in that XCD's L2;
 //   * grouped: a workgroup's BM rows lie in one 128-row block; its expert id is the
 //     largest id among those rows (padding rows carry -1); a block of padding only
-//     exits at once, and rows whose id is -1 are not stored.
+//     exits at once, and rows whose id is -1 are not stored;
+//   * UE8M0 scales (kE8; page "transformers/integrations/deepgemm.py", the power-of-two
+//     scale factors of _ceil_to_ue8m0 / float8_e8m0fnu): As and Bs are powers of two given
+//     by their exponent bytes, so the scaled MFMA applies them exactly in the matrix core
+//     and accumulates into the FP32 tile itself; the VALU promotion disappears.
 #include <algorithm>
 #include <type_traits>
 
@@ -60,7 +64,7 @@ __device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int 
   tn = r / gm;
 }
 
-template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped>
+template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped, bool kE8>
 __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs args) {
   constexpr int kWaves = WGN * WGM;  // waves per K group
   constexpr int WN = BN / WGN, WM = BM / WGM;
@@ -79,8 +83,14 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   static_assert(KG == 1 || BN * BM * 4 <= KG * STAGES * kStage, "the K-group sum reuses the stages");
   // K groups: KG sets of WGN x WGM waves; group g multiplies the K blocks kb = g, g + KG, ...
   // through its own LDS ring, and the groups' tiles are summed in group order at the end.
+  // Activation scales of a stage: BM floats, or with kE8 BM code bytes (one 64-lane dword copy
+  // fills 256 bytes).
+  constexpr int kAsWords = kE8 ? 64 : BM;
+  constexpr int kScaleBytes = kE8 ? 1 : 4;
+  static_assert(!kE8 || BM <= 256, "one copy holds the codes of 256 activation rows");
+  using ScaleT = std::conditional_t<kE8, int, float>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[KG][STAGES][kStage];
-  __shared__ __attribute__((aligned(16))) float as_lds[KG][STAGES][BM];
+  __shared__ __attribute__((aligned(16))) float as_lds[KG][STAGES][kAsWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,7 +107,8 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   const int n0 = tile_n * BN, m0 = tile_m * BM;
 
   const uint8_t* bmat = args.b;
-  const float* bsmat = args.bs;
+  const uint8_t* bsmat = static_cast<const uint8_t*>(args.bs);
+  const uint8_t* asmat = static_cast<const uint8_t*>(args.as);
   if constexpr (kGrouped) {
     int gid = -1;
     for (int i = lane; i < BM; i += 64) gid = max(gid, args.layout[m0 + i]);
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     // breaks the layout contract; such a block is skipped rather than read out of bounds.
     if (gid < 0 || gid >= args.G) return;
     bmat += (int64_t)gid * N * args.ldb;
-    bsmat += (int64_t)gid * ((N + kBlock - 1) / kBlock) * args.ld_bs;
+    bsmat += (int64_t)gid * ((N + kBlock - 1) / kBlock) * args.ld_bs * kScaleBytes;
   }
 
   // Copy plan. Wave w copies stage rows [w * 8 * kCopies, ...) in 8-row pieces; lane l of
@@ -127,9 +138,13 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     const int64_t ld = prow < BN ? args.ldb : args.lda;
     coff[j] = (uint32_t)((int64_t)row * ld + lcol * 16);
   }
-  // Activation scales of a K block: waves 0 .. BM/64-1 copy 64 of them each (clamped rows).
-  const bool copies_as = w < BM / 64;
-  const uint32_t as_voff = (uint32_t)min(m0 + (copies_as ? w : 0) * 64 + lane, M - 1) * 4u;
+  // Activation scales of a K block: waves 0 .. BM/64-1 copy 64 of them each (clamped rows);
+  // UE8M0 codes: wave 0 copies 4 codes per lane (dwords clamped to the one holding row M-1,
+  // which lies inside the row of codes: its length is a multiple of 4).
+  const bool copies_as = kE8 ? w == 0 : w < BM / 64;
+  const uint32_t as_voff = kE8 ? (uint32_t)min(m0 + 4 * lane, (M - 1) & ~3)
+                               : (uint32_t)min(m0 + (copies_as ? w : 0) * 64 + lane, M - 1) * 4u;
+  const uint32_t as_dst_off = kE8 ? 0u : (uint32_t)(w * 64 * 4);
 
   uint32_t stage_lds[STAGES], as_lds_addr[STAGES];
 #pragma unroll
@@ -147,8 +162,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 #pragma unroll
     for (int j = 0; j < kCopies; ++j)
       copy16_to_lds(prow_base + j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
-    if (copies_as)
-      copy4_to_lds(args.as + (int64_t)kb * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
+    if (copies_as) copy4_to_lds(asmat + (int64_t)kb * args.ld_as * kScaleBytes, as_voff, as_lds_addr[buf] + as_dst_off);
   };
   // One piece of a block's copy (for spreading a block's copies over the multiply steps).
   auto issue_piece = [&](int buf, int kb_local, int j) __attribute__((always_inline)) {
@@ -158,14 +172,19 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   };
   auto issue_scales = [&](int buf, int kb_local) __attribute__((always_inline)) {
     if (copies_as)
-      copy4_to_lds(args.as + (int64_t)gkb(kb_local) * args.ld_as, as_voff, as_lds_addr[buf] + (uint32_t)(w * 64 * 4));
+      copy4_to_lds(asmat + (int64_t)gkb(kb_local) * args.ld_as * kScaleBytes, as_voff, as_lds_addr[buf] + as_dst_off);
   };
 
   const int r = lane & 15, kc = lane >> 4;
   // Weight scale of this wave's strip, through the scalar cache (constant address space).
-  const __attribute__((address_space(4))) float* bsp =
-      (const __attribute__((address_space(4))) float*)(bsmat +
-                                                       (int64_t)(min(n0 + wn * WN, N - 1) / kBlock) * args.ld_bs);
+  const uint8_t* bs_row = bsmat + (int64_t)(min(n0 + wn * WN, N - 1) / kBlock) * args.ld_bs * kScaleBytes;
+  auto weight_scale = [&](int kb_global) __attribute__((always_inline)) -> ScaleT {
+    if constexpr (kE8) {
+      return e8_code_scalar((const __attribute__((address_space(4))) uint32_t*)bs_row, kb_global);
+    } else {
+      return ((const __attribute__((address_space(4))) float*)bs_row)[kb_global];
+    }
+  };
 
   float acc[TN][TM][4];
 #pragma unroll
@@ -192,7 +211,13 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   auto frag_a = [&](const uint8_t* stage, int tm) __attribute__((always_inline)) {
     return frag_at(stage, BN + wm * WM + tm * 16);
   };
-  auto act_scale = [&](int slot, int tm) __attribute__((always_inline)) { return as_lds[g][slot][wm * WM + tm * 16 + r]; };
+  auto act_scale = [&](int slot, int tm) __attribute__((always_inline)) -> ScaleT {
+    if constexpr (kE8) {
+      return reinterpret_cast<const uint8_t*>(&as_lds[g][slot][0])[wm * WM + tm * 16 + r];
+    } else {
+      return as_lds[g][slot][wm * WM + tm * 16 + r];
+    }
+  };
 
   // Software pipeline. Sub-tiles are visited activation-row by activation-row: step
   // t = tm * TN + tn multiplies weight fragment tn by activation fragment tm. Block kb is
@@ -204,8 +229,8 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   // which iteration kb + 1 reads.
   v8i fa[TM];
   v8i fb[TN];
-  float sa[TM];
-  float bsv;
+  ScaleT sa[TM];
+  ScaleT bsv;
   constexpr int kSteps = TN * TM;
 
   // Copies issued per wave per K block; the wait for block kb + 2 at the end of iteration kb
@@ -227,10 +252,12 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     // branches; those registers are never used.
     const int nslot = (kb + 1) % STAGES;
     const uint8_t* nstage = &smem[g][nslot][0];
-    const float bs_next = bsp[gkb(min(kb + 1, KB - 1))];
+    const ScaleT bs_next = weight_scale(gkb(min(kb + 1, KB - 1)));
     float sc[TM];
+    if constexpr (!kE8) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) sc[tm] = sa[tm] * bsv;
+      for (int tm = 0; tm < TM; ++tm) sc[tm] = sa[tm] * bsv;
+    }
     if constexpr (kSteady) issue_scales(cslot, kb + STAGES);
     // Step t issues the MFMA of sub-tile t, the promotion FMAs of sub-tile t - 2 (whose
     // result is then at least one MFMA old), its share of the copies and of the next block's
@@ -249,8 +276,17 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
       const int tm = t / TN, tn = t % TN;
-      const v4f p = mfma_block(fb[tn], fa[tm]);
-      if (t >= 2) promote(t - 2, p2);
+      v4f p;
+      if constexpr (kE8) {
+        // The scaled product is added to the tile by the MFMA itself.
+        const v4f cur = {acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
+        const v4f nxt = mfma_block_e8(fb[tn], fa[tm], cur, bsv, sa[tm]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tn][tm][e] = nxt[e];
+      } else {
+        p = mfma_block(fb[tn], fa[tm]);
+        if (t >= 2) promote(t - 2, p2);
+      }
       if constexpr (kSteady) {
 #pragma unroll
         for (int j = 0; j < kCopies; ++j)
@@ -262,11 +298,15 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
       }
       if (tm == TM - 1) fb[tn] = frag_b(nstage, tn);
       __builtin_amdgcn_sched_barrier(0);
-      p2 = p1;
-      p1 = p;
+      if constexpr (!kE8) {
+        p2 = p1;
+        p1 = p;
+      }
     }
-    promote(kSteps - 2, p2);
-    promote(kSteps - 1, p1);
+    if constexpr (!kE8) {
+      promote(kSteps - 2, p2);
+      promote(kSteps - 1, p1);
+    }
     bsv = bs_next;
     // Block kb + 2 is in LDS once every wave's copies of it have landed; the barrier also
     // orders this iteration's reads of stage (kb + 1) % STAGES before its refill.
@@ -286,7 +326,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   }
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_b(&smem[g][0][0], tn);
-  bsv = bsp[g];
+  bsv = weight_scale(g);
   // every wave has read stage 0 before iteration 0 refills it
   lds_barrier();
   int kb = 0;
@@ -395,8 +435,13 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 
 template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool G>
 hipError_t launch_tiled_cfg(const GemmArgs& args, int tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G>), dim3((unsigned)tiles),
-                     dim3(KG * WGN * WGM * 64), 0, stream, args);
+  if (args.e8) {
+    hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G, true>), dim3((unsigned)tiles),
+                       dim3(KG * WGN * WGM * 64), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G, false>), dim3((unsigned)tiles),
+                       dim3(KG * WGN * WGM * 64), 0, stream, args);
+  }
   return hipGetLastError();
 }
 

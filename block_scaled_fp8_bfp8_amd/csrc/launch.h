@@ -15,11 +15,11 @@ constexpr int kInBf16 = 1;
 struct GemmArgs {
   const uint8_t* a;  // [M][lda] e4m3 activations
   int64_t lda;
-  const float* as;  // [K/128][ld_as] activation scales (group-major)
+  const void* as;  // [K/128][ld_as] activation scales (group-major): float32, or UE8M0 bytes if e8
   int64_t ld_as;
   const uint8_t* b;  // [G][N][ldb] e4m3 weights (G = 1 for the dense GEMM)
   int64_t ldb;
-  const float* bs;  // [G][ceil(N/128)][ld_bs] weight block scales
+  const void* bs;  // [G][ceil(N/128)][ld_bs] weight block scales: float32, or UE8M0 bytes if e8
   int64_t ld_bs;
   uint16_t* c;  // [M][ldc] bf16 output
   int64_t ldc;
@@ -27,6 +27,10 @@ struct GemmArgs {
   const int32_t* layout;  // grouped GEMM only: [M] group id per row, -1 = padding
   int G;
   const uint16_t* bias;  // optional bf16 [N], added to the bf16 output (nullptr = none)
+  // UE8M0 scales: byte e stands for 2^(e - 127); both scale arrays start 4-byte aligned and
+  // have leading dimensions that are multiples of 4. The kernels then apply the scales
+  // inside the scaled MFMA and accumulate in its FP32 accumulator (no separate promotion).
+  bool e8;
 };
 
 // Tiled-schedule plan for a dense GEMM: tile shape, and the workspace it needs (none so far).
@@ -37,8 +41,9 @@ struct TiledPlan {
 };
 TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K);
 
+// Writes float32 scales to `as`, or with e8 their UE8M0 codes (one byte each).
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                            int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
+                            int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream);
 
 // Largest M the automatic choice gives to the K-split schedule (BFP8_SCHED_SMALL_M); the
 // tiled schedule takes larger M.

@@ -7,6 +7,12 @@
 //   s = fl32(max(amax, 1e-10) / 448),  q = e4m3fn_RNE(clamp(fl32(x / s), -448, 448)),
 // and writes the scale group-major: as[g * ld_as + m].
 //
+// UE8M0 variant (page "transformers/integrations/deepgemm.py": _ceil_to_ue8m0 and the
+// use_ue8m0 recipe of _select_fp8_cast_kwargs): the same s is rounded up to a power of two
+// by adding 2^23 - 1 to its bit pattern and clearing the mantissa; the group is divided by
+// that power of two (exactly) and the scale is written as its UE8M0 code, the biased
+// exponent byte.
+//
 // HBM-bound: per element it reads 4 (fp32) or 2 (bf16) bytes and writes 1, plus
 // 4 bytes of scale per 128 elements. Mapping: 16 lanes per group, 8 consecutive
 // elements per lane (one or two 16-byte loads), 4 groups per wave, so one wave
@@ -25,10 +31,10 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kGroupsPerBlock = kQuantThreads / 16;
 
-template <bool kBf16>
+template <bool kBf16, bool kE8>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
-                                                                  float* __restrict__ as, int64_t ld_as,
+                                                                  void* __restrict__ as, int64_t ld_as,
                                                                   int groups_per_row, int64_t total_groups) {
   const int sub = threadIdx.x & 15;  // which 8-element slice of the group
   const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
@@ -63,7 +69,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
 #pragma unroll
   for (int mask = 1; mask < 16; mask <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mask));
 
-  const float s = fmaxf(amax, 1e-10f) / 448.0f;  // correctly rounded divide
+  float s = fmaxf(amax, 1e-10f) / 448.0f;  // correctly rounded divide
+  if constexpr (kE8) s = __uint_as_float((__float_as_uint(s) + 0x7fffffu) & ~0x7fffffu);
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
@@ -75,23 +82,40 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
 
   if (valid) {
     *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(w0, w1);
-    if (sub == 0) as[(int64_t)g * ld_as + m] = s;
+    if (sub == 0) {
+      if constexpr (kE8) {
+        static_cast<uint8_t*>(as)[(int64_t)g * ld_as + m] = (uint8_t)(__float_as_uint(s) >> 23);
+      } else {
+        static_cast<float*>(as)[(int64_t)g * ld_as + m] = s;
+      }
+    }
   }
 }
 
 }  // namespace
 
+namespace {
+
+template <bool kBf16, bool kE8>
+void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as, int groups_per_row,
+                      int64_t total, hipStream_t stream) {
+  const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  hipLaunchKernelGGL((quant_act_kernel<kBf16, kE8>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, x, ldx,
+                     q, ldq, as, ld_as, groups_per_row, total);
+}
+
+}  // namespace
+
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                            int64_t ldq, float* as, int64_t ld_as, hipStream_t stream) {
+                            int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream) {
   const int groups_per_row = (int)(K / kBlock);
   const int64_t total = M * groups_per_row;
-  const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
   if (x_dtype == kInBf16) {
-    hipLaunchKernelGGL(quant_act_kernel<true>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, x, ldx, q,
-                       ldq, as, ld_as, groups_per_row, total);
+    if (e8) launch_quant_cfg<true, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
+    else launch_quant_cfg<true, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
   } else {
-    hipLaunchKernelGGL(quant_act_kernel<false>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, x, ldx, q,
-                       ldq, as, ld_as, groups_per_row, total);
+    if (e8) launch_quant_cfg<false, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
+    else launch_quant_cfg<false, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
   }
   return hipGetLastError();
 }

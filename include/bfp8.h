@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 2
+#define BFP8_ABI_VERSION 3
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -215,6 +215,40 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
                           const uint16_t* bias, uint16_t* c, int64_t ldc, int64_t N,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * UE8M0 (power-of-two) scale factors (page "transformers/integrations/deepgemm.py":
+ * _ceil_to_ue8m0, the use_ue8m0 recipe of _select_fp8_cast_kwargs, and float8_e8m0fnu scales
+ * in _coerce_sf_for_kernel). A scale is given by its UE8M0 code, one byte e standing for
+ * 2^(e - 127) (torch.float8_e8m0fnu); code 255 (NaN) is outside the contract.
+ *
+ * bfp8_quant_act_ue8m0: as bfp8_quant_act, but the group's float32 scale
+ * fl32(max(amax, 1e-10) / 448) is rounded up to a power of two by adding 2^23 - 1 to its bit
+ * pattern and clearing the mantissa bits; the group is divided by it (exactly) and its code
+ * is written to as[(k/128) * ld_as + m] (one byte; no alignment needed).
+ */
+bfp8_status_t bfp8_quant_act_ue8m0(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, uint8_t* as, int64_t ld_as, void* stream);
+
+/*
+ * bfp8_gemm and bfp8_grouped_gemm_contiguous with UE8M0 scale codes:
+ *   C[m, n] = bf16( sum_kb P_kb[m, n] * 2^(as[kb][m] - 127) * 2^(bs[n/128][kb] - 127) ).
+ * Same operands, layouts, workspace and errors as the float-scale calls, plus: as and bs
+ * 4-byte aligned and ld_as, ld_bs multiples of 4 (BFP8_ERR_MISALIGNED otherwise), since the
+ * kernels read the codes four at a time. The scales are applied by gfx950's scaled MFMA,
+ * which also accumulates the K blocks in its FP32 accumulator, so there is no separate
+ * promotion step; the sum is the matrix core's (within 2^-17 * (K/128 + 1) of the sum of
+ * absolute block terms, on top of the float-scale path's error, see the design notes).
+ */
+bfp8_status_t bfp8_gemm_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as,
+                              const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs,
+                              uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+bfp8_status_t bfp8_grouped_gemm_contiguous_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as,
+                                                 const uint8_t* b, int64_t ldb, const uint8_t* bs, int64_t ld_bs,
+                                                 const int32_t* grouped_layout, int32_t G,
+                                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Process-wide schedule override for bfp8_gemm (tests and benchmarks):
  * BFP8_SCHED_AUTO restores the automatic choice. Returns BFP8_ERR_INVALID_ARGUMENT

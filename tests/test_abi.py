@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 2
+    assert lib.bfp8_abi_version() == 3
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -188,6 +188,37 @@ def test_linear_rejections(lib, kw, status):
 
 def test_linear_m_zero_ok_without_device(lib):
     assert _linear(lib, M=0, x=None, ws=None, wsb=0) == _native.BFP8_OK
+
+
+def _gemm_e8(lib, a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=4, c=C, ldc=64, M=8, N=64, K=256):
+    return lib.bfp8_gemm_ue8m0(a, lda, as_, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ld_as=9), _native.BFP8_ERR_MISALIGNED),
+    (dict(ld_bs=2), _native.BFP8_ERR_MISALIGNED),
+    (dict(ld_bs=6), _native.BFP8_ERR_MISALIGNED),
+    (dict(as_=AS + 2), _native.BFP8_ERR_MISALIGNED),
+    (dict(bs=BS + 1), _native.BFP8_ERR_MISALIGNED),
+    (dict(ld_as=4), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=200), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(bs=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+])
+def test_gemm_ue8m0_rejections(lib, kw, status):
+    assert _gemm_e8(lib, **kw) == status, lib.bfp8_last_error_message()
+
+
+def test_ue8m0_m_zero_and_grouped(lib):
+    assert _gemm_e8(lib, M=0, a=None, as_=None, c=None) == _native.BFP8_OK
+    st = lib.bfp8_grouped_gemm_contiguous_ue8m0(A, 256, AS, 130, B, 256, BS, 4, 0x60000000, 2, C, 64, 128, 64, 256,
+                                                None, 0, None)
+    assert st == _native.BFP8_ERR_MISALIGNED, lib.bfp8_last_error_message()
+
+
+def test_quant_ue8m0_accepts_byte_aligned_scales(lib):
+    # one-byte codes need no alignment and any ld_as >= M; M = 0 is a no-op
+    assert lib.bfp8_quant_act_ue8m0(A, 0, 0, 256, 256, B, 256, None, 0, None) == _native.BFP8_OK
+    assert lib.bfp8_quant_act_ue8m0(A, 0, 4, 256, 256, B, 256, AS, 3, None) == _native.BFP8_ERR_INVALID_ARGUMENT
 
 
 def _gpu_count():

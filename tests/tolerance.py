@@ -121,3 +121,42 @@ def compare_linear(got_bits, ref_out_bits, ref_c_bits, mag, k, what=""):
         raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {i}: "
                              f"got {got[i]!r} ref {ref[i]!r}")
     return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_out_bits))}
+
+
+# UE8M0 GEMMs: the scaled MFMA adds each K block's product to the running FP32 tile inside
+# the matrix core. Measured with one-wave probes (workload-like codes, the running value from
+# equal to 4096x the block's mass): error <= 2**-19 * (|running value| + block mass) per step.
+# With a 4x margin and |running value| <= mag, K/128 steps give at most
+#   (K/128 + 1) * 2**-17 * mag,
+# which replaces the float32-accumulation floor of the float-scale path.
+E8_STEP_ETA = 2.0**-17
+
+
+def compare_e8(got_bits, ref_bits, mag, k, what="", hw_block=None):
+    """compare() for the UE8M0 GEMMs: the stated bound plus the hardware accumulation floor."""
+    got = bf16.from_bits(got_bits)
+    ref = bf16.from_bits(ref_bits)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
+    stated = 2 * bf16.ulp(ref) + 1e-3 * np.abs(ref)
+    floor = (k / 128 + 1) * E8_STEP_ETA * mag
+    if hw_block is not None:
+        floor = floor + HW_BLOCK_ETA * hw_block
+    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3"
+    bad = d > stated + floor
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {d.size} elements over the bound, first at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r} bound {(stated + floor)[i]!r}")
+    return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_bits)) if d.size else 1.0,
+            "over_stated": int((d > stated).sum()), "n": int(d.size)}
+
+
+def reference_e8(a_q, a_e, b_q, b_e, rows=None, cols=None):
+    """(rows, cols, ref_bits, mag) from the oracle, UE8M0 scale codes."""
+    from oracle import ue8m0
+
+    return reference(a_q, ue8m0.decode(np.asarray(a_e)).astype(np.float32), b_q,
+                     ue8m0.decode(np.asarray(b_e)).astype(np.float32), rows, cols)

@@ -16,6 +16,10 @@ Workloads (all sizes N x K are weight shapes, A is [M, K]):
   * dense-transformer linears at hidden 5120: QKV (K=5120, N=10240),
     o_proj (K=8192, N=5120), gate+up (K=5120, N=51200), down (K=25600,
     N=5120); weights like the sweep's, activations bf16 N(0, 1) with seed 300 + M.
+  * UE8M0 weights (power-of-two block scales, the page "transformers/integrations/
+    deepgemm.py" checkpoints with float8_e8m0fnu scale factors): the e4m3 codes of
+    ``weight``, with scale codes drawn uniformly from [113, 121], i.e. scales 2**-14 ..
+    2**-6, the binades that U(0, 1e-2) mostly covers.
   * M-grouped contiguous MoE: 16 experts with weights [4096, 7168]; token counts
     ~ Multinomial(4096, Dirichlet(1)) (seed 4); each expert's rows padded up to a
     multiple of 128; a per-row int32 expert id, -1 on padding rows; bf16 N(0, 1)
@@ -68,6 +72,14 @@ def weight(n: int, k: int, seed: int) -> Weight:
     q = _fp8_codes_from_uniform(torch.rand(n, k, generator=g, dtype=torch.float32))
     s = torch.rand(_cdiv(n, BLOCK), _cdiv(k, BLOCK), generator=g, dtype=torch.float32) * 1e-2
     return Weight(q.contiguous(), s.contiguous())
+
+
+def weight_ue8m0(n: int, k: int, seed: int) -> Weight:
+    """e4m3 weight codes [N, K] and UE8M0 scale codes [ceil(N/128), ceil(K/128)] (uint8)."""
+    g = torch.Generator().manual_seed(seed)
+    q = _fp8_codes_from_uniform(torch.rand(n, k, generator=g, dtype=torch.float32))
+    e = torch.randint(113, 122, (_cdiv(n, BLOCK), _cdiv(k, BLOCK)), generator=g, dtype=torch.int32).to(torch.uint8)
+    return Weight(q.contiguous(), e.contiguous())
 
 
 def act_uniform(m: int, k: int, seed: int) -> torch.Tensor:
