@@ -23,7 +23,9 @@ Also reported (same JSON line):
   * per_m: per-shape GEMM latency (p50 of 5 replays of a captured HIP graph of
     back-to-back launches, so host launch cost is excluded), TFLOP/s and the fraction
     of the HBM (M <= 256) or FP8 (M >= 512) roofline, plus the quantizer's GB/s;
-  * cpu_baseline: the CPU oracle on a bounded sample of the same sweep.
+  * cpu_baseline: the CPU oracle on a bounded sample of the same sweep;
+  * per_m[...]["ue8m0"]: the same GEMM with power-of-two (UE8M0) scales, which the
+    hardware-scaled MFMA applies (bfp8_gemm_ue8m0; not part of the step).
 """
 
 from __future__ import annotations
@@ -257,7 +259,18 @@ def main() -> int:
             del g
             return float(np.median(trials))
 
+        w8 = workloads.weight_ue8m0(N, K, seed=1)  # the same e4m3 codes as the sweep's weight
+        if not torch.equal(w8.q, w.q):
+            raise RuntimeError("the UE8M0 weight must share the sweep weight's codes")
+        be8 = bfp8.ue8m0_scales(w8.s.to(dev))
         for m in sweep:
+            q8, e8 = bfp8.quant_act_ue8m0(xs[m])
+            c8 = torch.empty_like(cs[m])
+
+            def gemm8_calls(n):
+                for j in range(n):
+                    bfp8.gemm_ue8m0(q8, e8, bq[j % copies], be8, out=c8)
+
             def gemm_calls(n):
                 for j in range(n):
                     i = j % copies
@@ -268,7 +281,8 @@ def main() -> int:
                     bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
 
             calls = copies if m <= 2048 else max(copies // 4, 4)
-            res = {"gemm": graph_time_us(gemm_calls, calls), "quant": graph_time_us(quant_calls, min(calls, 32))}
+            res = {"gemm": graph_time_us(gemm_calls, calls), "quant": graph_time_us(quant_calls, min(calls, 32)),
+                   "gemm_ue8m0": graph_time_us(gemm8_calls, calls)}
             us = res["gemm"]
             tflops = 2.0 * m * N * K / (us * 1e-6) / 1e12
             gbs = gemm_alg_bytes(m) / (us * 1e-6) / 1e9
@@ -278,10 +292,12 @@ def main() -> int:
             per_m[str(m)] = {"gemm_us": round(us, 2), "tflops": round(tflops, 1), "alg_gbs": round(gbs, 1),
                              "bound": "hbm" if hbm_bound else "mfma", "frac": round(frac, 4),
                              "schedule": bfp8.schedule_for(m, N, K), "quant_us": round(res["quant"], 2),
-                             "quant_gbs": round(qgbs, 1)}
+                             "quant_gbs": round(qgbs, 1),
+                             "ue8m0": {"gemm_us": round(res["gemm_ue8m0"], 2),
+                                       "tflops": round(2.0 * m * N * K / (res["gemm_ue8m0"] * 1e-6) / 1e12, 1)}}
             log(f"M={m:5d}  gemm {us:8.2f} us  {tflops:8.1f} TFLOP/s  {gbs:7.1f} GB/s  "
                 f"{'HBM' if hbm_bound else 'FP8'} frac {frac:.3f}  [{per_m[str(m)]['schedule']}]   "
-                f"quant {res['quant']:7.2f} us {qgbs:7.1f} GB/s")
+                f"quant {res['quant']:7.2f} us {qgbs:7.1f} GB/s   ue8m0 gemm {res['gemm_ue8m0']:8.2f} us")
 
     cpu = None
     if not args.no_cpu_baseline and not args.only_m:
