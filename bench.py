@@ -62,6 +62,18 @@ def quant_alg_bytes(m: int, k: int = K, in_bytes: int = 4) -> int:
     return m * k * in_bytes + m * k + m * (k // 128) * 4
 
 
+RIDGE_FLOP_PER_BYTE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def roofline_entry(us: float, flops: float, alg_bytes: float) -> dict:
+    """Time, rates and the fraction of the roofline that bounds this shape (HBM below the ridge)."""
+    tflops = flops / (us * 1e-6) / 1e12
+    gbs = alg_bytes / (us * 1e-6) / 1e9
+    hbm = flops / alg_bytes < RIDGE_FLOP_PER_BYTE
+    return {"us": round(us, 2), "tflops": round(tflops, 1), "alg_gbs": round(gbs, 1), "bound": "hbm" if hbm else "mfma",
+            "frac": round(gbs / PEAK_HBM_GBS if hbm else tflops / PEAK_FP8_TFLOPS, 4)}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -120,6 +132,8 @@ def main() -> int:
     ap.add_argument("--no-table", action="store_true", help="skip the per-M latency table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-m", type=int, default=0, help="profile helper: run only this M (steps of GEMM+quant)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the transformer-linear and MoE grouped-GEMM configurations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (for counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -234,30 +248,31 @@ def main() -> int:
 
     # ---- per-M table: back-to-back launches replayed from a captured HIP graph (so host-side
     # launch cost is not measured), p50 of 5 trials; cold mode cycles the weight copies ----
+    graph_stream = torch.cuda.Stream(dev)
+
+    def graph_time_us(fn, calls: int) -> float:
+        """Median per-call time of `calls` back-to-back calls of fn, captured once and replayed."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(graph_stream):
+            fn(calls)  # warm the code paths on the capture stream
+            graph_stream.synchronize()
+            with torch.cuda.graph(g, stream=graph_stream):
+                fn(calls)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        trials = []
+        for _ in range(5):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            trials.append(e0.elapsed_time(e1) * 1e3 / calls)
+        del g
+        return float(np.median(trials))
+
     per_m = {}
     if not args.no_table:
-        graph_stream = torch.cuda.Stream(dev)
-
-        def graph_time_us(fn, calls: int) -> float:
-            """Median per-call time of `calls` back-to-back calls of fn, captured once and replayed."""
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(graph_stream):
-                fn(calls)  # warm the code paths on the capture stream
-                graph_stream.synchronize()
-                with torch.cuda.graph(g, stream=graph_stream):
-                    fn(calls)
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            trials = []
-            for _ in range(5):
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                trials.append(e0.elapsed_time(e1) * 1e3 / calls)
-            del g
-            return float(np.median(trials))
 
         w8 = workloads.weight_ue8m0(N, K, seed=1)  # the same e4m3 codes as the sweep's weight
         if not torch.equal(w8.q, w.q):
@@ -293,11 +308,69 @@ def main() -> int:
                              "bound": "hbm" if hbm_bound else "mfma", "frac": round(frac, 4),
                              "schedule": bfp8.schedule_for(m, N, K), "quant_us": round(res["quant"], 2),
                              "quant_gbs": round(qgbs, 1),
-                             "ue8m0": {"gemm_us": round(res["gemm_ue8m0"], 2),
-                                       "tflops": round(2.0 * m * N * K / (res["gemm_ue8m0"] * 1e-6) / 1e12, 1)}}
+                             "ue8m0": roofline_entry(res["gemm_ue8m0"], 2.0 * m * N * K,
+                                                     gemm_alg_bytes(m) - m * (K // 128) * 3 - (N // 128) * (K // 128) * 3)}
             log(f"M={m:5d}  gemm {us:8.2f} us  {tflops:8.1f} TFLOP/s  {gbs:7.1f} GB/s  "
                 f"{'HBM' if hbm_bound else 'FP8'} frac {frac:.3f}  [{per_m[str(m)]['schedule']}]   "
                 f"quant {res['quant']:7.2f} us {qgbs:7.1f} GB/s   ue8m0 gemm {res['gemm_ue8m0']:8.2f} us")
+
+    # ---- the other workload configurations (not part of the step): the FP8 linear layer on the
+    # hidden-5120 transformer shapes, and the M-grouped contiguous MoE GEMM ----
+    configs = {}
+    if not args.no_configs and not args.only_m:
+        del bq, bsc  # the sweep's weight copies
+        torch.cuda.empty_cache()
+        lin = {}
+        for layer, (n_l, k_l) in workloads.TRANSFORMER_LAYERS.items():
+            wl = workloads.transformer_weight(layer)
+            n_copies = max(1, min(6, -(-2 * LLC_BYTES // (n_l * k_l)) + 1))
+            wq_l = [wl.q.to(dev) for _ in range(n_copies)]
+            ws_l = [wl.s.to(dev) for _ in range(n_copies)]
+            lin[layer] = {}
+            for m in workloads.TRANSFORMER_M:
+                x_l = workloads.transformer_act(layer, m).to(dev)
+                o_l = torch.empty((m, n_l), dtype=torch.bfloat16, device=dev)
+                wsp = torch.empty(bfp8.linear_workspace_bytes(m, n_l, k_l), dtype=torch.uint8, device=dev)
+
+                def lin_calls(n, x_l=x_l, o_l=o_l, wsp=wsp, wq_l=wq_l, ws_l=ws_l):
+                    for j in range(n):
+                        bfp8.linear(x_l, wq_l[j % len(wq_l)], ws_l[j % len(wq_l)], out=o_l, workspace=wsp)
+
+                us = graph_time_us(lin_calls, 2 * n_copies if m < 2048 else n_copies)
+                kb_l = k_l // 128
+                alg = 2 * m * k_l + n_l * k_l + (-(-n_l // 128)) * kb_l * 4 + 2 * m * n_l
+                lin[layer][str(m)] = {"n": n_l, "k": k_l, **roofline_entry(us, 2.0 * m * n_l * k_l, alg)}
+                log(f"linear {layer:8s} M={m:5d} N={n_l} K={k_l}: {us:8.2f} us  {lin[layer][str(m)]['tflops']:8.1f} "
+                    f"TFLOP/s  {lin[layer][str(m)]['bound']} frac {lin[layer][str(m)]['frac']:.3f}")
+            del wq_l, ws_l
+            torch.cuda.empty_cache()
+        configs["transformer_linear"] = {"what": "bfp8_linear (bf16 x quantized per 1x128 group, blockwise FP8 GEMM, "
+                                                 "bf16 out), graph replay of back-to-back calls",
+                                         "layers": lin}
+        case = workloads.moe_case()
+        bq_g = torch.stack([w_.q for w_ in case.weights]).to(dev)
+        bs_g = torch.stack([w_.s for w_ in case.weights]).to(dev)
+        q_g, s_g = bfp8.quant_act(case.act.to(dev))
+        lay_g = case.layout.to(dev)
+        out_g = torch.empty((case.layout.numel(), workloads.MOE_N), dtype=torch.bfloat16, device=dev)
+
+        def grouped_calls(n):
+            for _ in range(n):
+                bfp8.grouped_gemm_contiguous(q_g, s_g, bq_g, bs_g, lay_g, out=out_g)
+
+        us = graph_time_us(grouped_calls, 4)
+        m_real = int(case.counts.sum())
+        m_pad = case.layout.numel()
+        g_n, g_k, g_g = workloads.MOE_N, workloads.MOE_K, workloads.MOE_GROUPS
+        alg = m_pad * g_k + m_pad * (g_k // 128) * 4 + g_g * (g_n * g_k + (g_n // 128) * (g_k // 128) * 4) + 2 * m_real * g_n
+        configs["moe_grouped"] = {"groups": g_g, "n": g_n, "k": g_k, "tokens": m_real, "padded_rows": m_pad,
+                                  "flops": "2 * tokens * N * K (padding rows not counted)",
+                                  **roofline_entry(us, 2.0 * m_real * g_n * g_k, alg)}
+        log(f"grouped MoE G={g_g} N={g_n} K={g_k} tokens={m_real} (padded {m_pad}): {us:8.2f} us  "
+            f"{configs['moe_grouped']['tflops']:8.1f} TFLOP/s  {configs['moe_grouped']['bound']} "
+            f"frac {configs['moe_grouped']['frac']:.3f}")
+        del bq_g, bs_g
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline and not args.only_m:
@@ -324,6 +397,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_m": per_m,
+        "configs": configs,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out, ensure_ascii=False), flush=True)
