@@ -24,6 +24,9 @@ What is computed, and where it is defined on the pages:
   (per-row expert id, -1 on padding rows) and ``deepgemm_fp8_fp4_experts_forward``.
 * FP8 linear layer (``linear.linear_ref``): page "transformers/integrations/deepgemm.py",
   ``deepgemm_fp8_fp4_linear`` (quantize, GEMM into a bf16 output, then add the bias to it).
+* MoE chain (``moe``): same page, ``_dispatch_routed_input``, ``_build_deepgemm_contiguous_layout``,
+  ``deepgemm_fp8_fp4_experts_forward`` and ``_combine_routed_output`` (routing layout, the
+  expert MLP with the gate activation between the two grouped GEMMs, weighted top-k combine).
 * UE8M0 (power-of-two) scale factors (``ue8m0``): same page, ``_ceil_to_ue8m0``,
   ``_select_fp8_cast_kwargs`` (``use_ue8m0``) and ``_coerce_sf_for_kernel``
   (``float8_e8m0fnu`` codes): the quantizer with its scale rounded up to a power of two,
@@ -34,6 +37,6 @@ routines, brute force with exact rationals, closed forms and invariants); none
 is "parity unpinned".
 """
 
-from . import bf16, e4m3, gemm, linear, quant, ue8m0  # noqa: F401
+from . import bf16, e4m3, gemm, linear, moe, quant, ue8m0  # noqa: F401
 
-__all__ = ["bf16", "e4m3", "gemm", "linear", "quant", "ue8m0"]
+__all__ = ["bf16", "e4m3", "gemm", "linear", "moe", "quant", "ue8m0"]
