@@ -24,7 +24,9 @@ from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
     "quant_act", "gemm", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
-    "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales", "set_schedule", "get_schedule", "schedule_for",
+    "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
+    "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
+    "moe_forward_workspace_bytes", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
 
@@ -376,6 +378,138 @@ def grouped_gemm_contiguous_ue8m0(a_q: torch.Tensor, a_e: torch.Tensor, b_q: tor
         b_e.data_ptr(), b_e.stride(1), layout.data_ptr(), g, out.data_ptr(), out.stride(0), m, n, k, None, 0,
         _stream(a_q.device))
     _check(st, "bfp8_grouped_gemm_contiguous_ue8m0")
+    return out
+
+
+def moe_padded_rows(s: int, e: int, align: int = 128) -> int:
+    """Rows of the padded MoE buffer for s (token, expert) pairs and e experts."""
+    return _native.lib().bfp8_moe_padded_rows(s, e, align)
+
+
+def moe_dispatch(topk_ids: torch.Tensor, num_experts: int, align: int = 128):
+    """Routing layout on the device: (row_of_pair [S], pair_of_row [R], layout [R], expert_start [E+1]),
+    int32, for topk_ids [T, top_k] (ids outside [0, E) are sentinels)."""
+    _require(topk_ids, "topk_ids", torch.int32, 2)
+    ids = topk_ids.contiguous()
+    s_pairs = ids.numel()
+    lib = _native.lib()
+    rows = lib.bfp8_moe_padded_rows(s_pairs, num_experts, align)
+    dev = ids.device
+    row_of_pair = torch.empty(s_pairs, dtype=torch.int32, device=dev)
+    pair_of_row = torch.empty(rows, dtype=torch.int32, device=dev)
+    layout = torch.empty(rows, dtype=torch.int32, device=dev)
+    expert_start = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    scratch = torch.empty(max(lib.bfp8_moe_dispatch_workspace_bytes(s_pairs, num_experts), 4), dtype=torch.uint8,
+                          device=dev)
+    st = lib.bfp8_moe_dispatch(ids.data_ptr(), s_pairs, num_experts, align, row_of_pair.data_ptr(),
+                               pair_of_row.data_ptr(), layout.data_ptr(), expert_start.data_ptr(), scratch.data_ptr(),
+                               scratch.numel(), _stream(dev))
+    _check(st, "bfp8_moe_dispatch")
+    return row_of_pair, pair_of_row, layout, expert_start
+
+
+def quant_act_gather(x: torch.Tensor, row_src: torch.Tensor, src_div: int = 1):
+    """quant_act of the gathered rows: output row m quantizes x[row_src[m] // src_div]; rows with
+    row_src[m] < 0 are left unwritten. Returns (q [M, K], s [M, K/128] group-major)."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise NotImplementedError(f"quant_act_gather takes float32 or bfloat16 input, got {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    _require(row_src, "row_src", torch.int32, 1)
+    if x.stride(1) != 1 or not row_src.is_contiguous():
+        raise ValueError("x must be K-contiguous and row_src contiguous")
+    m, k = row_src.numel(), x.shape[1]
+    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    s = torch.empty((k // 128, m), dtype=torch.float32, device=x.device).t()
+    dt = _native.BFP8_IN_F32 if x.dtype == torch.float32 else _native.BFP8_IN_BF16
+    st = _native.lib().bfp8_quant_act_gather(x.data_ptr(), dt, x.shape[0], k, x.stride(0), row_src.data_ptr(),
+                                             src_div, m, q.data_ptr(), q.stride(0), s.data_ptr(), max(m, 1),
+                                             _stream(x.device))
+    _check(st, "bfp8_quant_act_gather")
+    return q, s
+
+
+def swiglu_quant(proj: torch.Tensor, layout: torch.Tensor | None = None):
+    """h = bf16(bf16(silu(gate)) * up) of proj [M, 2I] (bf16, gate first) quantized per 1x128 group:
+    returns (q [M, I], s [M, I/128] group-major); rows with layout == -1 are left unwritten."""
+    _require(proj, "proj", torch.bfloat16, 2)
+    if proj.stride(1) != 1:
+        raise ValueError("proj must be contiguous along its columns")
+    m, two_i = proj.shape
+    i = two_i // 2
+    if layout is not None:
+        _require(layout, "layout", torch.int32, 1)
+        if layout.numel() != m or not layout.is_contiguous():
+            raise ValueError("layout must be a contiguous int32 vector of M entries")
+    q = torch.empty((m, i), dtype=torch.uint8, device=proj.device)
+    s = torch.empty((i // 128, m), dtype=torch.float32, device=proj.device).t()
+    st = _native.lib().bfp8_swiglu_quant(proj.data_ptr(), m, i, proj.stride(0),
+                                         layout.data_ptr() if layout is not None else None, q.data_ptr(), q.stride(0),
+                                         s.data_ptr(), max(m, 1), _stream(proj.device))
+    _check(st, "bfp8_swiglu_quant")
+    return q, s
+
+
+def moe_combine(out: torch.Tensor, row_of_pair: torch.Tensor, topk_weights: torch.Tensor) -> torch.Tensor:
+    """y [T, H] = per token, sum_j bf16(out[row_of_pair[t, j]] * bf16(w[t, j])) (float32 sum, in order j)."""
+    _require(out, "out", torch.bfloat16, 2)
+    _require(topk_weights, "topk_weights", torch.float32, 2)
+    _require(row_of_pair, "row_of_pair", torch.int32, row_of_pair.dim())
+    t, k = topk_weights.shape
+    if row_of_pair.numel() != t * k or not row_of_pair.is_contiguous() or not topk_weights.is_contiguous():
+        raise ValueError("row_of_pair and topk_weights must be contiguous with T * top_k entries")
+    h = out.shape[1]
+    y = torch.empty((t, h), dtype=torch.bfloat16, device=out.device)
+    st = _native.lib().bfp8_moe_combine(out.data_ptr(), out.stride(0), row_of_pair.data_ptr(), topk_weights.data_ptr(),
+                                        t, k, h, y.data_ptr(), y.stride(0), _stream(out.device))
+    _check(st, "bfp8_moe_combine")
+    return y
+
+
+def moe_forward_workspace_bytes(t: int, top_k: int, e: int, h: int, i: int) -> int:
+    return _native.lib().bfp8_moe_forward_workspace_bytes(t, top_k, e, h, i)
+
+
+def moe_forward(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w_up: torch.Tensor,
+                s_up: torch.Tensor, w_down: torch.Tensor, s_down: torch.Tensor, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """FP8 experts forward: hidden [T, H] bf16, topk_ids [T, k] int32, topk_weights [T, k] float32,
+    w_up [E, 2I, H] e4m3 with s_up [E, 2I/128, H/128], w_down [E, H, I] with s_down [E, H/128, I/128]."""
+    _require(hidden, "hidden", torch.bfloat16, 2)
+    _require(topk_ids, "topk_ids", torch.int32, 2)
+    _require(topk_weights, "topk_weights", torch.float32, 2)
+    w_up, w_down = _as_u8(w_up, "w_up"), _as_u8(w_down, "w_down")
+    _require(w_up, "w_up", torch.uint8, 3)
+    _require(w_down, "w_down", torch.uint8, 3)
+    _require(s_up, "s_up", torch.float32, 3)
+    _require(s_down, "s_down", torch.float32, 3)
+    t, h = hidden.shape
+    e, two_i, h2 = w_up.shape
+    i = two_i // 2
+    if h2 != h or tuple(w_down.shape) != (e, h, i) or topk_ids.shape != topk_weights.shape or topk_ids.shape[0] != t:
+        raise ValueError("shape mismatch between hidden, routing and expert weights")
+    if tuple(s_up.shape) != (e, -(-two_i // 128), h // 128) or tuple(s_down.shape) != (e, -(-h // 128), i // 128):
+        raise ValueError("scale shapes do not match the expert weights")
+    for name, ten in (("w_up", w_up), ("w_down", w_down), ("s_up", s_up), ("s_down", s_down),
+                      ("topk_ids", topk_ids), ("topk_weights", topk_weights)):
+        if not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if hidden.stride(1) != 1:
+        raise ValueError("hidden must be contiguous along H")
+    if out is None:
+        out = torch.empty((t, h), dtype=torch.bfloat16, device=hidden.device)
+    _require(out, "out", torch.bfloat16, 2)
+    lib = _native.lib()
+    need = lib.bfp8_moe_forward_workspace_bytes(t, topk_ids.shape[1], e, h, i)
+    if workspace is None:
+        ws_ptr, ws_bytes = _workspace(hidden.device, need)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib.bfp8_moe_forward(hidden.data_ptr(), t, h, hidden.stride(0), topk_ids.data_ptr(), topk_weights.data_ptr(),
+                              topk_ids.shape[1], e, w_up.data_ptr(), s_up.data_ptr(), w_down.data_ptr(),
+                              s_down.data_ptr(), i, out.data_ptr(), out.stride(0), ws_ptr or None, ws_bytes,
+                              _stream(hidden.device))
+    _check(st, "bfp8_moe_forward")
     return out
 
 

@@ -37,6 +37,16 @@ SIGNATURES = [
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_grouped_gemm_contiguous_ue8m0", ctypes.c_int,
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_moe_padded_rows", _i64, [_i64, _i32, _i32]),
+    ("bfp8_moe_dispatch_workspace_bytes", _sz, [_i64, _i32]),
+    ("bfp8_moe_dispatch", ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    ("bfp8_quant_act_gather", ctypes.c_int,
+     [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
+    ("bfp8_swiglu_quant", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]),
+    ("bfp8_moe_combine", ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _i64, _vp]),
+    ("bfp8_moe_forward_workspace_bytes", _sz, [_i64, _i32, _i32, _i64, _i64]),
+    ("bfp8_moe_forward", ctypes.c_int,
+     [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     ("bfp8_linear_workspace_bytes", _sz, [_i64, _i64, _i64]),
     ("bfp8_linear", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),

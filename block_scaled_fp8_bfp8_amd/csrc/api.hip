@@ -336,6 +336,247 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
   return launch_dense(q, K, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream);
 }
 
+// ---- MoE chain ------------------------------------------------------------------------------
+
+int64_t bfp8_moe_padded_rows(int64_t S, int32_t E, int32_t align) {
+  if (S < 0 || E < 1 || align < 1) return 0;
+  const int64_t bound = S + (S < E ? S : (int64_t)E) * (align - 1);
+  return (bound + align - 1) / align * align;
+}
+
+size_t bfp8_moe_dispatch_workspace_bytes(int64_t S, int32_t E) {
+  if (S < 0 || E < 1) return 0;
+  return (size_t)(bfp8::moe_dispatch_blocks(S) * E + E) * 4;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int32_t kMaxExperts = 1024;  // the placement kernel keeps 16 x E counters in LDS
+
+bfp8_status_t check_dispatch_args(const int32_t* ids, int64_t S, int32_t E, int32_t align, const int32_t* row_of_pair,
+                                  const int32_t* pair_of_row, const int32_t* layout, const int32_t* expert_start) {
+  if (S < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "S = %lld is negative", (long long)S);
+  if (E < 1 || E > kMaxExperts) return fail(BFP8_ERR_UNSUPPORTED, "E = %d must be in [1, %d]", (int)E, (int)kMaxExperts);
+  if (align < 1 || align > 4096) return fail(BFP8_ERR_INVALID_ARGUMENT, "alignment %d must be in [1, 4096]", (int)align);
+  if (bfp8_moe_padded_rows(S, E, align) > (int64_t)INT32_MAX)
+    return fail(BFP8_ERR_UNSUPPORTED, "the padded buffer of %lld pairs would exceed 2^31 rows", (long long)S);
+  if (S > 0 && (!ids || !row_of_pair || !pair_of_row || !layout))
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "ids, row_of_pair, pair_of_row and layout must not be NULL when S > 0");
+  if (!expert_start) return fail(BFP8_ERR_INVALID_ARGUMENT, "expert_start must not be NULL");
+  if (!aligned(ids, 4) || !aligned(row_of_pair, 4) || !aligned(pair_of_row, 4) || !aligned(layout, 4) ||
+      !aligned(expert_start, 4))
+    return fail(BFP8_ERR_MISALIGNED, "the int32 arrays must be 4-byte aligned");
+  return BFP8_OK;
+}
+
+bfp8_status_t dispatch(const int32_t* ids, int64_t S, int32_t E, int32_t align, int32_t* row_of_pair,
+                       int32_t* pair_of_row, int32_t* layout, int32_t* expert_start, int32_t* scratch,
+                       void* stream) {
+  const int64_t rows = bfp8_moe_padded_rows(S, E, align);
+  int32_t* block_counts = scratch;
+  int32_t* expert_count = scratch + bfp8::moe_dispatch_blocks(S) * E;
+  return launched(bfp8::launch_moe_dispatch(ids, S, E, align, rows, row_of_pair, pair_of_row, layout, expert_start,
+                                            expert_count, block_counts, (hipStream_t)stream),
+                  "moe_dispatch");
+}
+
+bfp8_status_t check_swiglu_args(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout,
+                                const uint8_t* q, int64_t ldq, const float* as, int64_t ld_as) {
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (I < bfp8::kBlock || I % bfp8::kBlock != 0 || I > kMaxDim)
+    return fail(BFP8_ERR_UNSUPPORTED, "I = %lld must be a positive multiple of 128 (at most 2^30)", (long long)I);
+  if (M > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M must be at most 2^30");
+  if (M == 0) return BFP8_OK;
+  if (!proj || !q || !as) return fail(BFP8_ERR_INVALID_ARGUMENT, "proj, q and as must not be NULL");
+  if (ldp < 2 * I) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldp = %lld < 2 I = %lld", (long long)ldp, (long long)(2 * I));
+  if (ldq < I) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldq = %lld < I = %lld", (long long)ldq, (long long)I);
+  if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
+  if ((ldp * 2) % 16 || ldq % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
+  if (!aligned(proj, 16) || !aligned(q, 16) || !aligned(as, 4) || !aligned(layout, 4))
+    return fail(BFP8_ERR_MISALIGNED, "proj and q must be 16-byte aligned, as and layout 4-byte aligned");
+  return BFP8_OK;
+}
+
+bfp8_status_t check_combine_args(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair, const float* w,
+                                 int64_t T, int32_t top_k, int64_t H, const uint16_t* y, int64_t ldy) {
+  if (T < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "T = %lld is negative", (long long)T);
+  if (top_k < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "top_k = %d must be >= 1", (int)top_k);
+  if (H < 8 || H % 8 != 0 || H > kMaxDim)
+    return fail(BFP8_ERR_UNSUPPORTED, "H = %lld must be a positive multiple of 8", (long long)H);
+  if (T * top_k > (int64_t)INT32_MAX) return fail(BFP8_ERR_UNSUPPORTED, "T * top_k must be below 2^31");
+  if (T == 0) return BFP8_OK;
+  if (!out || !row_of_pair || !w || !y)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "out, row_of_pair, weights and y must not be NULL");
+  if (ldo < H || ldy < H) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldo and ldy must be >= H");
+  if ((ldo * 2) % 16 || (ldy * 2) % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
+  if (!aligned(out, 16) || !aligned(y, 16) || !aligned(row_of_pair, 4) || !aligned(w, 4))
+    return fail(BFP8_ERR_MISALIGNED, "out and y must be 16-byte aligned, row_of_pair and weights 4-byte aligned");
+  return BFP8_OK;
+}
+
+// Workspace of the MoE forward, each part 256-byte aligned.
+struct MoeLayout {
+  size_t row_of_pair, pair_of_row, layout, expert_start, scratch, q, as, proj, q2, as2, out, total;
+  int64_t rows;
+};
+
+MoeLayout moe_layout(int64_t T, int32_t top_k, int32_t E, int64_t H, int64_t I) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  MoeLayout L{};
+  const int64_t S = T * top_k;
+  L.rows = bfp8_moe_padded_rows(S, E, bfp8::kBlock);
+  const size_t R = (size_t)L.rows;
+  size_t off = 0;
+  L.row_of_pair = off; off += up(4 * (size_t)S);
+  L.pair_of_row = off; off += up(4 * R);
+  L.layout = off; off += up(4 * R);
+  L.expert_start = off; off += up(4 * ((size_t)E + 1));
+  L.scratch = off; off += up(bfp8_moe_dispatch_workspace_bytes(S, E));
+  L.q = off; off += up(R * (size_t)H);
+  L.as = off; off += up(4 * (size_t)(H / bfp8::kBlock) * R);
+  L.proj = off; off += up(2 * R * 2 * (size_t)I);
+  L.q2 = off; off += up(R * (size_t)I);
+  L.as2 = off; off += up(4 * (size_t)(I / bfp8::kBlock) * R);
+  L.out = off; off += up(2 * R * (size_t)H);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+bfp8_status_t bfp8_moe_dispatch(const int32_t* topk_ids, int64_t S, int32_t E, int32_t align, int32_t* row_of_pair,
+                                int32_t* pair_of_row, int32_t* layout, int32_t* expert_start, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  bfp8_status_t st = check_dispatch_args(topk_ids, S, E, align, row_of_pair, pair_of_row, layout, expert_start);
+  if (st != BFP8_OK) return st;
+  const size_t need = bfp8_moe_dispatch_workspace_bytes(S, E);
+  if (!workspace || workspace_bytes < need)
+    return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!aligned(workspace, 4)) return fail(BFP8_ERR_MISALIGNED, "workspace must be 4-byte aligned");
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return dispatch(topk_ids, S, E, align, row_of_pair, pair_of_row, layout, expert_start,
+                  static_cast<int32_t*>(workspace), stream);
+}
+
+bfp8_status_t bfp8_quant_act_gather(const void* x, int x_dtype, int64_t src_rows, int64_t K, int64_t ldx,
+                                    const int32_t* row_src, int32_t src_div, int64_t M, uint8_t* q, int64_t ldq,
+                                    float* as, int64_t ld_as, void* stream) {
+  bfp8_status_t st = check_quant_args(x, x_dtype, M, K, ldx, q, ldq, as, ld_as);
+  if (st != BFP8_OK || M == 0) return st;
+  if (src_rows < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "src_rows = %lld must be >= 1", (long long)src_rows);
+  if (src_div < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "src_div = %d must be >= 1", (int)src_div);
+  if (!row_src) return fail(BFP8_ERR_INVALID_ARGUMENT, "row_src must not be NULL");
+  if (!aligned(row_src, 4)) return fail(BFP8_ERR_MISALIGNED, "row_src must be 4-byte aligned");
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, false, (hipStream_t)stream,
+                                         row_src, src_div),
+                  "quant_act_gather");
+}
+
+bfp8_status_t bfp8_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout,
+                                uint8_t* q, int64_t ldq, float* as, int64_t ld_as, void* stream) {
+  bfp8_status_t st = check_swiglu_args(proj, M, I, ldp, layout, q, ldq, as, ld_as);
+  if (st != BFP8_OK || M == 0) return st;
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_swiglu_quant(proj, M, I, ldp, layout, q, ldq, as, ld_as, (hipStream_t)stream),
+                  "swiglu_quant");
+}
+
+bfp8_status_t bfp8_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair,
+                               const float* topk_weights, int64_t T, int32_t top_k, int64_t H, uint16_t* y,
+                               int64_t ldy, void* stream) {
+  bfp8_status_t st = check_combine_args(out, ldo, row_of_pair, topk_weights, T, top_k, H, y, ldy);
+  if (st != BFP8_OK || T == 0) return st;
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_moe_combine(out, ldo, row_of_pair, topk_weights, T, top_k, H, y, ldy,
+                                           (hipStream_t)stream),
+                  "moe_combine");
+}
+
+size_t bfp8_moe_forward_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int64_t H, int64_t I) {
+  if (T <= 0 || top_k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  if (T * top_k > (int64_t)INT32_MAX || H > kMaxDim || I > kMaxDim) return 0;
+  return moe_layout(T, top_k, E, H, I).total;
+}
+
+bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int64_t ldh, const int32_t* topk_ids,
+                               const float* topk_weights, int32_t top_k, int32_t E, const uint8_t* w_up,
+                               const float* s_up, const uint8_t* w_down, const float* s_down, int64_t I, uint16_t* y,
+                               int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "T = %lld is negative", (long long)T);
+  if (top_k < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "top_k = %d must be >= 1", (int)top_k);
+  if (E < 1 || E > kMaxExperts) return fail(BFP8_ERR_UNSUPPORTED, "E = %d must be in [1, %d]", (int)E, (int)kMaxExperts);
+  if (H < bfp8::kBlock || H % bfp8::kBlock != 0 || I < bfp8::kBlock || I % bfp8::kBlock != 0)
+    return fail(BFP8_ERR_UNSUPPORTED, "H and I must be positive multiples of 128");
+  if (H > kMaxDim || I > kMaxDim || T * top_k > (int64_t)INT32_MAX / 2)
+    return fail(BFP8_ERR_UNSUPPORTED, "sizes too large");
+  if (!w_up || !s_up || !w_down || !s_down) return fail(BFP8_ERR_INVALID_ARGUMENT, "weights must not be NULL");
+  if (T == 0) return ok();
+  if (!hidden || !topk_ids || !topk_weights || !y)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "hidden, topk_ids, topk_weights and y must not be NULL");
+  if (ldh < H || (ldh * 2) % 16 || !aligned(hidden, 16))
+    return fail(BFP8_ERR_MISALIGNED, "hidden: ldh >= H, rows 16-byte aligned");
+  const MoeLayout L = moe_layout(T, top_k, E, H, I);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  if (!aligned(workspace, 256)) return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t S = T * top_k, R = L.rows;
+  int32_t* row_of_pair = reinterpret_cast<int32_t*>(ws + L.row_of_pair);
+  int32_t* pair_of_row = reinterpret_cast<int32_t*>(ws + L.pair_of_row);
+  int32_t* layout = reinterpret_cast<int32_t*>(ws + L.layout);
+  int32_t* expert_start = reinterpret_cast<int32_t*>(ws + L.expert_start);
+  uint8_t* q = ws + L.q;
+  float* as = reinterpret_cast<float*>(ws + L.as);
+  uint16_t* proj = reinterpret_cast<uint16_t*>(ws + L.proj);
+  uint8_t* q2 = ws + L.q2;
+  float* as2 = reinterpret_cast<float*>(ws + L.as2);
+  uint16_t* out = reinterpret_cast<uint16_t*>(ws + L.out);
+  // Every argument of every step, validated before the first launch.
+  bfp8_status_t st = check_dispatch_args(topk_ids, S, E, bfp8::kBlock, row_of_pair, pair_of_row, layout, expert_start);
+  if (st == BFP8_OK) st = check_quant_args(hidden, BFP8_IN_BF16, R, H, ldh, q, H, as, R);
+  if (st == BFP8_OK)
+    st = check_gemm_args(q, H, as, R, w_up, H, s_up, H / bfp8::kBlock, proj, 2 * I, R, 2 * I, H, nullptr, 0, true);
+  if (st == BFP8_OK) st = check_swiglu_args(proj, R, I, 2 * I, layout, q2, I, as2, R);
+  if (st == BFP8_OK)
+    st = check_gemm_args(q2, I, as2, R, w_down, I, s_down, I / bfp8::kBlock, out, H, R, H, I, nullptr, 0, true);
+  if (st == BFP8_OK) st = check_combine_args(out, H, row_of_pair, topk_weights, T, top_k, H, y, ldy);
+  if (st != BFP8_OK) return st;
+  if ((int64_t)E * 2 * I * H > ((int64_t)1 << 40) || (int64_t)E * H * I > ((int64_t)1 << 40))
+    return fail(BFP8_ERR_UNSUPPORTED, "expert weights too large");
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  st = dispatch(topk_ids, S, E, bfp8::kBlock, row_of_pair, pair_of_row, layout, expert_start,
+                reinterpret_cast<int32_t*>(ws + L.scratch), stream);
+  if (st != BFP8_OK) return st;
+  st = launched(bfp8::launch_quant_act(hidden, BFP8_IN_BF16, R, H, ldh, q, H, as, R, false, (hipStream_t)stream,
+                                       pair_of_row, top_k),
+                "quant_act_gather");
+  if (st != BFP8_OK) return st;
+  const bfp8::GemmArgs up_args{q, H, as, R, w_up, H, s_up, H / bfp8::kBlock, proj, 2 * I, (int)R, (int)(2 * I),
+                               (int)H, layout, E, nullptr, false};
+  st = launched(bfp8::launch_grouped_tiled(up_args, (hipStream_t)stream), "grouped_gemm_up");
+  if (st != BFP8_OK) return st;
+  st = launched(bfp8::launch_swiglu_quant(proj, R, I, 2 * I, layout, q2, I, as2, R, (hipStream_t)stream),
+                "swiglu_quant");
+  if (st != BFP8_OK) return st;
+  const bfp8::GemmArgs down_args{q2, I, as2, R, w_down, I, s_down, I / bfp8::kBlock, out, H, (int)R, (int)H,
+                                 (int)I, layout, E, nullptr, false};
+  st = launched(bfp8::launch_grouped_tiled(down_args, (hipStream_t)stream), "grouped_gemm_down");
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_moe_combine(out, H, row_of_pair, topk_weights, T, top_k, H, y, ldy,
+                                           (hipStream_t)stream),
+                  "moe_combine");
+}
+
 bfp8_status_t bfp8_set_schedule(int schedule) {
   if (schedule < BFP8_SCHED_AUTO || schedule >= BFP8_SCHED_COUNT_)
     return fail(BFP8_ERR_INVALID_ARGUMENT, "unknown schedule %d", schedule);

@@ -41,9 +41,23 @@ struct TiledPlan {
 };
 TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K);
 
-// Writes float32 scales to `as`, or with e8 their UE8M0 codes (one byte each).
+// Writes float32 scales to `as`, or with e8 their UE8M0 codes (one byte each). With src_rows,
+// output row m quantizes input row src_rows[m] / src_div and rows with a negative entry are
+// not written.
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                            int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream);
+                            int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream,
+                            const int32_t* src_rows = nullptr, int src_div = 1);
+
+// MoE chain (moe.hip). Dispatch: block_counts holds moe_dispatch_blocks(S) * E ints of scratch;
+// rows = length of layout and pair_of_row.
+int64_t moe_dispatch_blocks(int64_t S);
+hipError_t launch_moe_dispatch(const int32_t* ids, int64_t S, int E, int align, int64_t rows, int32_t* row_of_pair,
+                               int32_t* pair_of_row, int32_t* layout, int32_t* expert_start, int32_t* expert_count,
+                               int32_t* block_counts, hipStream_t stream);
+hipError_t launch_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout,
+                               uint8_t* q, int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair, const float* w, int64_t T,
+                              int top_k, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream);
 
 // Largest M the automatic choice gives to the K-split schedule (BFP8_SCHED_SMALL_M); the
 // tiled schedule takes larger M.

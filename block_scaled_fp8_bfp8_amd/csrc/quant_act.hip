@@ -31,11 +31,15 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kGroupsPerBlock = kQuantThreads / 16;
 
-template <bool kBf16, bool kE8>
+// Gather variant (kGather): output row m quantizes input row src_rows[m] / src_div, and rows
+// whose entry is negative are left unwritten (the MoE dispatch's padded buffer: entry = pair
+// index, src_div = top_k, so the input row is the pair's token).
+template <bool kBf16, bool kE8, bool kGather>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
                                                                   void* __restrict__ as, int64_t ld_as,
-                                                                  int groups_per_row, int64_t total_groups) {
+                                                                  int groups_per_row, int64_t total_groups,
+                                                                  const int32_t* __restrict__ src_rows, int src_div) {
   const int sub = threadIdx.x & 15;  // which 8-element slice of the group
   const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
   const bool valid = gid < total_groups;
@@ -45,10 +49,17 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   const int64_t m = g_lin / groups_per_row;
   const int g = (int)(g_lin - m * groups_per_row);
   const int64_t col = (int64_t)g * kBlock + sub * 8;
+  int64_t src = m;
+  bool store = valid;
+  if constexpr (kGather) {
+    const int32_t p = src_rows[m];  // the same for the group's 16 lanes
+    store = store && p >= 0;
+    src = p >= 0 ? p / src_div : 0;  // an unwritten row still reads a valid input row
+  }
 
   float v[8];
   if constexpr (kBf16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + m * ldx + col);
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -56,7 +67,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
-    const float* p = static_cast<const float*>(x) + m * ldx + col;
+    const float* p = static_cast<const float*>(x) + src * ldx + col;
     const float4 lo = *reinterpret_cast<const float4*>(p);
     const float4 hi = *reinterpret_cast<const float4*>(p + 4);
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
@@ -80,7 +91,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
 
-  if (valid) {
+  if (store) {
     *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(w0, w1);
     if (sub == 0) {
       if constexpr (kE8) {
@@ -98,24 +109,30 @@ namespace {
 
 template <bool kBf16, bool kE8>
 void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as, int groups_per_row,
-                      int64_t total, hipStream_t stream) {
+                      int64_t total, const int32_t* src_rows, int src_div, hipStream_t stream) {
   const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  hipLaunchKernelGGL((quant_act_kernel<kBf16, kE8>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream, x, ldx,
-                     q, ldq, as, ld_as, groups_per_row, total);
+  if (src_rows) {
+    hipLaunchKernelGGL((quant_act_kernel<kBf16, kE8, true>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div);
+  } else {
+    hipLaunchKernelGGL((quant_act_kernel<kBf16, kE8, false>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                            int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream) {
+                            int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream, const int32_t* src_rows,
+                            int src_div) {
   const int groups_per_row = (int)(K / kBlock);
   const int64_t total = M * groups_per_row;
   if (x_dtype == kInBf16) {
-    if (e8) launch_quant_cfg<true, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
-    else launch_quant_cfg<true, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
+    if (e8) launch_quant_cfg<true, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    else launch_quant_cfg<true, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
   } else {
-    if (e8) launch_quant_cfg<false, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
-    else launch_quant_cfg<false, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, stream);
+    if (e8) launch_quant_cfg<false, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    else launch_quant_cfg<false, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
   }
   return hipGetLastError();
 }

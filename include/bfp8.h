@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 3
+#define BFP8_ABI_VERSION 4
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -249,6 +249,79 @@ bfp8_status_t bfp8_grouped_gemm_contiguous_ue8m0(const uint8_t* a, int64_t lda, 
                                                  const int32_t* grouped_layout, int32_t G,
                                                  uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mixture-of-experts chain around the M-grouped GEMM (page "transformers/integrations/deepgemm.py":
+ * _dispatch_routed_input, _build_deepgemm_contiguous_layout, deepgemm_fp8_fp4_experts_forward,
+ * _combine_routed_output). S = T * top_k (token, expert) pairs; pair p = t * top_k + j.
+ *
+ * bfp8_moe_padded_rows: rows of the padded buffer, the page's upper bound S + min(S, E) * (align - 1)
+ * rounded up to a multiple of align (known on the host, no device-to-host sync).
+ *
+ * bfp8_moe_dispatch: for topk_ids [S] (int32; ids outside [0, E) are sentinels: placed nowhere)
+ * writes, on stream:
+ *   row_of_pair [S]     the pair's row in the padded buffer (-1 for a sentinel),
+ *   pair_of_row [rows]  the pair in each row (-1 on padding),
+ *   layout [rows]       each row's expert id, -1 on padding (the grouped GEMM's layout),
+ *   expert_start [E+1]  expert e owns rows [expert_start[e], expert_start[e] + count_e), blocks
+ *                       aligned to align and in expert order; expert_start[E] = rows in use.
+ * Inside an expert the pairs keep their index order (deterministic). 1 <= E <= 1024,
+ * 1 <= align <= 4096. workspace: bfp8_moe_dispatch_workspace_bytes(S, E) bytes, 4-byte aligned
+ * (scratch, overwritten).
+ */
+int64_t bfp8_moe_padded_rows(int64_t S, int32_t E, int32_t align);
+size_t bfp8_moe_dispatch_workspace_bytes(int64_t S, int32_t E);
+bfp8_status_t bfp8_moe_dispatch(const int32_t* topk_ids, int64_t S, int32_t E, int32_t align,
+                                int32_t* row_of_pair, int32_t* pair_of_row, int32_t* layout,
+                                int32_t* expert_start, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bfp8_quant_act_gather: bfp8_quant_act of a gathered matrix: output row m (of M) quantizes input
+ * row row_src[m] / src_div of x [src_rows][ldx]; rows with row_src[m] < 0 are not written (with
+ * the dispatch: row_src = pair_of_row, src_div = top_k, so row m holds its pair's token).
+ * Entries must be -1 or below src_rows * src_div (device data, not checked).
+ */
+bfp8_status_t bfp8_quant_act_gather(const void* x, int x_dtype, int64_t src_rows, int64_t K, int64_t ldx,
+                                    const int32_t* row_src, int32_t src_div, int64_t M, uint8_t* q,
+                                    int64_t ldq, float* as, int64_t ld_as, void* stream);
+
+/*
+ * bfp8_swiglu_quant: the gate activation fused with the second quantization. Row m of
+ * proj [M][ldp] (bf16; gate in columns [0, I), up in [I, 2I)) gives
+ *   h = bf16( bf16(silu(gate)) * up ),  silu(x) = x / (1 + exp(-x)) rounded once to bf16,
+ * quantized per 1x128 group exactly as bfp8_quant_act does into q [M][ldq] and
+ * as[(i/128) * ld_as + m]. Rows whose layout entry is -1 are skipped (layout may be NULL).
+ * I a multiple of 128; proj and q rows 16-byte aligned.
+ */
+bfp8_status_t bfp8_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout,
+                                uint8_t* q, int64_t ldq, float* as, int64_t ld_as, void* stream);
+
+/*
+ * bfp8_moe_combine: y[t, :] = bf16( sum_j bf16(out[row_of_pair[p], :] * bf16(topk_weights[p])) ),
+ * p = t * top_k + j, the sum in float32 in order j; pairs with row -1 add nothing (their rows
+ * are never read). out [rows][ldo], y [T][ldy] bf16 with 16-byte aligned rows; H % 8 == 0.
+ */
+bfp8_status_t bfp8_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair,
+                               const float* topk_weights, int64_t T, int32_t top_k, int64_t H, uint16_t* y,
+                               int64_t ldy, void* stream);
+
+/*
+ * bfp8_moe_forward: the FP8 experts forward of the page, end to end on stream: dispatch (align
+ * 128), gathered quantization of hidden [T][ldh] (bf16), grouped GEMM with
+ *   w_up [E][2I][H] e4m3, s_up [E][2I/128][H/128] float32 (row stride H, H/128),
+ * SwiGLU + quantization, grouped GEMM with
+ *   w_down [E][H][I] e4m3, s_down [E][H/128][I/128] float32 (row stride I, I/128),
+ * and the weighted top-k combine into y [T][ldy] bf16. topk_ids / topk_weights are [T][top_k]
+ * (int32 / float32). H and I are multiples of 128, 1 <= E <= 1024. workspace:
+ * bfp8_moe_forward_workspace_bytes(T, top_k, E, H, I) bytes, 256-byte aligned; it holds the
+ * layout and every intermediate (overwritten). Errors and validation as for the calls above;
+ * nothing is launched unless every step's arguments are valid.
+ */
+size_t bfp8_moe_forward_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int64_t H, int64_t I);
+bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int64_t ldh, const int32_t* topk_ids,
+                               const float* topk_weights, int32_t top_k, int32_t E, const uint8_t* w_up,
+                               const float* s_up, const uint8_t* w_down, const float* s_down, int64_t I,
+                               uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Process-wide schedule override for bfp8_gemm (tests and benchmarks):
  * BFP8_SCHED_AUTO restores the automatic choice. Returns BFP8_ERR_INVALID_ARGUMENT

@@ -20,6 +20,9 @@ Workloads (all sizes N x K are weight shapes, A is [M, K]):
     deepgemm.py" checkpoints with float8_e8m0fnu scale factors): the e4m3 codes of
     ``weight``, with scale codes drawn uniformly from [113, 121], i.e. scales 2**-14 ..
     2**-6, the binades that U(0, 1e-2) mostly covers.
+  * MoE routing for the expert chain: per token, top_k distinct experts drawn with
+    Dirichlet(1) expert probabilities (numpy), router weights U(0, 1) normalized per token;
+    expert weights: gate+up [E, 2I, H] and down [E, H, I] like ``weight``.
   * M-grouped contiguous MoE: 16 experts with weights [4096, 7168]; token counts
     ~ Multinomial(4096, Dirichlet(1)) (seed 4); each expert's rows padded up to a
     multiple of 128; a per-row int32 expert id, -1 on padding rows; bf16 N(0, 1)
@@ -155,3 +158,24 @@ def moe_case(groups: int = MOE_GROUPS, n: int = MOE_N, k: int = MOE_K, tokens: i
     act[torch.from_numpy(layout < 0)] = 0
     weights = [weight(n, k, seed=seed * 100 + g) for g in range(groups)] if with_weights else []
     return MoeCase(counts, torch.from_numpy(layout), act, weights)
+
+
+def moe_routing(tokens: int, top_k: int, experts: int, seed: int, sentinel_frac: float = 0.0):
+    """(topk_ids [T, top_k] int32, topk_weights [T, top_k] float32); with sentinel_frac > 0, that
+    share of the pairs is replaced by the id `experts` (an expert-parallel sentinel)."""
+    rng = np.random.default_rng(seed)
+    p = rng.dirichlet(np.ones(experts))
+    ids = np.stack([rng.choice(experts, top_k, replace=False, p=p) for _ in range(tokens)]).astype(np.int32)
+    if sentinel_frac > 0:
+        ids[rng.random(ids.shape) < sentinel_frac] = experts
+    w = rng.uniform(0.0, 1.0, (tokens, top_k))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return torch.from_numpy(ids), torch.from_numpy(w)
+
+
+def moe_experts(experts: int, hidden: int, inter: int, seed: int):
+    """(w_up [E, 2I, H], s_up, w_down [E, H, I], s_down): e4m3 codes and float32 128x128 scales."""
+    up = [weight(2 * inter, hidden, seed=seed + 2 * g) for g in range(experts)]
+    down = [weight(hidden, inter, seed=seed + 2 * g + 1) for g in range(experts)]
+    return (torch.stack([w.q for w in up]), torch.stack([w.s for w in up]),
+            torch.stack([w.q for w in down]), torch.stack([w.s for w in down]))
