@@ -372,6 +372,50 @@ def main() -> int:
         del bq_g, bs_g
         torch.cuda.empty_cache()
 
+        # MoE expert chain: 512 tokens, top-8 of 16 experts (4096 pairs, like the grouped
+        # configuration), hidden 7168, intermediate 2048 (gate+up weights [16, 4096, 7168]).
+        t_c, k_c, e_c, h_c, i_c = 512, 8, 16, 7168, 2048
+        ids_c, w_c = workloads.moe_routing(t_c, k_c, e_c, seed=31)
+        wts_c = [a.to(dev) for a in workloads.moe_experts(e_c, h_c, i_c, seed=32)]
+        x_c = workloads.act_normal_bf16(t_c, h_c, seed=33).to(dev)
+        ids_d, w_d = ids_c.to(dev), w_c.to(dev)
+        y_c = torch.empty((t_c, h_c), dtype=torch.bfloat16, device=dev)
+        ws_c = torch.empty(bfp8.moe_forward_workspace_bytes(t_c, k_c, e_c, h_c, i_c), dtype=torch.uint8, device=dev)
+
+        def chain_calls(n):
+            for _ in range(n):
+                bfp8.moe_forward(x_c, ids_d, w_d, *wts_c, out=y_c, workspace=ws_c)
+
+        us = graph_time_us(chain_calls, 3)
+        # the steps one by one, for the breakdown
+        rop, por, lay, _ = bfp8.moe_dispatch(ids_d, e_c)
+        q_c, s_c = bfp8.quant_act_gather(x_c, por, k_c)
+        proj_c = bfp8.grouped_gemm_contiguous(q_c, s_c, wts_c[0], wts_c[1], lay)
+        q2_c, s2_c = bfp8.swiglu_quant(proj_c, lay)
+        out_c = bfp8.grouped_gemm_contiguous(q2_c, s2_c, wts_c[2], wts_c[3], lay)
+        steps = {
+            "dispatch": graph_time_us(lambda n: [bfp8.moe_dispatch(ids_d, e_c) for _ in range(n)], 8),
+            "quant_gather": graph_time_us(lambda n: [bfp8.quant_act_gather(x_c, por, k_c) for _ in range(n)], 8),
+            "grouped_up": graph_time_us(lambda n: [bfp8.grouped_gemm_contiguous(q_c, s_c, wts_c[0], wts_c[1], lay,
+                                                                                out=proj_c) for _ in range(n)], 3),
+            "swiglu_quant": graph_time_us(lambda n: [bfp8.swiglu_quant(proj_c, lay) for _ in range(n)], 8),
+            "grouped_down": graph_time_us(lambda n: [bfp8.grouped_gemm_contiguous(q2_c, s2_c, wts_c[2], wts_c[3], lay,
+                                                                                  out=out_c) for _ in range(n)], 3),
+            "combine": graph_time_us(lambda n: [bfp8.moe_combine(out_c, rop, w_d) for _ in range(n)], 8),
+        }
+        pairs = int(((ids_c >= 0) & (ids_c < e_c)).sum())
+        flops = 2.0 * pairs * (2 * i_c * h_c + h_c * i_c)
+        wbytes = e_c * (2 * i_c * h_c + h_c * i_c) + 4 * e_c * ((2 * i_c // 128) * (h_c // 128) + (h_c // 128) * (i_c // 128))
+        alg = wbytes + 2 * t_c * h_c * 2 + 8 * t_c * k_c
+        configs["moe_chain"] = {"tokens": t_c, "top_k": k_c, "experts": e_c, "hidden": h_c, "intermediate": i_c,
+                                "flops": "2 * pairs * (2I*H + H*I)", **roofline_entry(us, flops, alg),
+                                "steps_us": {k_: round(v_, 2) for k_, v_ in steps.items()}}
+        log(f"MoE chain T={t_c} top{k_c} of E={e_c} H={h_c} I={i_c}: {us:8.2f} us  "
+            f"{configs['moe_chain']['tflops']:8.1f} TFLOP/s  {configs['moe_chain']['bound']} "
+            f"frac {configs['moe_chain']['frac']:.3f}  steps " + ", ".join(f"{k_} {v_:.1f}" for k_, v_ in steps.items()))
+        del wts_c, ws_c, proj_c, out_c, q_c, q2_c
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline and not args.only_m:
         log("cpu baseline (oracle) ...")

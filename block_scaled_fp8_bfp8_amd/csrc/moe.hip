@@ -16,7 +16,9 @@
 //     row are read once, h = bf16(bf16(silu(gate)) * up) stays in registers, and each 1x128
 //     group of h is quantized exactly as the activation quantizer does. silu is evaluated in
 //     float64 and rounded once to bf16 (through float with round-to-odd, which cannot double
-//     round), so the bf16 value, and every FP8 code derived from it, is the exact one;
+//     round), so the bf16 value, and every FP8 code derived from it, is the exact one (a float32
+//     evaluation decides all but the elements near a bf16 rounding midpoint); padding rows are
+//     skipped;
 //   * combine: per token and 8 output columns, sum_j bf16(out[row] * bf16(w)) in float32 in the
 //     order of the token's pairs, rounded once to bf16; sentinel pairs add nothing and their
 //     rows are never read.
@@ -146,6 +148,29 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
 
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
+// bf16(silu(x)) for a bf16 input x, equal to rounding the exact silu once. Fast path in float32:
+// s = x / (1 + exp(-x)) is within a few float32 ulps of silu(x) (exp within 2 ulps, one rounding
+// for the sum and one for the IEEE divide), so its bf16 rounding is the exact one unless s lies
+// within 16 float32 ulps of a bf16 rounding midpoint (low 16 bits near 0x8000), or is tiny, where
+// float32 loses relative accuracy; those few elements are evaluated again in float64.
+__device__ __forceinline__ uint32_t silu_bf16(float x) {
+  const float s = x / (1.0f + expf(-x));
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t low = u & 0xffffu;
+  const bool clear = (low < 0x8000u - 16u || low > 0x8000u + 16u) && fabsf(s) >= 0x1p-100f && fabsf(s) < 0x1p100f;
+  if (clear) return f32_to_bf16_rne(s);
+  const double xd = (double)x;
+  return f64_to_bf16_rne(xd / (1.0 + exp(-xd)));
+}
+
+// bf16(a * b) for bf16 values a, b: the product has at most 16 significant bits, so float32 holds
+// it exactly unless it falls below the normal range; those are formed in float64.
+__device__ __forceinline__ uint32_t mul_bf16(float a, float b) {
+  const float pr = a * b;
+  if (fabsf(pr) >= 0x1p-126f || pr == 0.0f && (a == 0.0f || b == 0.0f)) return f32_to_bf16_rne(pr);
+  return f64_to_bf16_rne((double)a * (double)b);
+}
+
 constexpr int kSwigluThreads = 256;
 constexpr int kSwigluGroupsPerBlock = kSwigluThreads / 16;
 
@@ -162,7 +187,9 @@ __global__ __launch_bounds__(kSwigluThreads) void swiglu_quant_kernel(const uint
   const int64_t g_lin = valid ? gid : total_groups - 1;
   const int64_t m = g_lin / groups_per_row;
   const int g = (int)(g_lin - m * groups_per_row);
-  if (layout != nullptr && layout[m] < 0) valid = false;  // padding row: computed on row data, not stored
+  // A padding row is not computed at all; its 16-lane groups exchange values only among
+  // themselves, so the other groups of the wave are unaffected.
+  if (layout != nullptr && layout[m] < 0) return;
   const int64_t col = (int64_t)g * kBlock + sub * 8;
   const uint4 graw = *reinterpret_cast<const uint4*>(proj + m * ldp + col);
   const uint4 uraw = *reinterpret_cast<const uint4*>(proj + m * ldp + I + col);
@@ -173,9 +200,8 @@ __global__ __launch_bounds__(kSwigluThreads) void swiglu_quant_kernel(const uint
   for (int i = 0; i < 8; ++i) {
     const uint32_t gb = (gw[i / 2] >> (16 * (i & 1))) & 0xffffu;
     const uint32_t ub = (uw[i / 2] >> (16 * (i & 1))) & 0xffffu;
-    const double x = (double)bf16_value(gb);
-    const float sb = bf16_value(f64_to_bf16_rne(x / (1.0 + exp(-x))));
-    h[i] = bf16_value(f64_to_bf16_rne((double)sb * (double)bf16_value(ub)));
+    const float sb = bf16_value(silu_bf16(bf16_value(gb)));
+    h[i] = bf16_value(mul_bf16(sb, bf16_value(ub)));
   }
   float amax = 0.f;
 #pragma unroll
@@ -211,13 +237,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
     const int64_t p = t * top_k + j;
     const int r = row_of_pair[p];
     if (r < 0) continue;
-    const double wb = (double)bf16_value(f32_to_bf16_rne(w[p]));
+    const float wb = bf16_value(f32_to_bf16_rne(w[p]));
     const uint4 raw = *reinterpret_cast<const uint4*>(out + (int64_t)r * ldo + c);
     const uint32_t ow[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double o = (double)bf16_value((ow[e / 2] >> (16 * (e & 1))) & 0xffffu);
-      acc[e] += bf16_value(f64_to_bf16_rne(o * wb));
+      const float o = bf16_value((ow[e / 2] >> (16 * (e & 1))) & 0xffffu);
+      acc[e] += bf16_value(mul_bf16(o, wb));
     }
   }
   uint4 res;

@@ -53,8 +53,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   bool store = valid;
   if constexpr (kGather) {
     const int32_t p = src_rows[m];  // the same for the group's 16 lanes
-    store = store && p >= 0;
-    src = p >= 0 ? p / src_div : 0;  // an unwritten row still reads a valid input row
+    // An unwritten row is not computed: the group's lanes exchange values only among
+    // themselves, so leaving it early does not affect the other groups of the wave.
+    if (p < 0) return;
+    src = p / src_div;
   }
 
   float v[8];
