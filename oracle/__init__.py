@@ -22,6 +22,8 @@ What is computed, and where it is defined on the pages:
 * M-grouped contiguous GEMM (``gemm.grouped_gemm_contiguous_ref``): page
   "transformers/integrations/deepgemm.py", ``_build_deepgemm_contiguous_layout``
   (per-row expert id, -1 on padding rows) and ``deepgemm_fp8_fp4_experts_forward``.
+* fp16 rounding (``f16``): the fp16 output of the linear layer for fp16 activations (same page
+  as below: the output dtype follows the input).
 * FP8 linear layer (``linear.linear_ref``): page "transformers/integrations/deepgemm.py",
   ``deepgemm_fp8_fp4_linear`` (quantize, GEMM into a bf16 output, then add the bias to it).
 * MoE chain (``moe``): same page, ``_dispatch_routed_input``, ``_build_deepgemm_contiguous_layout``,
@@ -37,6 +39,6 @@ routines, brute force with exact rationals, closed forms and invariants); none
 is "parity unpinned".
 """
 
-from . import bf16, e4m3, gemm, linear, moe, quant, ue8m0  # noqa: F401
+from . import bf16, e4m3, f16, gemm, linear, moe, quant, ue8m0  # noqa: F401
 
-__all__ = ["bf16", "e4m3", "gemm", "linear", "moe", "quant", "ue8m0"]
+__all__ = ["bf16", "e4m3", "f16", "gemm", "linear", "moe", "quant", "ue8m0"]

@@ -11,14 +11,15 @@ to bf16.
     out = bf16( float32( bf16(C) ) + float32(bias) )
 
 The quantization and C are the pinned functions of ``quant`` and ``gemm``; only the bias
-step is new here.
+step is new here. For fp16 activations the layer's output, and C, are fp16 instead
+(``linear_f16_ref``).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, gemm, quant
+from . import bf16, f16, gemm, quant
 
 
 def bias_add_bf16(c_bits, bias) -> np.ndarray:
@@ -29,6 +30,29 @@ def bias_add_bf16(c_bits, bias) -> np.ndarray:
     with np.errstate(over="ignore", invalid="ignore"):
         total = c + b[None, :]  # float32 addition, one rounding
     return bf16.to_bits(total.astype(np.float64))  # exact widening, then one bf16 rounding
+
+
+def bias_add_f16(c_bits, bias) -> np.ndarray:
+    """fp16 bits of fp16(float32(c) + float32(bias[n])): the same step for an fp16 layer."""
+    c = f16.from_bits(c_bits).astype(np.float32)
+    b = np.asarray(bias, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        total = c + b[None, :]
+    return f16.to_bits(total.astype(np.float64))
+
+
+def linear_f16_ref(x, w_q, w_s, bias=None, rows=None, cols=None):
+    """linear_ref for fp16 activations: the output, and the GEMM result before the bias, are fp16
+    (the page's output dtype follows the input)."""
+    q, s = quant.quant_act_ref(np.asarray(x, dtype=np.float32))
+    acc, _ = gemm.gemm_acc_ref(q, s, w_q, w_s, rows, cols)
+    c_bits = f16.to_bits(acc)
+    if bias is None:
+        return c_bits, c_bits, q, s
+    b = np.asarray(bias, dtype=np.float32)
+    if cols is not None:
+        b = b[np.asarray(cols)]
+    return bias_add_f16(c_bits, b), c_bits, q, s
 
 
 def linear_ref(x, w_q, w_s, bias=None, rows=None, cols=None):

@@ -69,3 +69,29 @@ def test_linear_bias_is_added_after_bf16_rounding():
     row0 = bf16.from_bits(c[0]).astype(np.float32)
     out, _, _, _ = linear.linear_ref(x[:1], w_q, w_s, bias=-row0)
     assert (bf16.from_bits(out) == 0).all()
+
+
+def test_f16_rounding_against_numpy_and_exact_rationals():
+    """fp16 RNE from float64 against numpy's own float64 -> float16 cast (correctly rounded) on
+    values spread over every binade incl. subnormals and overflow, and exact rationals on ties."""
+    from oracle import f16
+
+    rng = np.random.default_rng(41)
+    v = rng.uniform(-1, 1, 400000) * np.exp2(rng.integers(-30, 18, 400000))
+    np.testing.assert_array_equal(f16.to_bits(v), v.astype(np.float16).view(np.uint16))
+    # ties: halfway between two fp16 neighbours rounds to the even one
+    for a in (1.0, 1.0 + 2.0**-10, 2.0**-14, 3 * 2.0**-24):
+        mid = Fraction(a) + Fraction(float(f16.ulp(a))) / 2
+        got = Fraction(float(f16.round_to_f16(float(mid))))
+        lo, hi = Fraction(a), Fraction(a) + Fraction(float(f16.ulp(a)))
+        want = lo if (int(np.float16(a).view(np.uint16)) & 1) == 0 else hi
+        assert got == want, a
+    assert np.isinf(f16.round_to_f16(65520.0)) and f16.round_to_f16(65519.0) == 65504.0
+
+
+def test_f16_bias_add_equals_torch_f16_add():
+    rng = np.random.default_rng(42)
+    c = torch.from_numpy(rng.standard_normal((32, 64)) * 100).to(torch.float16)
+    b = torch.from_numpy(rng.standard_normal(64) * 3).to(torch.float16)
+    got = linear.bias_add_f16(c.view(torch.int16).numpy().view(np.uint16), b.float().numpy())
+    np.testing.assert_array_equal(got, (c + b).view(torch.int16).numpy().view(np.uint16))
