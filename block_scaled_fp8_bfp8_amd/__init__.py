@@ -23,7 +23,7 @@ from . import _native
 from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
-    "quant_act", "gemm", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
+    "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
     "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
     "moe_forward_workspace_bytes", "set_schedule", "get_schedule", "schedule_for",
@@ -93,6 +93,16 @@ def _workspace(device: torch.device, nbytes: int) -> tuple[int, int]:
     return buf.data_ptr(), buf.numel()
 
 
+_IN_DTYPES = {torch.float32: _native.BFP8_IN_F32, torch.bfloat16: _native.BFP8_IN_BF16,
+              torch.float16: _native.BFP8_IN_F16}
+
+
+def _in_dtype(x: torch.Tensor, what: str) -> int:
+    if x.dtype not in _IN_DTYPES:
+        raise NotImplementedError(f"{what} takes float32, bfloat16 or float16 input, got {x.dtype}")
+    return _IN_DTYPES[x.dtype]
+
+
 def abi_version() -> int:
     return _native.lib().bfp8_abi_version()
 
@@ -103,8 +113,7 @@ def quant_act(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tens
     Returns (q, s): q uint8 e4m3fn codes [M, K]; s float32 [M, K/128], stored group-major
     (s.stride() == (1, M)), i.e. the "column-major" activation scales the GEMM reads.
     """
-    if x.dtype not in (torch.float32, torch.bfloat16):
-        raise NotImplementedError(f"quant_act takes float32 or bfloat16 input, got {x.dtype}")
+    dt = _in_dtype(x, "quant_act")
     _require(x, "x", x.dtype, 2)
     if x.stride(1) != 1:
         raise ValueError("x must be K-contiguous")
@@ -118,7 +127,6 @@ def quant_act(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tens
     _require(scales, "scales", torch.float32, 2)
     if q.stride(1) != 1 or scales.stride(0) != 1:
         raise ValueError("q must be K-contiguous and scales group-major (stride(0) == 1)")
-    dt = _native.BFP8_IN_F32 if x.dtype == torch.float32 else _native.BFP8_IN_BF16
     st = _native.lib().bfp8_quant_act(x.data_ptr(), dt, m, k, x.stride(0), q.data_ptr(), q.stride(0),
                                       scales.data_ptr(), scales.stride(1) if scales.dim() == 2 else m,
                                       _stream(x.device))
@@ -137,9 +145,18 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Ten
     """C[M, N] (bf16) = blockwise FP8 product of a_q [M, K] and b_q [N, K] with scales a_s [M, K/128]
     (group-major) and b_s [ceil(N/128), K/128].
 
-    workspace: optional caller-owned uint8 buffer on the same device (zero-filled before its
-    first use, at least bfp8_gemm_workspace_bytes(M, N, K) bytes); by default one buffer per
-    (device, stream) is kept here."""
+    workspace: optional caller-owned uint8 buffer on the same device (at least
+    bfp8_gemm_workspace_bytes(M, N, K) bytes); by default one buffer per (device, stream) is kept."""
+    return _gemm(a_q, a_s, b_q, b_s, out, workspace, torch.bfloat16)
+
+
+def gemm_f16(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm with an fp16 output."""
+    return _gemm(a_q, a_s, b_q, b_s, out, workspace, torch.float16)
+
+
+def _gemm(a_q, a_s, b_q, b_s, out, workspace, out_dtype):
     a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
     _require(a_q, "a_q", torch.uint8, 2)
     _require(b_q, "b_q", torch.uint8, 2)
@@ -154,8 +171,8 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Ten
     if tuple(a_s.shape) != (m, -(-k // 128)) or tuple(b_s.shape) != (-(-n // 128), -(-k // 128)):
         raise ValueError(f"scale shapes {tuple(a_s.shape)}, {tuple(b_s.shape)} do not match M={m}, N={n}, K={k}")
     if out is None:
-        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
-    _require(out, "out", torch.bfloat16, 2)
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    _require(out, "out", out_dtype, 2)
     if out.stride(1) != 1:
         raise ValueError("out must be contiguous along N")
     lib = _native.lib()
@@ -164,10 +181,11 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Ten
     else:
         _require(workspace, "workspace", torch.uint8, 1)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    st = lib.bfp8_gemm(a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m),
-                       b_q.data_ptr(), b_q.stride(0), b_s.data_ptr(), b_s.stride(0),
-                       out.data_ptr(), out.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream(a_q.device))
-    _check(st, "bfp8_gemm")
+    entry, name = (lib.bfp8_gemm, "bfp8_gemm") if out_dtype == torch.bfloat16 else (lib.bfp8_gemm_f16, "bfp8_gemm_f16")
+    st = entry(a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m),
+               b_q.data_ptr(), b_q.stride(0), b_s.data_ptr(), b_s.stride(0),
+               out.data_ptr(), out.stride(0), m, n, k, ws_ptr or None, ws_bytes, _stream(a_q.device))
+    _check(st, name)
     return out
 
 
@@ -203,14 +221,16 @@ def grouped_gemm_contiguous(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Ten
 
 def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Tensor | None = None,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """FP8 linear layer, bf16 in and out: per-1x128-group quantization of x [M, K] (bf16), the
-    blockwise FP8 product with w_q [N, K] / w_s [ceil(N/128), K/128], then bf16(out + bias).
+    """FP8 linear layer, bf16 (or fp16) in and out: per-1x128-group quantization of x [M, K], the
+    blockwise FP8 product with w_q [N, K] / w_s [ceil(N/128), K/128], then out + bias, the output
+    and bias having x's dtype.
 
     workspace: optional uint8 buffer of at least bfp8_linear_workspace_bytes(M, N, K) bytes
     (holds the quantized activations); by default one buffer per (device, stream) is kept."""
-    if x.dtype != torch.bfloat16:
-        raise NotImplementedError(f"linear takes bfloat16 activations (bf16 output), got {x.dtype}")
-    _require(x, "x", torch.bfloat16, 2)
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise NotImplementedError(f"linear takes bfloat16 or float16 activations (the output has their dtype), "
+                                  f"got {x.dtype}")
+    _require(x, "x", x.dtype, 2)
     w_q = _as_u8(w_q, "w_q")
     _require(w_q, "w_q", torch.uint8, 2)
     _require(w_s, "w_s", torch.float32, 2)
@@ -223,12 +243,12 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Te
     if tuple(w_s.shape) != (-(-n // 128), -(-k // 128)):
         raise ValueError(f"w_s shape {tuple(w_s.shape)} does not match N={n}, K={k}")
     if bias is not None:
-        _require(bias, "bias", torch.bfloat16, 1)
+        _require(bias, "bias", x.dtype, 1)
         if bias.shape[0] != n or bias.stride(0) != 1:
             raise ValueError("bias must be a contiguous bf16 vector of length N")
     if out is None:
-        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    _require(out, "out", torch.bfloat16, 2)
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    _require(out, "out", x.dtype, 2)
     if out.stride(1) != 1:
         raise ValueError("out must be contiguous along N")
     lib = _native.lib()
@@ -237,7 +257,7 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Te
     else:
         _require(workspace, "workspace", torch.uint8, 1)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    st = lib.bfp8_linear(x.data_ptr(), _native.BFP8_IN_BF16, m, k, x.stride(0), w_q.data_ptr(), w_q.stride(0),
+    st = lib.bfp8_linear(x.data_ptr(), _IN_DTYPES[x.dtype], m, k, x.stride(0), w_q.data_ptr(), w_q.stride(0),
                          w_s.data_ptr(), w_s.stride(0), bias.data_ptr() if bias is not None else None,
                          out.data_ptr(), out.stride(0), n, ws_ptr or None, ws_bytes, _stream(x.device))
     _check(st, "bfp8_linear")
@@ -276,8 +296,7 @@ def ue8m0_scales(codes: torch.Tensor) -> torch.Tensor:
 def quant_act_ue8m0(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """quant_act with power-of-two scales: returns (q, e) with e the UE8M0 codes [M, K/128]
     (uint8), stored group-major with a row of codes padded to a multiple of 4 bytes."""
-    if x.dtype not in (torch.float32, torch.bfloat16):
-        raise NotImplementedError(f"quant_act_ue8m0 takes float32 or bfloat16 input, got {x.dtype}")
+    dt = _in_dtype(x, "quant_act_ue8m0")
     _require(x, "x", x.dtype, 2)
     if x.stride(1) != 1:
         raise ValueError("x must be K-contiguous")
@@ -292,7 +311,6 @@ def quant_act_ue8m0(x: torch.Tensor, q: torch.Tensor | None = None, scales: torc
     _require(scales, "scales", torch.uint8, 2)
     if q.stride(1) != 1 or (scales.stride(0) != 1 and m > 1):
         raise ValueError("q must be K-contiguous and scales group-major (stride(0) == 1)")
-    dt = _native.BFP8_IN_F32 if x.dtype == torch.float32 else _native.BFP8_IN_BF16
     st = _native.lib().bfp8_quant_act_ue8m0(x.data_ptr(), dt, m, k, x.stride(0), q.data_ptr(), q.stride(0),
                                             scales.data_ptr(), scales.stride(1), _stream(x.device))
     _check(st, "bfp8_quant_act_ue8m0")
@@ -411,8 +429,7 @@ def moe_dispatch(topk_ids: torch.Tensor, num_experts: int, align: int = 128):
 def quant_act_gather(x: torch.Tensor, row_src: torch.Tensor, src_div: int = 1):
     """quant_act of the gathered rows: output row m quantizes x[row_src[m] // src_div]; rows with
     row_src[m] < 0 are left unwritten. Returns (q [M, K], s [M, K/128] group-major)."""
-    if x.dtype not in (torch.float32, torch.bfloat16):
-        raise NotImplementedError(f"quant_act_gather takes float32 or bfloat16 input, got {x.dtype}")
+    dt = _in_dtype(x, "quant_act_gather")
     _require(x, "x", x.dtype, 2)
     _require(row_src, "row_src", torch.int32, 1)
     if x.stride(1) != 1 or not row_src.is_contiguous():
@@ -420,7 +437,6 @@ def quant_act_gather(x: torch.Tensor, row_src: torch.Tensor, src_div: int = 1):
     m, k = row_src.numel(), x.shape[1]
     q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
     s = torch.empty((k // 128, m), dtype=torch.float32, device=x.device).t()
-    dt = _native.BFP8_IN_F32 if x.dtype == torch.float32 else _native.BFP8_IN_BF16
     st = _native.lib().bfp8_quant_act_gather(x.data_ptr(), dt, x.shape[0], k, x.stride(0), row_src.data_ptr(),
                                              src_div, m, q.data_ptr(), q.stride(0), s.data_ptr(), max(m, 1),
                                              _stream(x.device))

@@ -18,6 +18,7 @@ BFP8_ERR_LAUNCH = 6
 
 BFP8_IN_F32 = 0
 BFP8_IN_BF16 = 1
+BFP8_IN_F16 = 2
 
 SCHEDULES = {"auto": 0, "small_m": 1, "tiled": 2}
 
@@ -32,6 +33,8 @@ SIGNATURES = [
     ("bfp8_gemm", ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_grouped_gemm_contiguous", ctypes.c_int,
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_gemm_f16", ctypes.c_int,
+     [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_quant_act_ue8m0", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
     ("bfp8_gemm_ue8m0", ctypes.c_int,
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),

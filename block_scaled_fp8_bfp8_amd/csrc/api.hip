@@ -112,8 +112,8 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const void* as, int
 // Arguments of the activation quantizer (no device access).
 bfp8_status_t check_quant_args(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* q,
                                int64_t ldq, const void* as, int64_t ld_as, bool e8 = false) {
-  if (x_dtype != BFP8_IN_F32 && x_dtype != BFP8_IN_BF16)
-    return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is neither BFP8_IN_F32 nor BFP8_IN_BF16", x_dtype);
+  if (x_dtype != BFP8_IN_F32 && x_dtype != BFP8_IN_BF16 && x_dtype != BFP8_IN_F16)
+    return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is not BFP8_IN_F32, BFP8_IN_BF16 or BFP8_IN_F16", x_dtype);
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
   if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
   if (K % bfp8::kBlock != 0)
@@ -200,9 +200,9 @@ namespace {
 bfp8_status_t launch_dense(const uint8_t* a, int64_t lda, const void* as, int64_t ld_as, const uint8_t* b,
                            int64_t ldb, const void* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
                            int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace, void* stream,
-                           bool e8 = false) {
+                           bool e8 = false, bool out_f16 = false) {
   const bfp8::GemmArgs args{a,      lda,    as,     ld_as,   b, ldb, bs, ld_bs, c,
-                            ldc,    (int)M, (int)N, (int)K,  nullptr, 1, bias, e8};
+                            ldc,    (int)M, (int)N, (int)K,  nullptr, 1, bias, e8, out_f16};
   const int sched = choose_schedule(M, N, K);
   if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_ksplit(args, (hipStream_t)stream), "gemm_ksplit");
   return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
@@ -231,6 +231,18 @@ bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t 
   st = check_device();
   if (st != BFP8_OK) return st;
   return launch_dense(a, lda, as, ld_as, b, ldb, bs, ld_bs, nullptr, c, ldc, M, N, K, workspace, stream);
+}
+
+bfp8_status_t bfp8_gemm_f16(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
+                            int64_t ldb, const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
+                            int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
+                                     workspace_bytes, false);
+  if (st != BFP8_OK) return st;
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launch_dense(a, lda, as, ld_as, b, ldb, bs, ld_bs, nullptr, c, ldc, M, N, K, workspace, stream, false, true);
 }
 
 bfp8_status_t bfp8_gemm_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as, const uint8_t* b,
@@ -302,9 +314,9 @@ size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
                           int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
                           int64_t ldc, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
-  if (x_dtype != BFP8_IN_BF16)
-    return fail(BFP8_ERR_UNSUPPORTED, "the linear layer takes bf16 activations (its output is bf16), got x_dtype %d",
-                x_dtype);
+  if (x_dtype != BFP8_IN_BF16 && x_dtype != BFP8_IN_F16)
+    return fail(BFP8_ERR_UNSUPPORTED,
+                "the linear layer takes bf16 or fp16 activations (its output has their dtype), got x_dtype %d", x_dtype);
   if (!aligned(bias, 2)) return fail(BFP8_ERR_MISALIGNED, "bias must be 2-byte aligned");
   if (workspace && !aligned(workspace, 256)) return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   // Shapes first (a negative or oversized size must not reach the workspace arithmetic).
@@ -333,7 +345,8 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
   if (st != BFP8_OK) return st;
   st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, K, as, M, false, (hipStream_t)stream), "quant_act");
   if (st != BFP8_OK) return st;
-  return launch_dense(q, K, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream);
+  return launch_dense(q, K, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream, false,
+                      x_dtype == BFP8_IN_F16);
 }
 
 // ---- MoE chain ------------------------------------------------------------------------------

@@ -62,10 +62,30 @@ __device__ __forceinline__ uint32_t bf16_out(float acc, const uint16_t* bias, in
 
 // Store 4 consecutive bf16 outputs c[0..3] of one row (columns n .. n+3), with column tail
 // masking and an optional bias.
-__device__ __forceinline__ void store_bf16x4(uint16_t* c, int n, int N, bool vec_ok, float v0, float v1,
-                                             float v2, float v3, const uint16_t* bias) {
-  const uint32_t b0 = bf16_out(v0, bias, min(n, N - 1)), b1 = bf16_out(v1, bias, min(n + 1, N - 1));
-  const uint32_t b2 = bf16_out(v2, bias, min(n + 2, N - 1)), b3 = bf16_out(v3, bias, min(n + 3, N - 1));
+// float32 -> fp16 bit pattern: the hardware conversion rounds to nearest even (default mode),
+// overflows to infinity and keeps fp16 subnormals.
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Output element n as 16-bit bits: bf16 (bf16_out), or with f16 the same steps in fp16 (the
+// linear layer's output dtype follows its input: fp16(float(fp16(C)) + float(bias[n]))).
+__device__ __forceinline__ uint32_t out16(float acc, const uint16_t* bias, int n, bool f16) {
+  if (f16) {
+    uint32_t h = f32_to_f16_rne(acc);
+    if (bias != nullptr) h = f32_to_f16_rne(f16_value(h) + f16_value(bias[n]));
+    return h;
+  }
+  return bf16_out(acc, bias, n);
+}
+
+__device__ __forceinline__ void store_out16x4(uint16_t* c, int n, int N, bool vec_ok, float v0, float v1,
+                                              float v2, float v3, const uint16_t* bias, bool f16) {
+  const uint32_t b0 = out16(v0, bias, min(n, N - 1), f16), b1 = out16(v1, bias, min(n + 1, N - 1), f16);
+  const uint32_t b2 = out16(v2, bias, min(n + 2, N - 1), f16), b3 = out16(v3, bias, min(n + 3, N - 1), f16);
   if (vec_ok && n + 3 < N) {
     uint2 pk;
     pk.x = b0 | (b1 << 16);

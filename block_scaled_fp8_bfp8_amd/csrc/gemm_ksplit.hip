@@ -218,7 +218,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
       v += *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(&slots[ww][0][0]) + q * 4);
     const int m = m0 + (tile % TM) * 16 + (ln & 15);
     const int n = n0 + (tile / TM) * 16 + 4 * (ln >> 4);
-    if (m < M && n < N) store_bf16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, v[0], v[1], v[2], v[3], args.bias);
+    if (m < M && n < N)
+      store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, v[0], v[1], v[2], v[3], args.bias, args.out_f16);
   }
 }
 

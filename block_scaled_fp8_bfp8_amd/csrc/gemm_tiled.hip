@@ -378,10 +378,10 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
         for (int tn = 0; tn < TN; ++tn) {
           const int nb = n0 + wn * WN + tn * 16 + 4 * kc;  // bias columns, clamped on tails (not stored)
           uint2 pk;
-          pk.x = bf16_out(acc[tn][tm][0], args.bias, min(nb, N - 1)) |
-                 (bf16_out(acc[tn][tm][1], args.bias, min(nb + 1, N - 1)) << 16);
-          pk.y = bf16_out(acc[tn][tm][2], args.bias, min(nb + 2, N - 1)) |
-                 (bf16_out(acc[tn][tm][3], args.bias, min(nb + 3, N - 1)) << 16);
+          pk.x = out16(acc[tn][tm][0], args.bias, min(nb, N - 1), args.out_f16) |
+                 (out16(acc[tn][tm][1], args.bias, min(nb + 1, N - 1), args.out_f16) << 16);
+          pk.y = out16(acc[tn][tm][2], args.bias, min(nb + 2, N - 1), args.out_f16) |
+                 (out16(acc[tn][tm][3], args.bias, min(nb + 3, N - 1), args.out_f16) << 16);
           *reinterpret_cast<uint2*>(out_lds + ((tm - c0) * 16 + r) * kRowBytes + (tn * 16 + 4 * kc) * 2) = pk;
         }
       // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
@@ -427,8 +427,8 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     for (int tn = 0; tn < TN; ++tn) {
       const int n = n0 + wn * WN + tn * 16 + 4 * kc;
       if (n < N)
-        store_bf16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][0], acc[tn][tm][1],
-                     acc[tn][tm][2], acc[tn][tm][3], args.bias);
+        store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][0], acc[tn][tm][1],
+                      acc[tn][tm][2], acc[tn][tm][3], args.bias, args.out_f16);
     }
   }
 }

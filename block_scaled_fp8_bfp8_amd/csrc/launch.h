@@ -11,6 +11,7 @@ constexpr int kBlock = 128;  // K block of the scale grid, also the N block of t
 
 constexpr int kInF32 = 0;
 constexpr int kInBf16 = 1;
+constexpr int kInF16 = 2;
 
 struct GemmArgs {
   const uint8_t* a;  // [M][lda] e4m3 activations
@@ -31,6 +32,7 @@ struct GemmArgs {
   // have leading dimensions that are multiples of 4. The kernels then apply the scales
   // inside the scaled MFMA and accumulate in its FP32 accumulator (no separate promotion).
   bool e8;
+  bool out_f16;  // C (and bias) are fp16 instead of bf16
 };
 
 // Tiled-schedule plan for a dense GEMM: tile shape, and the workspace it needs (none so far).

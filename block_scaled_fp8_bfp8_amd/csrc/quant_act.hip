@@ -13,7 +13,7 @@
 // that power of two (exactly) and the scale is written as its UE8M0 code, the biased
 // exponent byte.
 //
-// HBM-bound: per element it reads 4 (fp32) or 2 (bf16) bytes and writes 1, plus
+// HBM-bound: per element it reads 4 (fp32) or 2 (bf16, fp16) bytes and writes 1, plus
 // 4 bytes of scale per 128 elements. Mapping: 16 lanes per group, 8 consecutive
 // elements per lane (one or two 16-byte loads), 4 groups per wave, so one wave
 // streams 512 consecutive elements of a row. The group's amax is reduced with
@@ -34,7 +34,7 @@ constexpr int kGroupsPerBlock = kQuantThreads / 16;
 // Gather variant (kGather): output row m quantizes input row src_rows[m] / src_div, and rows
 // whose entry is negative are left unwritten (the MoE dispatch's padded buffer: entry = pair
 // index, src_div = top_k, so the input row is the pair's token).
-template <bool kBf16, bool kE8, bool kGather>
+template <int kIn, bool kE8, bool kGather>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
                                                                   void* __restrict__ as, int64_t ld_as,
@@ -60,13 +60,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   }
 
   float v[8];
-  if constexpr (kBf16) {
+  if constexpr (kIn == kInBf16) {
     const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else if constexpr (kIn == kInF16) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = f16_value(w[i] & 0xffffu);  // exact widening
+      v[2 * i + 1] = f16_value(w[i] >> 16);
     }
   } else {
     const float* p = static_cast<const float*>(x) + src * ldx + col;
@@ -109,15 +117,15 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
 
 namespace {
 
-template <bool kBf16, bool kE8>
+template <int kIn, bool kE8>
 void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as, int groups_per_row,
                       int64_t total, const int32_t* src_rows, int src_div, hipStream_t stream) {
   const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
   if (src_rows) {
-    hipLaunchKernelGGL((quant_act_kernel<kBf16, kE8, true>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+    hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, true>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
                        x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div);
   } else {
-    hipLaunchKernelGGL((quant_act_kernel<kBf16, kE8, false>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+    hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, false>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
                        x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div);
   }
 }
@@ -130,11 +138,14 @@ hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, in
   const int groups_per_row = (int)(K / kBlock);
   const int64_t total = M * groups_per_row;
   if (x_dtype == kInBf16) {
-    if (e8) launch_quant_cfg<true, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
-    else launch_quant_cfg<true, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    if (e8) launch_quant_cfg<kInBf16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    else launch_quant_cfg<kInBf16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+  } else if (x_dtype == kInF16) {
+    if (e8) launch_quant_cfg<kInF16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    else launch_quant_cfg<kInF16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
   } else {
-    if (e8) launch_quant_cfg<false, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
-    else launch_quant_cfg<false, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    if (e8) launch_quant_cfg<kInF32, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    else launch_quant_cfg<kInF32, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
   }
   return hipGetLastError();
 }

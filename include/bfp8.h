@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 4
+#define BFP8_ABI_VERSION 5
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -73,7 +73,8 @@ typedef enum bfp8_status {
 /* Activation dtypes accepted by bfp8_quant_act. */
 typedef enum bfp8_in_dtype {
   BFP8_IN_F32 = 0,
-  BFP8_IN_BF16 = 1
+  BFP8_IN_BF16 = 1,
+  BFP8_IN_F16 = 2
 } bfp8_in_dtype_t;
 
 /* GEMM schedules (page "lmdeploy/pull/4830", section "Kernel design": one schedule
@@ -112,7 +113,7 @@ const char* bfp8_last_error_message(void);
  * x is widened to float32 first (exact for bf16).
  *
  *   x       device, [M][ldx] elements of x_dtype, row-major; read only
- *   x_dtype BFP8_IN_F32 or BFP8_IN_BF16
+ *   x_dtype BFP8_IN_F32, BFP8_IN_BF16 or BFP8_IN_F16 (the 16-bit inputs widen to float32 exactly)
  *   M, K    M >= 0, K > 0 and K % 128 == 0
  *   ldx     >= K, elements; ldx * sizeof(element) % 16 == 0; x 16-byte aligned
  *   q       device, [M][ldq] bytes (e4m3fn codes); ldq >= K, ldq % 16 == 0; written
@@ -199,12 +200,12 @@ size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * bfp8_quant_act does, multiplied with the FP8 weight as bfp8_gemm does into a bf16 result,
  * and, when a bias is given, the bias is added to that bf16 result:
  *   out[m, n] = bf16(float(bf16(C[m, n])) + float(bias[n]))   (bias NULL: out = bf16(C)),
- * which is the page's output.add_(bias) on a bf16 output.
- *   x      [M][ldx] bf16 activations (x_dtype must be BFP8_IN_BF16; the page's output dtype
- *          follows the input, and this library writes bf16 only)
+ * which is the page's output.add_(bias) on a bf16 output; with fp16 activations the output,
+ * the bias and both roundings are fp16 (the page's output dtype follows the input).
+ *   x      [M][ldx] activations, x_dtype BFP8_IN_BF16 or BFP8_IN_F16
  *   b, bs  as for bfp8_gemm (weights [N][ldb] e4m3, scales [ceil(N/128)][ld_bs])
- *   bias   NULL or bf16 [N], 2-byte aligned
- *   c      [M][ldc] bf16 output
+ *   bias   NULL or [N] of x's dtype, 2-byte aligned
+ *   c      [M][ldc] output of x's dtype
  *   workspace / workspace_bytes: at least bfp8_linear_workspace_bytes(M, N, K) bytes,
  *          256-byte aligned (BFP8_ERR_WORKSPACE if smaller); it holds the quantized
  *          activations, which the call overwrites.
@@ -215,6 +216,16 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
                           const uint16_t* bias, uint16_t* c, int64_t ldc, int64_t N,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bfp8_gemm with an fp16 output: C[m, n] = fp16(sum_kb P_kb * As * Bs), rounded to nearest even
+ * once (overflow to infinity). Everything else as bfp8_gemm. For the linear layer's fp16 form
+ * (page "transformers/integrations/deepgemm.py": the output dtype follows the input).
+ */
+bfp8_status_t bfp8_gemm_f16(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                            const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                            uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * UE8M0 (power-of-two) scale factors (page "transformers/integrations/deepgemm.py":

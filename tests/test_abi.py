@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 4
+    assert lib.bfp8_abi_version() == 5
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -100,7 +100,7 @@ def _quant(lib, x=A, dt=0, M=4, K=256, ldx=256, q=B, ldq=256, as_=AS, ld_as=4):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dt=2), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(dt=3), _native.BFP8_ERR_UNSUPPORTED),
     (dict(M=-3), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(K=130, ldx=256, ldq=256), _native.BFP8_ERR_UNSUPPORTED),
     (dict(x=None), _native.BFP8_ERR_INVALID_ARGUMENT),

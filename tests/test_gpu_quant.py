@@ -97,9 +97,9 @@ def test_rejects_bad_arguments(gpu):
     x = torch.zeros(4, 200, dtype=torch.float32, device=gpu)
     with pytest.raises(NotImplementedError):
         bfp8.quant_act(x)  # K % 128 != 0
-    x16 = torch.zeros(4, 256, dtype=torch.float16, device=gpu)
+    x64 = torch.zeros(4, 256, dtype=torch.float64, device=gpu)
     with pytest.raises(NotImplementedError):
-        bfp8.quant_act(x16)
+        bfp8.quant_act(x64)
     xo = torch.zeros(4, 257, dtype=torch.float32, device=gpu)[:, 1:]  # misaligned base
     with pytest.raises(ValueError):
         bfp8.quant_act(xo)

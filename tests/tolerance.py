@@ -160,3 +160,23 @@ def reference_e8(a_q, a_e, b_q, b_e, rows=None, cols=None):
 
     return reference(a_q, ue8m0.decode(np.asarray(a_e)).astype(np.float32), b_q,
                      ue8m0.decode(np.asarray(b_e)).astype(np.float32), rows, cols)
+
+
+def compare_f16(got_bits, ref_bits, mag, k, what=""):
+    """compare() for fp16 outputs: the same bound with fp16's ulp (rounded once, to nearest even)."""
+    from oracle import f16
+
+    got = f16.from_bits(got_bits)
+    ref = f16.from_bits(ref_bits)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
+    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3"
+    bound = 2 * f16.ulp(ref) + 1e-3 * np.abs(ref) + (k / 128 + 130) * 2.0**-24 * mag
+    bad = d > bound
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r}")
+    return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_bits))}
