@@ -118,3 +118,34 @@ def grouped_gemm_contiguous_ref(a_q, a_s, b_q, b_s, layout, rows=None, cols=None
     """(rows, bf16 bits) of the grouped product for the non-padding rows."""
     valid, acc, _ = grouped_gemm_contiguous_acc_ref(a_q, a_s, b_q, b_s, layout, rows, cols)
     return valid, bf16.to_bits(acc)
+
+
+def grouped_gemm_contiguous_nn_acc_ref(a_q, a_s, b_nn, bs_nn, layout, rows=None, cols=None):
+    """The grouped product with NN expert weights (page "transformers/integrations/deepgemm.py",
+    ``grouped_fp8_fp4_matmul_nn`` for ``is_transposed`` experts): b_nn [G, K, N] (N contiguous) and
+    its scales bs_nn [G, ceil(K/128), ceil(N/128)]; C[m, n] = sum_kb sum_{k in kb} a[m, k] b_nn[g][k, n]
+    * As[m, kb] * Bs_nn[g][kb, n // 128]. Returns (rows, acc) for the non-padding rows.
+
+    Written on the NN operands directly: per expert, per K block, decoded codes multiplied with
+    the K-major weight block as it is stored."""
+    layout = np.asarray(layout)
+    b_nn = np.asarray(b_nn)
+    bs_nn = np.asarray(bs_nn, dtype=np.float32)
+    a_q = np.asarray(a_q)
+    a_s = np.asarray(a_s, dtype=np.float32)
+    k = a_q.shape[1]
+    n = b_nn.shape[2]
+    all_rows = np.arange(layout.shape[0]) if rows is None else np.asarray(rows)
+    valid = all_rows[layout[all_rows] >= 0]
+    cols = np.arange(n) if cols is None else np.asarray(cols)
+    acc = np.zeros((valid.size, cols.size), dtype=np.float64)
+    for g in np.unique(layout[valid]):
+        sel = np.nonzero(layout[valid] == g)[0]
+        r = valid[sel]
+        a_val = e4m3.decode(a_q[r])
+        b_val = e4m3.decode(b_nn[g][:, cols])  # [K, cols]
+        for kb in range(-(-k // BLOCK)):
+            ks = slice(kb * BLOCK, min((kb + 1) * BLOCK, k))
+            p = a_val[:, ks] @ b_val[ks, :]
+            acc[sel] += p * (a_s[r, kb].astype(np.float64)[:, None] * bs_nn[g, kb, cols // BLOCK].astype(np.float64)[None, :])
+    return valid, acc

@@ -171,3 +171,33 @@ def test_moe_layout_generator_contract():
     for g, c in enumerate(counts):
         assert (layout == g).sum() == c
     assert torch.from_numpy(layout).dtype == torch.int32
+
+
+def test_grouped_nn_brute_force_and_against_nt():
+    """NN expert weights [G, K, N]: exact rationals on a tiny case, and the same numbers as the NT
+    form when the NT operand is the transpose (a layout, not a different product)."""
+    from fractions import Fraction
+
+    from oracle import e4m3, gemm
+
+    rng = np.random.default_rng(71)
+    g_count, m, n, k = 2, 256, 136, 256
+    a = rng.integers(0, 0x7E, (m, k)).astype(np.uint8)
+    b_nn = rng.integers(0, 0x7E, (g_count, k, n)).astype(np.uint8) | (rng.integers(0, 2, (g_count, k, n)).astype(np.uint8) << 7)
+    a_s = rng.uniform(1e-3, 1e-2, (m, 2)).astype(np.float32)
+    bs_nn = rng.uniform(1e-3, 1e-2, (g_count, 2, 2)).astype(np.float32)
+    layout = np.concatenate([np.zeros(100, np.int32), -np.ones(28, np.int32), np.ones(128, np.int32)])
+    rows, acc = gemm.grouped_gemm_contiguous_nn_acc_ref(a, a_s, b_nn, bs_nn, layout)
+    assert rows.tolist() == list(range(100)) + list(range(128, 256))
+    av, bv = e4m3.decode(a), e4m3.decode(b_nn)
+    for i, r in enumerate(rows[::37]):
+        for c in (0, 77, 128, 135):
+            g = layout[r]
+            want = Fraction(0)
+            for kb in range(2):
+                s = sum(Fraction(float(av[r, kk])) * Fraction(float(bv[g, kk, c])) for kk in range(kb * 128, kb * 128 + 128))
+                want += s * Fraction(float(a_s[r, kb])) * Fraction(float(bs_nn[g, kb, c // 128]))
+            assert abs(Fraction(float(acc[i * 37, c])) - want) <= abs(want) * Fraction(1, 2**46), (r, c)  # float64 rounding only
+    rows2, acc2, _ = gemm.grouped_gemm_contiguous_acc_ref(a, a_s, b_nn.transpose(0, 2, 1), bs_nn.transpose(0, 2, 1), layout)
+    np.testing.assert_array_equal(rows, rows2)
+    np.testing.assert_allclose(acc, acc2, rtol=1e-14, atol=0)
