@@ -26,7 +26,7 @@ __all__ = [
     "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
     "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
-    "moe_forward_workspace_bytes", "set_schedule", "get_schedule", "schedule_for",
+    "moe_forward_workspace_bytes", "nn_to_nt_weights", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
 
@@ -527,6 +527,27 @@ def moe_forward(hidden: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torc
                               _stream(hidden.device))
     _check(st, "bfp8_moe_forward")
     return out
+
+
+def nn_to_nt_weights(w_nn: torch.Tensor, s_nn: torch.Tensor):
+    """NN expert weights w_nn [E, K, N] (e4m3) and scales s_nn [E, K/128, ceil(N/128)] converted once
+    to the NT layout the grouped GEMM reads: (w [E, N, K], s [E, ceil(N/128), K/128])."""
+    w_nn = _as_u8(w_nn, "w_nn")
+    _require(w_nn, "w_nn", torch.uint8, 3)
+    _require(s_nn, "s_nn", torch.float32, 3)
+    if not (w_nn.is_contiguous() and s_nn.is_contiguous()):
+        raise ValueError("w_nn and s_nn must be contiguous")
+    e, k, n = w_nn.shape
+    if tuple(s_nn.shape) != (e, -(-k // 128), -(-n // 128)):
+        raise ValueError("s_nn shape does not match w_nn")
+    w = torch.empty((e, n, k), dtype=torch.uint8, device=w_nn.device)
+    s = torch.empty((e, s_nn.shape[2], s_nn.shape[1]), dtype=torch.float32, device=w_nn.device)
+    lib = _native.lib()
+    _check(lib.bfp8_transpose_weights(w_nn.data_ptr(), e, k, n, n, w.data_ptr(), k, _stream(w_nn.device)),
+           "bfp8_transpose_weights")
+    _check(lib.bfp8_transpose_scales(s_nn.data_ptr(), e, s_nn.shape[1], s_nn.shape[2], s.data_ptr(),
+                                     _stream(w_nn.device)), "bfp8_transpose_scales")
+    return w, s
 
 
 def linear_workspace_bytes(m: int, n: int, k: int) -> int:

@@ -590,6 +590,33 @@ bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int
                   "moe_combine");
 }
 
+bfp8_status_t bfp8_transpose_weights(const uint8_t* src, int64_t E, int64_t K, int64_t N, int64_t ld_src,
+                                     uint8_t* dst, int64_t ld_dst, void* stream) {
+  if (E < 1 || K < 1 || N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "E, K and N must be >= 1");
+  if (E > 1024 || K > kMaxDim || N > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "E <= 1024, K, N <= 2^30");
+  if (ld_src < N || ld_dst < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_src must be >= N and ld_dst >= K");
+  if (!src || !dst) return fail(BFP8_ERR_INVALID_ARGUMENT, "src and dst must not be NULL");
+  const uint8_t* src_end = src + E * K * ld_src;
+  const uint8_t* dst_end = dst + E * N * ld_dst;
+  if (src < dst_end && dst < src_end) return fail(BFP8_ERR_INVALID_ARGUMENT, "src and dst must not overlap");
+  bfp8_status_t st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_transpose_u8(src, E, K, N, ld_src, dst, ld_dst, (hipStream_t)stream),
+                  "transpose_weights");
+}
+
+bfp8_status_t bfp8_transpose_scales(const float* src, int64_t E, int64_t R, int64_t C, float* dst, void* stream) {
+  if (E < 1 || R < 1 || C < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "E, R and C must be >= 1");
+  if (E * R * C > ((int64_t)1 << 40)) return fail(BFP8_ERR_UNSUPPORTED, "too many scales");
+  if (!src || !dst) return fail(BFP8_ERR_INVALID_ARGUMENT, "src and dst must not be NULL");
+  if (!aligned(src, 4) || !aligned(dst, 4)) return fail(BFP8_ERR_MISALIGNED, "src and dst must be 4-byte aligned");
+  if (src < dst + E * R * C && dst < src + E * R * C)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "src and dst must not overlap");
+  bfp8_status_t st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_transpose_f32(src, E, R, C, dst, (hipStream_t)stream), "transpose_scales");
+}
+
 bfp8_status_t bfp8_set_schedule(int schedule) {
   if (schedule < BFP8_SCHED_AUTO || schedule >= BFP8_SCHED_COUNT_)
     return fail(BFP8_ERR_INVALID_ARGUMENT, "unknown schedule %d", schedule);

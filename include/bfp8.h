@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 5
+#define BFP8_ABI_VERSION 6
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -333,6 +333,19 @@ bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int
                                const float* topk_weights, int32_t top_k, int32_t E, const uint8_t* w_up,
                                const float* s_up, const uint8_t* w_down, const float* s_down, int64_t I,
                                uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * NN expert weights (page "transformers/integrations/deepgemm.py": grouped_fp8_fp4_matmul_nn for
+ * experts stored transposed, [E, K, N]). The grouped GEMM reads NT weights; NN weights are
+ * converted once (they are static) with:
+ *   bfp8_transpose_weights: dst[e][n][k] = src[e][k][n], src [E][K][ld_src] (ld_src >= N),
+ *                           dst [E][N][ld_dst] (ld_dst >= K), bytes; no overlap.
+ *   bfp8_transpose_scales:  dst[e][c][r] = src[e][r][c] for contiguous float32 [E][R][C]
+ *                           (NN scales [E][K/128][ceil(N/128)] -> [E][ceil(N/128)][K/128]).
+ */
+bfp8_status_t bfp8_transpose_weights(const uint8_t* src, int64_t E, int64_t K, int64_t N, int64_t ld_src,
+                                     uint8_t* dst, int64_t ld_dst, void* stream);
+bfp8_status_t bfp8_transpose_scales(const float* src, int64_t E, int64_t R, int64_t C, float* dst, void* stream);
 
 /* Process-wide schedule override for bfp8_gemm (tests and benchmarks):
  * BFP8_SCHED_AUTO restores the automatic choice. Returns BFP8_ERR_INVALID_ARGUMENT

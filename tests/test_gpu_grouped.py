@@ -118,3 +118,32 @@ def test_grouped_rejections(gpu):
     with pytest.raises(ValueError):  # M % 128 != 0
         bfp8.grouped_gemm_contiguous(q, s, bq, bs, lay)
 
+
+
+def test_nn_weights_converted_once(gpu):
+    """NN expert weights [G, K, N] (the page's transposed experts): the conversion to [G, N, K] is
+    bit-exact, and the grouped GEMM on the converted weights matches the NN oracle."""
+    from oracle import gemm
+
+    g_count, n, k = 3, 200, 384
+    rng = np.random.default_rng(90)
+    ws = [workloads.weight(n, k, seed=91 + g) for g in range(g_count)]
+    w_nn = torch.stack([w.q.t().contiguous() for w in ws])  # [G, K, N]
+    s_nn = torch.stack([w.s.t().contiguous() for w in ws])  # [G, K/128, ceil(N/128)]
+    announce("nn_to_nt_weights", tuple(w_nn.shape))
+    w_nt, s_nt = bfp8.nn_to_nt_weights(w_nn.to(gpu), s_nn.to(gpu))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(w_nt.cpu().numpy(), w_nn.numpy().transpose(0, 2, 1))
+    np.testing.assert_array_equal(s_nt.cpu().numpy(), s_nn.numpy().transpose(0, 2, 1))
+    layout = np.concatenate([np.full(128, 2, np.int32), np.full(90, 0, np.int32), np.full(38, -1, np.int32),
+                             np.full(128, 1, np.int32)])
+    x = workloads.act_normal_bf16(layout.size, k, seed=95)
+    q, s, q_ref, s_ref = quant_gpu_checked(x, gpu, "nn activations")
+    c = _grouped(q, s, w_nt, s_nt, torch.from_numpy(layout).to(gpu), "nn weights")
+    rows, acc = gemm.grouped_gemm_contiguous_nn_acc_ref(q_ref, s_ref, w_nn.numpy(), s_nn.numpy(), layout)
+    from oracle import bf16
+    mag = np.zeros_like(acc)
+    for g in range(g_count):
+        sel = np.nonzero(layout[rows] == g)[0]
+        mag[sel] = tolerance.abs_product_mass(q_ref, s_ref, ws[g].q.numpy(), ws[g].s.numpy(), rows[sel], np.arange(n))
+    tolerance.compare(bits(c)[rows], bf16.to_bits(acc), mag, k, "grouped nn")
