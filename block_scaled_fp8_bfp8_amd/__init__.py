@@ -26,7 +26,7 @@ __all__ = [
     "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
     "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
-    "moe_forward_workspace_bytes", "nn_to_nt_weights", "set_schedule", "get_schedule", "schedule_for",
+    "moe_forward_workspace_bytes", "nn_to_nt_weights", "pad_k", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
 
@@ -108,21 +108,23 @@ def abi_version() -> int:
 
 
 def quant_act(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
-    """Per-token-group FP8 quantization of x [M, K] (fp32 or bf16, row stride may exceed K).
+    """Per-token-group FP8 quantization of x [M, K] (fp32, bf16 or fp16; K a multiple of 16; row
+    stride may exceed K).
 
-    Returns (q, s): q uint8 e4m3fn codes [M, K]; s float32 [M, K/128], stored group-major
-    (s.stride() == (1, M)), i.e. the "column-major" activation scales the GEMM reads.
+    Returns (q, s): q uint8 e4m3fn codes [M, K], a view of rows padded to ceil(K/128) * 128 bytes
+    (the GEMMs read whole 128-byte blocks; the padding is never written); s float32
+    [M, ceil(K/128)], stored group-major (s.stride() == (1, M)), i.e. the "column-major"
+    activation scales the GEMM reads.
     """
     dt = _in_dtype(x, "quant_act")
     _require(x, "x", x.dtype, 2)
     if x.stride(1) != 1:
         raise ValueError("x must be K-contiguous")
     m, k = x.shape
-    if q is None:
-        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if q is None:  # rows of whole 128-byte blocks, as the GEMMs read them
+        q = torch.empty((m, -(-k // 128) * 128), dtype=torch.uint8, device=x.device)[:, :k]
     if scales is None:
-        scales = torch.empty((k // 128 if k % 128 == 0 else -(-k // 128), m), dtype=torch.float32,
-                             device=x.device).t()
+        scales = torch.empty((-(-k // 128), m), dtype=torch.float32, device=x.device).t()
     _require(q, "q", torch.uint8, 2)
     _require(scales, "scales", torch.float32, 2)
     if q.stride(1) != 1 or scales.stride(0) != 1:
@@ -140,10 +142,34 @@ def _scale_ld_as(a_s: torch.Tensor, m: int) -> int:
     return a_s.stride(1) if a_s.size(1) > 1 else max(m, 1)
 
 
+def pad_k(codes: torch.Tensor) -> torch.Tensor:
+    """A [..., K] view of the uint8 codes whose rows are padded with zeros to ceil(K/128) * 128
+    bytes, the row length the GEMMs read (a copy unless they already are laid out so)."""
+    codes = _as_u8(codes, "codes")
+    *lead, k = codes.shape
+    kp = -(-k // 128) * 128
+    want, span = [1], kp
+    for d in reversed(lead):  # strides of a contiguous [..., Kp] buffer
+        want.insert(0, span)
+        span *= d
+    if codes.stride() == tuple(want) and codes.data_ptr() % 16 == 0:
+        return codes
+    buf = torch.zeros((*lead, kp), dtype=torch.uint8, device=codes.device)
+    buf[..., :k] = codes
+    return buf[..., :k]
+
+
+def _check_expert_codes(b_q: torch.Tensor):
+    """Expert weights [G, N, K]: K-contiguous rows, ldb apart, matrices N * ldb apart."""
+    if b_q.stride(2) != 1 or b_q.stride(0) != b_q.shape[1] * b_q.stride(1):
+        raise ValueError("b_q must be [G, N, K] with contiguous rows (padded rows from pad_k are fine)")
+
+
 def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """C[M, N] (bf16) = blockwise FP8 product of a_q [M, K] and b_q [N, K] with scales a_s [M, K/128]
-    (group-major) and b_s [ceil(N/128), K/128].
+    """C[M, N] (bf16) = blockwise FP8 product of a_q [M, K] and b_q [N, K] with scales a_s
+    [M, ceil(K/128)] (group-major) and b_s [ceil(N/128), ceil(K/128)]. K is a multiple of 16; the
+    row strides of a_q and b_q must be at least ceil(K/128) * 128 (what quant_act and pad_k give).
 
     workspace: optional caller-owned uint8 buffer on the same device (at least
     bfp8_gemm_workspace_bytes(M, N, K) bytes); by default one buffer per (device, stream) is kept."""
@@ -193,7 +219,8 @@ def grouped_gemm_contiguous(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Ten
                             layout: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """M-grouped contiguous product: row m uses expert layout[m] (int32; -1 = padding, not written).
 
-    a_q [M, K] (M % 128 == 0), a_s [M, K/128] group-major, b_q [G, N, K], b_s [G, ceil(N/128), K/128]."""
+    a_q [M, K] (M % 128 == 0), a_s [M, ceil(K/128)] group-major, b_q [G, N, K] (rows of whole
+    128-byte blocks, as for gemm), b_s [G, ceil(N/128), ceil(K/128)]."""
     a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
     _require(a_q, "a_q", torch.uint8, 2)
     _require(b_q, "b_q", torch.uint8, 3)
@@ -204,8 +231,9 @@ def grouped_gemm_contiguous(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Ten
     g, n, k2 = b_q.shape
     if k2 != k or layout.shape[0] != m:
         raise ValueError("shape mismatch between a_q, b_q and layout")
-    if not (b_q.is_contiguous() and b_s.is_contiguous() and layout.is_contiguous()):
-        raise ValueError("b_q, b_s and layout must be contiguous")
+    _check_expert_codes(b_q)
+    if not (b_s.is_contiguous() and layout.is_contiguous()):
+        raise ValueError("b_s and layout must be contiguous")
     if tuple(b_s.shape) != (g, -(-n // 128), -(-k // 128)) or tuple(a_s.shape) != (m, -(-k // 128)):
         raise ValueError("scale shapes do not match")
     if out is None:
@@ -301,8 +329,8 @@ def quant_act_ue8m0(x: torch.Tensor, q: torch.Tensor | None = None, scales: torc
     if x.stride(1) != 1:
         raise ValueError("x must be K-contiguous")
     m, k = x.shape
-    if q is None:
-        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if q is None:  # rows of whole 128-byte blocks, as the GEMMs read them
+        q = torch.empty((m, -(-k // 128) * 128), dtype=torch.uint8, device=x.device)[:, :k]
     if scales is None:
         ld = max(-(-m // 4) * 4, 4)
         scales = torch.empty((-(-k // 128), ld), dtype=torch.uint8, device=x.device)[:, :m].t()
@@ -377,8 +405,9 @@ def grouped_gemm_contiguous_ue8m0(a_q: torch.Tensor, a_e: torch.Tensor, b_q: tor
     nb = -(-n // 128)
     if k2 != k or layout.shape[0] != m:
         raise ValueError("shape mismatch between a_q, b_q and layout")
-    if not (b_q.is_contiguous() and layout.is_contiguous()):
-        raise ValueError("b_q and layout must be contiguous")
+    _check_expert_codes(b_q)
+    if not layout.is_contiguous():
+        raise ValueError("layout must be contiguous")
     if tuple(b_e.shape) != (g, nb, kb) or tuple(a_e.shape) != (m, kb):
         raise ValueError("scale shapes do not match")
     if b_e.stride(2) != 1 or b_e.stride(0) != nb * b_e.stride(1):
@@ -435,8 +464,8 @@ def quant_act_gather(x: torch.Tensor, row_src: torch.Tensor, src_div: int = 1):
     if x.stride(1) != 1 or not row_src.is_contiguous():
         raise ValueError("x must be K-contiguous and row_src contiguous")
     m, k = row_src.numel(), x.shape[1]
-    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    s = torch.empty((k // 128, m), dtype=torch.float32, device=x.device).t()
+    q = torch.empty((m, -(-k // 128) * 128), dtype=torch.uint8, device=x.device)[:, :k]
+    s = torch.empty((-(-k // 128), m), dtype=torch.float32, device=x.device).t()
     st = _native.lib().bfp8_quant_act_gather(x.data_ptr(), dt, x.shape[0], k, x.stride(0), row_src.data_ptr(),
                                              src_div, m, q.data_ptr(), q.stride(0), s.data_ptr(), max(m, 1),
                                              _stream(x.device))

@@ -77,21 +77,25 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const void* as, int
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
   if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
   if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
-  if (K % bfp8::kBlock != 0)
-    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128 (only whole 128-wide scale blocks)",
-                (long long)K);
+  if (K % 16 != 0)
+    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 16 (16-byte operand pieces)", (long long)K);
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return fail(BFP8_ERR_UNSUPPORTED, "M, N and K must each be at most 2^30");
+  // Rows are read in whole 128-byte K blocks; with K % 128 != 0 the last block's bytes past K
+  // are read (and masked), so every row must hold ceil(K/128) * 128 bytes.
+  const int64_t Kp = (K + bfp8::kBlock - 1) / bfp8::kBlock * bfp8::kBlock;
   if (!b || !bs) return fail(BFP8_ERR_INVALID_ARGUMENT, "b and bs must not be NULL");
   if (M > 0 && (!a || !as || !c)) return fail(BFP8_ERR_INVALID_ARGUMENT, "a, as and c must not be NULL when M > 0");
-  if (lda < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "lda = %lld < K = %lld", (long long)lda, (long long)K);
-  if (ldb < K) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldb = %lld < K = %lld", (long long)ldb, (long long)K);
+  if (lda < Kp)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "lda = %lld < K rounded up to 128 = %lld", (long long)lda, (long long)Kp);
+  if (ldb < Kp)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "ldb = %lld < K rounded up to 128 = %lld", (long long)ldb, (long long)Kp);
   if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
   if (workspace && !aligned(workspace, 256))
     return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-  if (ld_bs < K / bfp8::kBlock)
-    return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_bs = %lld < K/128 = %lld", (long long)ld_bs,
-                (long long)(K / bfp8::kBlock));
+  if (ld_bs < Kp / bfp8::kBlock)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_bs = %lld < ceil(K/128) = %lld", (long long)ld_bs,
+                (long long)(Kp / bfp8::kBlock));
   if (ldc < N) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldc = %lld < N = %lld", (long long)ldc, (long long)N);
   if (lda % 16 || ldb % 16) return fail(BFP8_ERR_MISALIGNED, "lda and ldb must be multiples of 16 bytes");
   if (!aligned(a, 16) || !aligned(b, 16)) return fail(BFP8_ERR_MISALIGNED, "a and b must be 16-byte aligned");
@@ -101,7 +105,7 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const void* as, int
   if (!aligned(c, 2)) return fail(BFP8_ERR_MISALIGNED, "c must be 2-byte aligned");
   // The kernels address a row inside A, and inside one weight matrix of B, with a 32-bit
   // byte offset from the operand's base.
-  if ((N - 1) * ldb + K > kMaxOperandSpan || (M > 0 && (M - 1) * lda + K > kMaxOperandSpan))
+  if ((N - 1) * ldb + Kp > kMaxOperandSpan || (M > 0 && (M - 1) * lda + Kp > kMaxOperandSpan))
     return fail(BFP8_ERR_UNSUPPORTED, "A (M x lda) and each weight matrix (N x ldb) must span less than 4 GiB");
   const size_t need = grouped ? 0 : bfp8_gemm_workspace_bytes(M, N, K);
   if (workspace_bytes < need || (need > 0 && !workspace))
@@ -116,8 +120,7 @@ bfp8_status_t check_quant_args(const void* x, int x_dtype, int64_t M, int64_t K,
     return fail(BFP8_ERR_UNSUPPORTED, "x_dtype %d is not BFP8_IN_F32, BFP8_IN_BF16 or BFP8_IN_F16", x_dtype);
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
   if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
-  if (K % bfp8::kBlock != 0)
-    return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128", (long long)K);
+  if (K % 16 != 0) return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 16", (long long)K);
   if (M > kMaxDim || K > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M and K must each be at most 2^30");
   if (M == 0) return ok();
   if (!x || !q || !as) return fail(BFP8_ERR_INVALID_ARGUMENT, "x, q and as must not be NULL");
@@ -186,7 +189,7 @@ bfp8_status_t bfp8_quant_act_ue8m0(const void* x, int x_dtype, int64_t M, int64_
 }
 
 size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % bfp8::kBlock != 0) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 0;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   if (choose_schedule(M, N, K) != BFP8_SCHED_TILED) return 0;
   return bfp8::plan_tiled(M, N, K).workspace_bytes;
@@ -211,8 +214,9 @@ bfp8_status_t launch_dense(const uint8_t* a, int64_t lda, const void* as, int64_
 LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   LinearLayout L;
-  L.as_off = up((size_t)M * (size_t)K);
-  L.gemm_off = L.as_off + up((size_t)4 * (size_t)M * (size_t)(K / bfp8::kBlock));
+  const size_t kp = (size_t)((K + bfp8::kBlock - 1) / bfp8::kBlock);  // K blocks (the last may be partial)
+  L.as_off = up((size_t)M * kp * bfp8::kBlock);  // codes in rows of whole 128-byte blocks
+  L.gemm_off = L.as_off + up((size_t)4 * (size_t)M * kp);
   L.total = L.gemm_off + bfp8_gemm_workspace_bytes(M, N, K);
   return L;
 }
@@ -306,7 +310,7 @@ bfp8_status_t bfp8_grouped_gemm_contiguous_ue8m0(const uint8_t* a, int64_t lda, 
 }
 
 size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % bfp8::kBlock != 0) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 0;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   return linear_layout(M, N, K).total;
 }
@@ -323,10 +327,11 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
   if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
   if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
   if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
-  if (K % bfp8::kBlock != 0) return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 128", (long long)K);
+  if (K % 16 != 0) return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 16", (long long)K);
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return fail(BFP8_ERR_UNSUPPORTED, "M, N and K must each be at most 2^30");
   const size_t need = bfp8_linear_workspace_bytes(M, N, K);
+  const int64_t Kp = (K + bfp8::kBlock - 1) / bfp8::kBlock * bfp8::kBlock;  // row stride of the codes
   if (M > 0 && (!workspace || workspace_bytes < need))
     return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   bfp8_status_t st = BFP8_OK;
@@ -336,16 +341,16 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
   float* as = M > 0 ? reinterpret_cast<float*>(ws + L.as_off) : nullptr;
   void* gws = M > 0 ? static_cast<void*>(ws + L.gemm_off) : nullptr;
   const size_t gws_bytes = M > 0 ? workspace_bytes - L.gemm_off : 0;
-  st = check_quant_args(x, x_dtype, M, K, ldx, q, K, as, M);
+  st = check_quant_args(x, x_dtype, M, K, ldx, q, Kp, as, M);
   if (st != BFP8_OK) return st;
-  st = check_gemm_args(q, K, as, M, b, ldb, bs, ld_bs, c, ldc, M, N, K, gws, gws_bytes, false);
+  st = check_gemm_args(q, Kp, as, M, b, ldb, bs, ld_bs, c, ldc, M, N, K, gws, gws_bytes, false);
   if (st != BFP8_OK) return st;
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
-  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, K, as, M, false, (hipStream_t)stream), "quant_act");
+  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, Kp, as, M, false, (hipStream_t)stream), "quant_act");
   if (st != BFP8_OK) return st;
-  return launch_dense(q, K, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream, false,
+  return launch_dense(q, Kp, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream, false,
                       x_dtype == BFP8_IN_F16);
 }
 

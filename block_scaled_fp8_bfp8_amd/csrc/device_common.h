@@ -24,6 +24,17 @@ __device__ __forceinline__ v4f mfma_block(const v8i& src0, const v8i& src1) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(src0, src1, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// Zeroes the bytes of an MFMA operand fragment that lie at or past K in a partial last K block
+// (K % 128 != 0, K a multiple of 16): lane (r, kc) holds bytes [32 kc, 32 kc + 32) of the block,
+// of which the first `valid` exist. Both operands are masked, so stale bytes (even e4m3 NaN
+// codes) past K contribute exact zeros.
+__device__ __forceinline__ v8i mask_k_tail(v8i f, int valid, int kc) {
+  const int v = valid - 32 * kc;  // a multiple of 16: whole dwords are kept or cleared
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v >= 4 * (i + 1) ? f[i] : 0;
+  return f;
+}
+
 // The same product with UE8M0 block scales applied by the hardware and the result added to
 // `acc`: D = acc + sum_k (src0[i][k] 2^(e0 - 127)) (src1[j][k] 2^(e1 - 127)). Lane l gives
 // the scale code of row l % 16 of each operand in the low byte of e0 / e1 (the instruction

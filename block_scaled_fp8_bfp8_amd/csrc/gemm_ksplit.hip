@@ -62,7 +62,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
   const int r = lane & 15, kc = lane >> 4;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int M = args.M, N = args.N;
-  const int KB = args.K / kBlock;
+  const int KB = (args.K + kBlock - 1) / kBlock;  // the last block may be partial (K % 128 != 0)
+  const int k_tail = args.K - (KB - 1) * kBlock;   // bytes of the last block that exist
   const int nkb = KB > w ? (KB - w + WAVES - 1) / WAVES : 0;  // this wave's blocks: w + i * WAVES
 
   // Copy plan: piece j is slot rows [8j, 8j + 8); lane l lands at row 8j + l/8, physical
@@ -153,11 +154,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     float sc[TM];
     ScaleT ea[TM];
     const ScaleT bs_kb = weight_scale(kb);
+    const bool tail = kb == KB - 1 && k_tail < kBlock;  // wave-uniform
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_at(sl, tn * 16);
+    for (int tn = 0; tn < TN; ++tn) {
+      fb[tn] = frag_at(sl, tn * 16);
+      if (tail) fb[tn] = mask_k_tail(fb[tn], k_tail, kc);
+    }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       fa[tm] = frag_at(sl, BN + tm * 16);
+      if (tail) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
       if constexpr (kE8) {
         ea[tm] = reinterpret_cast<const uint8_t*>(&as_slots[w][slot][0])[tm * 16 + r];
       } else {

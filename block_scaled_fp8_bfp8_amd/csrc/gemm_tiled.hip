@@ -64,7 +64,7 @@ __device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int 
   tn = r / gm;
 }
 
-template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped, bool kE8>
+template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped, bool kE8, bool kTail>
 __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs args) {
   constexpr int kWaves = WGN * WGM;  // waves per K group
   constexpr int WN = BN / WGN, WM = BM / WGM;
@@ -101,7 +101,12 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 
   const int n_tiles = (N + BN - 1) / BN;
   const int m_tiles = (M + BM - 1) / BM;
-  const int KB = args.K / kBlock / KG;  // K blocks per group (the plan makes K / 128 a multiple of KG)
+  // K blocks per group (the plan makes their count a multiple of KG). kTail kernels take a
+  // partial last block (K % 128 != 0): its k_tail existing bytes are kept in the fragments and
+  // the rest masked to zero; the others compile no mask at all.
+  const int KB_all = (args.K + kBlock - 1) / kBlock;
+  const int KB = KB_all / KG;
+  const int k_tail = kTail ? args.K - (KB_all - 1) * kBlock : kBlock;
   int tile_n, tile_m;
   map_tile(blockIdx.x, n_tiles, m_tiles, 8, tile_n, tile_m);
   const int n0 = tile_n * BN, m0 = tile_m * BM;
@@ -252,6 +257,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     // branches; those registers are never used.
     const int nslot = (kb + 1) % STAGES;
     const uint8_t* nstage = &smem[g][nslot][0];
+    const bool mask_next = kTail && kb + 1 < KB && gkb(kb + 1) == KB_all - 1;  // uniform
     const ScaleT bs_next = weight_scale(gkb(min(kb + 1, KB - 1)));
     float sc[TM];
     if constexpr (!kE8) {
@@ -294,9 +300,13 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
       }
       if (tn == TN - 1) {
         fa[tm] = frag_a(nstage, tm);
+        if (mask_next) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
         sa[tm] = act_scale(nslot, tm);
       }
-      if (tm == TM - 1) fb[tn] = frag_b(nstage, tn);
+      if (tm == TM - 1) {
+        fb[tn] = frag_b(nstage, tn);
+        if (mask_next) fb[tn] = mask_k_tail(fb[tn], k_tail, kc);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!kE8) {
         p2 = p1;
@@ -319,13 +329,18 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   // blocks 0 and 1 have landed once the copies of blocks 2 .. STAGES-1 are the only ones left
   wait_block_after_next(STAGES <= KB);
   lds_barrier();
+  const bool mask_first = kTail && gkb(0) == KB_all - 1;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     fa[tm] = frag_a(&smem[g][0][0], tm);
+    if (mask_first) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
     sa[tm] = act_scale(0, tm);
   }
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) fb[tn] = frag_b(&smem[g][0][0], tn);
+  for (int tn = 0; tn < TN; ++tn) {
+    fb[tn] = frag_b(&smem[g][0][0], tn);
+    if (mask_first) fb[tn] = mask_k_tail(fb[tn], k_tail, kc);
+  }
   bsv = weight_scale(g);
   // every wave has read stage 0 before iteration 0 refills it
   lds_barrier();
@@ -433,13 +448,14 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   }
 }
 
-template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool G>
-hipError_t launch_tiled_cfg(const GemmArgs& args, int tiles, hipStream_t stream) {
+template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool G, bool T>
+hipError_t launch_tiled_cfg(const GemmArgs& args, hipStream_t stream) {
+  const unsigned tiles = (unsigned)(((args.N + BN - 1) / BN) * ((args.M + BM - 1) / BM));
   if (args.e8) {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G, true>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G, true, T>), dim3(tiles),
                        dim3(KG * WGN * WGM * 64), 0, stream, args);
   } else {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G, false>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_tiled_kernel<BN, BM, WGN, WGM, STAGES, KG, G, false, T>), dim3(tiles),
                        dim3(KG * WGN * WGM * 64), 0, stream, args);
   }
   return hipGetLastError();
@@ -465,16 +481,23 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
   (void)workspace;
   const TiledPlan p = plan_tiled(args.M, args.N, args.K);
-  if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, 1, false>(args, p.tiles, stream);
-  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false>(args, p.tiles, stream);
-  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false>(args, p.tiles, stream);
-  return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false>(args, p.tiles, stream);
+  if (args.K % kBlock) {
+    // Partial last K block: the masked kernels. The 256 x 256 one would spill with the mask's
+    // registers, so that plan runs 256 x 128 tiles instead.
+    if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, true>(args, stream);
+    if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false, true>(args, stream);
+    return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false, true>(args, stream);
+  }
+  if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, 1, false, false>(args, stream);
+  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, false>(args, stream);
+  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false, false>(args, stream);
+  return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false, false>(args, stream);
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream) {
-  const int tiles = (int)(((args.N + 255) / 256) * (args.M / 128));
-  return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true>(args, tiles, stream);
+  if (args.K % kBlock) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true, true>(args, stream);
+  return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true, false>(args, stream);
 }
 
 }  // namespace bfp8

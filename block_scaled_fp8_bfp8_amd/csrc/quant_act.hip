@@ -39,7 +39,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
                                                                   uint8_t* __restrict__ q, int64_t ldq,
                                                                   void* __restrict__ as, int64_t ld_as,
                                                                   int groups_per_row, int64_t total_groups,
-                                                                  const int32_t* __restrict__ src_rows, int src_div) {
+                                                                  const int32_t* __restrict__ src_rows, int src_div,
+                                                                  int64_t K) {
   const int sub = threadIdx.x & 15;  // which 8-element slice of the group
   const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
   const bool valid = gid < total_groups;
@@ -49,8 +50,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   const int64_t m = g_lin / groups_per_row;
   const int g = (int)(g_lin - m * groups_per_row);
   const int64_t col = (int64_t)g * kBlock + sub * 8;
+  // A partial last group (K % 128 != 0; K is a multiple of 16) has lanes past K: they load
+  // nothing, count as zeros in the amax and store nothing.
+  const bool in_k = col < K;
   int64_t src = m;
-  bool store = valid;
+  bool store = valid && in_k;
   if constexpr (kGather) {
     const int32_t p = src_rows[m];  // the same for the group's 16 lanes
     // An unwritten row is not computed: the group's lanes exchange values only among
@@ -59,8 +63,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
     src = p / src_div;
   }
 
-  float v[8];
-  if constexpr (kIn == kInBf16) {
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (!in_k) {
+  } else if constexpr (kIn == kInBf16) {
     const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -119,14 +124,14 @@ namespace {
 
 template <int kIn, bool kE8>
 void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as, int groups_per_row,
-                      int64_t total, const int32_t* src_rows, int src_div, hipStream_t stream) {
+                      int64_t total, const int32_t* src_rows, int src_div, int64_t K, hipStream_t stream) {
   const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
   if (src_rows) {
     hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, true>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div);
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
   } else {
     hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, false>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div);
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
   }
 }
 
@@ -135,17 +140,17 @@ void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void*
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream, const int32_t* src_rows,
                             int src_div) {
-  const int groups_per_row = (int)(K / kBlock);
+  const int groups_per_row = (int)((K + kBlock - 1) / kBlock);
   const int64_t total = M * groups_per_row;
   if (x_dtype == kInBf16) {
-    if (e8) launch_quant_cfg<kInBf16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
-    else launch_quant_cfg<kInBf16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    if (e8) launch_quant_cfg<kInBf16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    else launch_quant_cfg<kInBf16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
   } else if (x_dtype == kInF16) {
-    if (e8) launch_quant_cfg<kInF16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
-    else launch_quant_cfg<kInF16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    if (e8) launch_quant_cfg<kInF16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    else launch_quant_cfg<kInF16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
   } else {
-    if (e8) launch_quant_cfg<kInF32, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
-    else launch_quant_cfg<kInF32, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, stream);
+    if (e8) launch_quant_cfg<kInF32, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    else launch_quant_cfg<kInF32, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
   }
   return hipGetLastError();
 }

@@ -37,11 +37,14 @@
  *   - Alignment: every uint8 operand pointer and every row stride in bytes is
  *     a multiple of 16; float pointers are 4-byte aligned; bf16 output
  *     pointers are 2-byte aligned. Violations return BFP8_ERR_MISALIGNED.
- *   - K must be a positive multiple of 128 (the scale grid's K blocks are then
- *     whole); other K return BFP8_ERR_UNSUPPORTED.
+ *   - K must be a positive multiple of 16; other K return BFP8_ERR_UNSUPPORTED. The
+ *     scale grid has ceil(K/128) K blocks (the pages size it with ceil); when K % 128 != 0
+ *     the last block is partial. The GEMMs read operand rows in whole 128-byte blocks, so
+ *     lda and ldb must be at least K rounded up to a multiple of 128 (Kp); the bytes between
+ *     K and Kp may hold anything (they are zeroed in the kernels' registers).
  *   - Only gfx950 devices are supported (BFP8_ERR_UNSUPPORTED otherwise).
- *   - Size: M, N, K are at most 2^30, and the activation matrix ((M - 1) * lda + K
- *     bytes) and each weight matrix ((N - 1) * ldb + K bytes) span less than 4 GiB;
+ *   - Size: M, N, K are at most 2^30, and the activation matrix ((M - 1) * lda + Kp
+ *     bytes) and each weight matrix ((N - 1) * ldb + Kp bytes) span less than 4 GiB;
  *     larger requests return BFP8_ERR_UNSUPPORTED.
  *   - Determinism: for fixed inputs and sizes every result is bitwise identical
  *     from run to run (fixed reduction orders, no floating-point atomics).
@@ -58,12 +61,12 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 6
+#define BFP8_ABI_VERSION 7
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
   BFP8_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative or inconsistent size or stride */
-  BFP8_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement (K % 128, arch, dtype) */
+  BFP8_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement (K % 16, arch, dtype) */
   BFP8_ERR_MISALIGNED = 3,       /* pointer or stride alignment (see conventions) */
   BFP8_ERR_WORKSPACE = 4,        /* workspace smaller than bfp8_gemm_workspace_bytes() */
   BFP8_ERR_DEVICE = 5,           /* HIP runtime query failed */
@@ -114,10 +117,10 @@ const char* bfp8_last_error_message(void);
  *
  *   x       device, [M][ldx] elements of x_dtype, row-major; read only
  *   x_dtype BFP8_IN_F32, BFP8_IN_BF16 or BFP8_IN_F16 (the 16-bit inputs widen to float32 exactly)
- *   M, K    M >= 0, K > 0 and K % 128 == 0
+ *   M, K    M >= 0, K > 0 and K % 16 == 0 (a last group of K % 128 columns gets its own scale)
  *   ldx     >= K, elements; ldx * sizeof(element) % 16 == 0; x 16-byte aligned
  *   q       device, [M][ldq] bytes (e4m3fn codes); ldq >= K, ldq % 16 == 0; written
- *   as      device, [K/128][ld_as] float32, group-major ("column-major" scales:
+ *   as      device, [ceil(K/128)][ld_as] float32, group-major ("column-major" scales:
  *           scale of row m, group g at as[g*ld_as + m]); ld_as >= M; written
  *   stream  hipStream_t or NULL
  * x may not overlap q or as.
@@ -140,17 +143,17 @@ size_t bfp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * "vllm-project/vllm/pull/19085" (gemm_fp8_fp8_bf16_nt); page
  * "transformers/integrations/deepgemm.py" (fp8_fp4_gemm_nt((a, sfa), (b, sfb), out)).
  *
- *   C[m, n] = bf16_RNE( sum_{kb < K/128} P_kb[m,n] * as[kb*ld_as + m] * bs[(n/128)*ld_bs + kb] )
- *   P_kb[m, n] = sum_{k = 128 kb}^{128 kb + 127} e4m3(a[m*lda + k]) * e4m3(b[n*ldb + k])
+ *   C[m, n] = bf16_RNE( sum_{kb < ceil(K/128)} P_kb[m,n] * as[kb*ld_as + m] * bs[(n/128)*ld_bs + kb] )
+ *   P_kb[m, n] = sum_{k = 128 kb}^{min(128 kb + 127, K - 1)} e4m3(a[m*lda + k]) * e4m3(b[n*ldb + k])
  * Each P_kb is accumulated in FP32 by the matrix cores and promoted into an FP32
  * accumulator with the product of the two scales.
  *
- *   a      device, [M][lda] e4m3fn codes (activations), lda >= K, 16-byte aligned rows
- *   as     device, [K/128][ld_as] float32 activation scales (group-major), ld_as >= M
- *   b      device, [N][ldb] e4m3fn codes (weights, K-contiguous), ldb >= K, 16-byte aligned rows
- *   bs     device, [ceil(N/128)][ld_bs] float32 weight block scales, ld_bs >= K/128
+ *   a      device, [M][lda] e4m3fn codes (activations), lda >= Kp, 16-byte aligned rows
+ *   as     device, [ceil(K/128)][ld_as] float32 activation scales (group-major), ld_as >= M
+ *   b      device, [N][ldb] e4m3fn codes (weights, K-contiguous), ldb >= Kp, 16-byte aligned rows
+ *   bs     device, [ceil(N/128)][ld_bs] float32 weight block scales, ld_bs >= ceil(K/128)
  *   c      device, [M][ldc] bf16 bit patterns, ldc >= N; written (only columns < N)
- *   M >= 0, N >= 1, K > 0 with K % 128 == 0
+ *   M >= 0, N >= 1, K > 0 with K % 16 == 0 (Kp = K rounded up to a multiple of 128)
  *   workspace / workspace_bytes: device scratch of at least
  *          bfp8_gemm_workspace_bytes(M, N, K) bytes under the contract above (may be
  *          NULL when that is 0); BFP8_ERR_WORKSPACE if smaller

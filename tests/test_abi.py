@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 6
+    assert lib.bfp8_abi_version() == 7
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -63,6 +63,9 @@ def _gemm(lib, a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=2, c=C,
     (dict(N=0), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(K=0), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(K=200, lda=256, ldb=256), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(K=144, lda=144, ldb=256), _native.BFP8_ERR_INVALID_ARGUMENT),  # rows must hold ceil(K/128) blocks
+    (dict(K=144, lda=256, ldb=160), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=144, lda=256, ldb=256, ld_bs=1), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(M=1 << 31), _native.BFP8_ERR_UNSUPPORTED),
     (dict(a=None), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(b=None), _native.BFP8_ERR_INVALID_ARGUMENT),
@@ -132,7 +135,8 @@ def _grouped(lib, a=A, lda=256, as_=AS, ld_as=128, b=B, ldb=256, bs=BS, ld_bs=2,
     (dict(G=0), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(lay=None), _native.BFP8_ERR_INVALID_ARGUMENT),
     (dict(lay=0x60000002), _native.BFP8_ERR_MISALIGNED),
-    (dict(K=192), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(K=200), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(K=192, lda=192), _native.BFP8_ERR_INVALID_ARGUMENT),  # A rows must hold two whole blocks
     (dict(ldc=32), _native.BFP8_ERR_INVALID_ARGUMENT),
 ])
 def test_grouped_rejections(lib, kw, status):

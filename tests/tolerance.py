@@ -40,8 +40,8 @@ def abs_product_mass(a_q, a_s, b_q, b_s, rows, cols):
     b_sc = np.abs(np.asarray(b_s, np.float64)[np.asarray(cols) // 128])
     k = a_val.shape[1]
     mag = np.zeros((len(rows), len(cols)))
-    for kb in range(k // 128):
-        ks = slice(kb * 128, kb * 128 + 128)
+    for kb in range(-(-k // 128)):  # the last block may be partial
+        ks = slice(kb * 128, min(k, kb * 128 + 128))
         mag += (a_val[:, ks] @ b_val[:, ks].T) * (a_sc[:, kb][:, None] * b_sc[:, kb][None, :])
     return mag
 
@@ -56,9 +56,10 @@ def block_max_mass(a_q, a_s, b_q, b_s, rows, cols):
     a_sc = np.abs(np.asarray(a_s, np.float64)[rows])
     b_sc = np.abs(np.asarray(b_s, np.float64)[np.asarray(cols) // 128])
     out = np.zeros((len(rows), len(cols)))
-    for kb in range(a_val.shape[1] // 128):
+    k_all = a_val.shape[1]
+    for kb in range(-(-k_all // 128)):
         cur = np.zeros_like(out)
-        for k in range(kb * 128, kb * 128 + 128):
+        for k in range(kb * 128, min(k_all, kb * 128 + 128)):
             np.maximum(cur, np.outer(a_val[:, k], b_val[:, k]), out=cur)
         out += cur * (a_sc[:, kb][:, None] * b_sc[:, kb][None, :])
     return out
