@@ -569,10 +569,11 @@ def nn_to_nt_weights(w_nn: torch.Tensor, s_nn: torch.Tensor):
     e, k, n = w_nn.shape
     if tuple(s_nn.shape) != (e, -(-k // 128), -(-n // 128)):
         raise ValueError("s_nn shape does not match w_nn")
-    w = torch.empty((e, n, k), dtype=torch.uint8, device=w_nn.device)
+    kp = -(-k // 128) * 128  # rows of whole 128-byte blocks, as the GEMMs read them
+    w = torch.empty((e, n, kp), dtype=torch.uint8, device=w_nn.device)[..., :k]
     s = torch.empty((e, s_nn.shape[2], s_nn.shape[1]), dtype=torch.float32, device=w_nn.device)
     lib = _native.lib()
-    _check(lib.bfp8_transpose_weights(w_nn.data_ptr(), e, k, n, n, w.data_ptr(), k, _stream(w_nn.device)),
+    _check(lib.bfp8_transpose_weights(w_nn.data_ptr(), e, k, n, n, w.data_ptr(), kp, _stream(w_nn.device)),
            "bfp8_transpose_weights")
     _check(lib.bfp8_transpose_scales(s_nn.data_ptr(), e, s_nn.shape[1], s_nn.shape[2], s.data_ptr(),
                                      _stream(w_nn.device)), "bfp8_transpose_scales")

@@ -175,3 +175,34 @@ def test_pad_k_layout(gpu):
     assert p.shape == codes.shape and p.stride() == (5 * 256, 256, 1)
     assert torch.equal(p.cpu(), codes)
     assert bfp8.pad_k(p) is p  # already laid out so: no copy
+
+
+def test_nn_weights_partial_last_block(gpu):
+    """NN expert weights [G, K, N] with K % 128 != 0: converted into rows of whole blocks, then
+    the grouped GEMM against the oracle written on the NN operand."""
+    g, n, k = 2, 264, 464
+    ws = [workloads.weight(n, k, seed=40 + i) for i in range(g)]
+    w_nn = torch.stack([w.q.t().contiguous() for w in ws])
+    s_nn = torch.stack([w.s.t().contiguous() for w in ws])
+    announce("nn_to_nt_weights tail", tuple(w_nn.shape))
+    w_nt, s_nt = bfp8.nn_to_nt_weights(w_nn.to(gpu), s_nn.to(gpu))
+    torch.cuda.synchronize()
+    assert w_nt.stride(1) == _kp(k)
+    np.testing.assert_array_equal(w_nt.cpu().numpy(), w_nn.numpy().transpose(0, 2, 1))
+    layout = np.full(384, -1, np.int32)
+    layout[:77] = 1
+    layout[128:300] = 0
+    x = workloads.act_normal_bf16(384, k, seed=41)
+    q, s, q_ref, s_ref = _quant_nan_padded(x, gpu, "nn tail activations")
+    announce("grouped nn tail", n, k)
+    c = bfp8.grouped_gemm_contiguous(q, s, w_nt, s_nt, torch.from_numpy(layout).to(gpu))
+    torch.cuda.synchronize()
+    from oracle import bf16, gemm
+
+    rows, acc = gemm.grouped_gemm_contiguous_nn_acc_ref(q_ref, s_ref, w_nn.numpy(), s_nn.numpy(), layout)
+    got = bits(c)[rows]
+    mag = np.zeros_like(acc)
+    for e in range(g):
+        sel = layout[rows] == e
+        mag[sel] = tolerance.abs_product_mass(q_ref, s_ref, ws[e].q.numpy(), ws[e].s.numpy(), rows[sel], np.arange(n))
+    tolerance.compare(got, bf16.to_bits(acc), mag, k, "grouped nn tail")
