@@ -478,12 +478,18 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K) {
   return {128, 64, tiles(128, 64), 0};
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
-  (void)workspace;
-  const TiledPlan p = plan_tiled(args.M, args.N, args.K);
+namespace {
+
+// The tile shape a dense launch runs: the plan's, except that with a partial last K block the
+// 256 x 256 plan runs 256 x 128 tiles (its masked kernel would spill).
+TiledPlan launched_plan(int64_t M, int64_t N, int64_t K) {
+  TiledPlan p = plan_tiled(M, N, K);
+  if (K % kBlock && p.bn == 256 && p.bm == 256) p = {256, 128, (int)(((N + 255) / 256) * ((M + 127) / 128)), 0};
+  return p;
+}
+
+hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t stream) {
   if (args.K % kBlock) {
-    // Partial last K block: the masked kernels. The 256 x 256 one would spill with the mask's
-    // registers, so that plan runs 256 x 128 tiles instead.
     if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, true>(args, stream);
     if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false, true>(args, stream);
     return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false, true>(args, stream);
@@ -492,6 +498,55 @@ hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t 
   if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, false>(args, stream);
   if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false, false>(args, stream);
   return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false, false>(args, stream);
+}
+
+// Time of one round of tiles of a shape, from the FLOP rate per CU that each shape reached on
+// the N = K = 4096 sweep (one full round, launch included): 256x256 8.5, 256x128 6.3,
+// 128x128 4.9 and 128x64 3.2 TFLOP/s per CU.
+double round_us(const TiledPlan& p, int64_t K) {
+  const double rate = p.bm == 256 ? 8.5 : p.bn == 256 ? 6.3 : p.bm == 128 ? 4.9 : 3.2;
+  return 2.0 * p.bn * p.bm * (double)K / (rate * 1e6);
+}
+
+double plan_us(const TiledPlan& p, int64_t K) { return (double)((p.tiles + kCUs - 1) / kCUs) * round_us(p, K); }
+
+constexpr double kLaunchGapUs = 3.0;  // a second launch on the stream
+
+}  // namespace
+
+// Wave quantization: when the tiles fill the 256 CUs some whole number of times plus a small
+// fraction, that last round would run a few workgroups on an otherwise idle chip. The columns
+// those tiles cover then run as a second launch of the same GEMM restricted to them (B, its
+// scales, C and the bias offset by whole 128-column strips), with the tile shape the plan picks
+// for that narrower problem; each output element is computed exactly as before. The split is
+// taken only when the per-shape round times above predict a gain.
+hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  const TiledPlan p = launched_plan(args.M, args.N, args.K);
+  const int full = p.tiles / (int)kCUs, rest = p.tiles % (int)kCUs;
+  if (full >= 1 && rest > 0) {
+    const int m_tiles = (args.M + p.bm - 1) / p.bm;
+    const int n1 = (int)(full * kCUs / m_tiles) * p.bn;  // columns of the whole rounds
+    if (n1 >= p.bn && n1 < args.N) {
+      TiledPlan lead = p;
+      lead.tiles = (n1 / p.bn) * m_tiles;
+      const TiledPlan tail = launched_plan(args.M, args.N - n1, args.K);
+      if (plan_us(lead, args.K) + plan_us(tail, args.K) + kLaunchGapUs < plan_us(p, args.K)) {
+        GemmArgs a1 = args;
+        a1.N = n1;
+        GemmArgs a2 = args;
+        a2.N = args.N - n1;
+        a2.b = args.b + (int64_t)n1 * args.ldb;
+        a2.bs = static_cast<const uint8_t*>(args.bs) + (int64_t)(n1 / kBlock) * args.ld_bs * (args.e8 ? 1 : 4);
+        a2.c = args.c + n1;
+        if (args.bias) a2.bias = args.bias + n1;
+        const hipError_t e = launch_planned(a1, lead, stream);
+        if (e != hipSuccess) return e;
+        return launch_planned(a2, tail, stream);
+      }
+    }
+  }
+  return launch_planned(args, p, stream);
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
