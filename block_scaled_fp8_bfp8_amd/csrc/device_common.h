@@ -55,10 +55,11 @@ __device__ __forceinline__ int e8_code_scalar(const __attribute__((address_space
 
 // float32 -> bf16 bit pattern, round to nearest, ties to even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  // Both results are formed and one selected, so the conversion compiles without branches.
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
 }
 
 // Output element n as bf16 bits: the FP32 result rounded to bf16, then, with a bias, the
@@ -84,6 +85,21 @@ __device__ __forceinline__ float f16_value(uint32_t bits) {
 
 // Output element n as 16-bit bits: bf16 (bf16_out), or with f16 the same steps in fp16 (the
 // linear layer's output dtype follows its input: fp16(float(fp16(C)) + float(bias[n]))).
+// The same conversion with the output dtype and the bias presence fixed at compile time; the
+// bias arrives as its 16-bit pattern (loaded once per column by the caller).
+template <bool kF16, bool kBias>
+__device__ __forceinline__ uint32_t conv16(float acc, uint32_t bias_bits) {
+  if constexpr (kF16) {
+    uint32_t h = f32_to_f16_rne(acc);
+    if constexpr (kBias) h = f32_to_f16_rne(f16_value(h) + f16_value(bias_bits));
+    return h;
+  } else {
+    uint32_t b = f32_to_bf16_rne(acc);
+    if constexpr (kBias) b = f32_to_bf16_rne(__uint_as_float(b << 16) + __uint_as_float(bias_bits << 16));
+    return b;
+  }
+}
+
 __device__ __forceinline__ uint32_t out16(float acc, const uint16_t* bias, int n, bool f16) {
   if (f16) {
     uint32_t h = f32_to_f16_rne(acc);

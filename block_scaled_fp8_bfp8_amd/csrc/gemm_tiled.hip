@@ -375,7 +375,10 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   // lines. Each wave uses its own part of the stages (after the K-group sum's area), in
   // chunks of 16-row blocks that fit.
   const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
-  if (vec16) {
+  // The staged output, compiled once per output dtype and bias presence so that the
+  // per-element conversion has no branches; the bias of the lane's columns is loaded once.
+  auto staged = [&](auto f16_c, auto bias_c) {
+    constexpr bool kF16 = decltype(f16_c)::value, kBias = decltype(bias_c)::value;
     constexpr int kRowBytes = WN * 2 + 16;
     constexpr int kBase = KG == 2 ? BN * BM * 4 : 0;
     constexpr int kFitRows = (KG * STAGES * kStage - kBase) / (kWaves * kRowBytes);
@@ -385,18 +388,25 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     constexpr int kRowsPerPass = 64 / kLanesPerRow;
     static_assert(64 % kLanesPerRow == 0 && (kChunkTM * 16) % kRowsPerPass == 0, "whole passes");
     uint8_t* out_lds = &smem[0][0][0] + kBase + w * (kChunkTM * 16 * kRowBytes);
+    uint32_t bias_bits[TN][4];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int nb = n0 + wn * WN + tn * 16 + 4 * kc + e;  // clamped on tails (not stored)
+        bias_bits[tn][e] = kBias ? (uint32_t)args.bias[min(nb, N - 1)] : 0u;
+      }
 #pragma unroll
     for (int c0 = 0; c0 < TM; c0 += kChunkTM) {
 #pragma unroll
       for (int tm = c0; tm < c0 + kChunkTM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const int nb = n0 + wn * WN + tn * 16 + 4 * kc;  // bias columns, clamped on tails (not stored)
           uint2 pk;
-          pk.x = out16(acc[tn][tm][0], args.bias, min(nb, N - 1), args.out_f16) |
-                 (out16(acc[tn][tm][1], args.bias, min(nb + 1, N - 1), args.out_f16) << 16);
-          pk.y = out16(acc[tn][tm][2], args.bias, min(nb + 2, N - 1), args.out_f16) |
-                 (out16(acc[tn][tm][3], args.bias, min(nb + 3, N - 1), args.out_f16) << 16);
+          pk.x = conv16<kF16, kBias>(acc[tn][tm][0], bias_bits[tn][0]) |
+                 (conv16<kF16, kBias>(acc[tn][tm][1], bias_bits[tn][1]) << 16);
+          pk.y = conv16<kF16, kBias>(acc[tn][tm][2], bias_bits[tn][2]) |
+                 (conv16<kF16, kBias>(acc[tn][tm][3], bias_bits[tn][3]) << 16);
           *reinterpret_cast<uint2*>(out_lds + ((tm - c0) * 16 + r) * kRowBytes + (tn * 16 + 4 * kc) * 2) = pk;
         }
       // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
@@ -427,6 +437,15 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+  };
+  if (vec16) {
+    if (args.out_f16) {
+      if (args.bias) staged(std::true_type{}, std::true_type{});
+      else staged(std::true_type{}, std::false_type{});
+    } else {
+      if (args.bias) staged(std::false_type{}, std::true_type{});
+      else staged(std::false_type{}, std::false_type{});
     }
     return;
   }
