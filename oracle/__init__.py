@@ -39,6 +39,6 @@ routines, brute force with exact rationals, closed forms and invariants); none
 is "parity unpinned".
 """
 
-from . import bf16, e4m3, f16, gemm, linear, moe, quant, ue8m0  # noqa: F401
+from . import bf16, e4m3, f16, gemm, linear, moe, quant, scales, ue8m0  # noqa: F401
 
 __all__ = ["bf16", "e4m3", "f16", "gemm", "linear", "moe", "quant", "ue8m0"]
