@@ -26,7 +26,7 @@ __all__ = [
     "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
     "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
-    "moe_forward_workspace_bytes", "nn_to_nt_weights", "pad_k", "set_schedule", "get_schedule", "schedule_for",
+    "moe_forward_workspace_bytes", "nn_to_nt_weights", "pad_k", "expand_act_scales", "expand_weight_scale", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
 
@@ -578,6 +578,34 @@ def nn_to_nt_weights(w_nn: torch.Tensor, s_nn: torch.Tensor):
     _check(lib.bfp8_transpose_scales(s_nn.data_ptr(), e, s_nn.shape[1], s_nn.shape[2], s.data_ptr(),
                                      _stream(w_nn.device)), "bfp8_transpose_scales")
     return w, s
+
+
+def expand_act_scales(s: torch.Tensor, m: int, k: int) -> torch.Tensor:
+    """Block activation scales [M, ceil(K/128)] (group-major, as quant_act returns them) from one
+    per-tensor scale (a 0-d or 1-element float32 tensor) or per-token scales s [M], on s's device."""
+    _require(s, "s", torch.float32, s.dim())
+    if s.dim() > 1 or (s.numel() != m and s.numel() != 1):
+        raise ValueError(f"s must hold one scale or one per row (M = {m}), got shape {tuple(s.shape)}")
+    s = s.contiguous()
+    g = -(-k // 128)
+    out = torch.empty((g, max(m, 1)), dtype=torch.float32, device=s.device)[:, :m].t()
+    stride = 1 if s.numel() == m and m != 1 else 0
+    _check(_native.lib().bfp8_expand_act_scales(s.data_ptr(), stride, m, k, out.data_ptr(), max(m, 1),
+                                                _stream(s.device)), "bfp8_expand_act_scales")
+    return out
+
+
+def expand_weight_scale(s: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """Block weight scales [ceil(N/128), ceil(K/128)] from one per-tensor scale (float32 tensor of
+    one element), on s's device."""
+    _require(s, "s", torch.float32, s.dim())
+    if s.numel() != 1:
+        raise ValueError("a per-tensor weight scale has one element (per-channel scales have no block form)")
+    s = s.contiguous()
+    out = torch.empty((-(-n // 128), -(-k // 128)), dtype=torch.float32, device=s.device)
+    _check(_native.lib().bfp8_expand_weight_scale(s.data_ptr(), n, k, out.data_ptr(), out.stride(0),
+                                                  _stream(s.device)), "bfp8_expand_weight_scale")
+    return out
 
 
 def linear_workspace_bytes(m: int, n: int, k: int) -> int:

@@ -52,6 +52,8 @@ SIGNATURES = [
      [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     ("bfp8_transpose_weights", ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp]),
     ("bfp8_transpose_scales", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    ("bfp8_expand_act_scales", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+    ("bfp8_expand_weight_scale", ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp]),
     ("bfp8_linear_workspace_bytes", _sz, [_i64, _i64, _i64]),
     ("bfp8_linear", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),

@@ -622,6 +622,36 @@ bfp8_status_t bfp8_transpose_scales(const float* src, int64_t E, int64_t R, int6
   return launched(bfp8::launch_transpose_f32(src, E, R, C, dst, (hipStream_t)stream), "transpose_scales");
 }
 
+bfp8_status_t bfp8_expand_act_scales(const float* s, int64_t s_stride, int64_t M, int64_t K, float* as,
+                                     int64_t ld_as, void* stream) {
+  if (M < 0 || K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "M must be >= 0 and K >= 1");
+  if (s_stride < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "s_stride = %lld is negative", (long long)s_stride);
+  const int64_t G = (K + bfp8::kBlock - 1) / bfp8::kBlock;
+  if (M > kMaxDim || K > kMaxDim || M * G > ((int64_t)1 << 38)) return fail(BFP8_ERR_UNSUPPORTED, "sizes too large");
+  if (M == 0) return ok();
+  if (!s || !as) return fail(BFP8_ERR_INVALID_ARGUMENT, "s and as must not be NULL");
+  if (ld_as < M) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld", (long long)ld_as, (long long)M);
+  if (!aligned(s, 4) || !aligned(as, 4)) return fail(BFP8_ERR_MISALIGNED, "s and as must be 4-byte aligned");
+  bfp8_status_t st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_expand_act_scales(s, s_stride, M, G, as, ld_as, (hipStream_t)stream),
+                  "expand_act_scales");
+}
+
+bfp8_status_t bfp8_expand_weight_scale(const float* s, int64_t N, int64_t K, float* bs, int64_t ld_bs,
+                                       void* stream) {
+  if (N < 1 || K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N and K must be >= 1");
+  const int64_t NB = (N + bfp8::kBlock - 1) / bfp8::kBlock, KB = (K + bfp8::kBlock - 1) / bfp8::kBlock;
+  if (N > kMaxDim || K > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "N and K must each be at most 2^30");
+  if (!s || !bs) return fail(BFP8_ERR_INVALID_ARGUMENT, "s and bs must not be NULL");
+  if (ld_bs < KB) return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_bs = %lld < ceil(K/128) = %lld", (long long)ld_bs,
+                              (long long)KB);
+  if (!aligned(s, 4) || !aligned(bs, 4)) return fail(BFP8_ERR_MISALIGNED, "s and bs must be 4-byte aligned");
+  bfp8_status_t st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_fill_weight_scales(s, NB, KB, bs, ld_bs, (hipStream_t)stream), "expand_weight_scale");
+}
+
 bfp8_status_t bfp8_set_schedule(int schedule) {
   if (schedule < BFP8_SCHED_AUTO || schedule >= BFP8_SCHED_COUNT_)
     return fail(BFP8_ERR_INVALID_ARGUMENT, "unknown schedule %d", schedule);

@@ -63,6 +63,10 @@ hipError_t launch_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64
 hipError_t launch_transpose_u8(const uint8_t* src, int64_t E, int64_t K, int64_t N, int64_t ld_src, uint8_t* dst,
                                int64_t ld_dst, hipStream_t stream);
 hipError_t launch_transpose_f32(const float* src, int64_t E, int64_t R, int64_t C, float* dst, hipStream_t stream);
+hipError_t launch_expand_act_scales(const float* s, int64_t s_stride, int64_t M, int64_t G, float* as, int64_t ld_as,
+                                    hipStream_t stream);
+hipError_t launch_fill_weight_scales(const float* s, int64_t NB, int64_t KB, float* bs, int64_t ld_bs,
+                                     hipStream_t stream);
 hipError_t launch_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair, const float* w, int64_t T,
                               int top_k, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream);
 

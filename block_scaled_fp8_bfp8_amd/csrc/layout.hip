@@ -7,6 +7,11 @@
 // conversion is a plain tiled transpose through LDS: a workgroup reads a 64 x 64 byte tile
 // along N (coalesced), and writes it along K (coalesced). The block scales [E, K/128, N/128]
 // are transposed the same way, element by element.
+//
+// Scale granularity: page "vllm/pull/19085" (review thread) runs FP8 models quantized per
+// tensor on the block kernel by expanding their scales to the block shape. A per-tensor or
+// per-token scale is constant over every activation group and weight block, so the expansion
+// (a broadcast into the grids the GEMMs read) is exact.
 #include "device_common.h"
 #include "launch.h"
 
@@ -53,7 +58,42 @@ __global__ __launch_bounds__(256) void transpose_f32_kernel(const float* __restr
   dst[i] = src[e * R * C + r * C + c];
 }
 
+// as[g * ld_as + m] = s[m * s_stride] for m < M, g < G (group-major activation scales).
+__global__ __launch_bounds__(256) void expand_act_scales_kernel(const float* __restrict__ s, int64_t s_stride,
+                                                                int64_t M, int64_t G, float* __restrict__ as,
+                                                                int64_t ld_as) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * G) return;
+  const int64_t g = i / M, m = i - g * M;
+  as[g * ld_as + m] = s[m * s_stride];
+}
+
+// bs[j * ld_bs + kb] = s[0] for j < NB, kb < KB (one scale for the whole weight).
+__global__ __launch_bounds__(256) void fill_weight_scales_kernel(const float* __restrict__ s, int64_t NB, int64_t KB,
+                                                                 float* __restrict__ bs, int64_t ld_bs) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= NB * KB) return;
+  const int64_t j = i / KB, kb = i - j * KB;
+  bs[j * ld_bs + kb] = s[0];
+}
+
 }  // namespace
+
+hipError_t launch_expand_act_scales(const float* s, int64_t s_stride, int64_t M, int64_t G, float* as, int64_t ld_as,
+                                    hipStream_t stream) {
+  const int64_t total = M * G;
+  hipLaunchKernelGGL(expand_act_scales_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, s,
+                     s_stride, M, G, as, ld_as);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_weight_scales(const float* s, int64_t NB, int64_t KB, float* bs, int64_t ld_bs,
+                                     hipStream_t stream) {
+  const int64_t total = NB * KB;
+  hipLaunchKernelGGL(fill_weight_scales_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, s, NB,
+                     KB, bs, ld_bs);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_u8(const uint8_t* src, int64_t E, int64_t K, int64_t N, int64_t ld_src, uint8_t* dst,
                                int64_t ld_dst, hipStream_t stream) {

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 7
+#define BFP8_ABI_VERSION 8
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -349,6 +349,26 @@ bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int
 bfp8_status_t bfp8_transpose_weights(const uint8_t* src, int64_t E, int64_t K, int64_t N, int64_t ld_src,
                                      uint8_t* dst, int64_t ld_dst, void* stream);
 bfp8_status_t bfp8_transpose_scales(const float* src, int64_t E, int64_t R, int64_t C, float* dst, void* stream);
+
+/*
+ * Coarser scales on the block kernels (page "vllm/pull/19085", the review thread on models
+ * quantized per tensor: their scales are expanded to the block shape). A per-tensor or
+ * per-token scale is constant over every 1x128 activation group and 128x128 weight block, so
+ * the GEMMs on the expanded grids compute the per-tensor / per-token FP8 product exactly as
+ * defined: C[m][n] = bf16(s_a[m] * s_b * sum_k A[m][k] B[n][k]). A per-output-channel weight
+ * scale changes inside a 128-row block and has no block form (not offered).
+ *   bfp8_expand_act_scales:   as[g * ld_as + m] = s[m * s_stride] for m < M, g < ceil(K/128):
+ *                             s_stride 1 for per-token scales s[M], 0 for one per-tensor scale.
+ *                             as is the group-major grid bfp8_gemm reads (ld_as >= M).
+ *   bfp8_expand_weight_scale: bs[j * ld_bs + kb] = s[0] for j < ceil(N/128), kb < ceil(K/128)
+ *                             (ld_bs >= ceil(K/128)).
+ * s, as and bs are device float32 arrays, 4-byte aligned; M = 0 is a no-op. Errors: as for the
+ * calls above; the expansion runs on stream, ordered with the GEMMs that read it.
+ */
+bfp8_status_t bfp8_expand_act_scales(const float* s, int64_t s_stride, int64_t M, int64_t K, float* as,
+                                     int64_t ld_as, void* stream);
+bfp8_status_t bfp8_expand_weight_scale(const float* s, int64_t N, int64_t K, float* bs, int64_t ld_bs,
+                                       void* stream);
 
 /* Process-wide schedule override for bfp8_gemm (tests and benchmarks):
  * BFP8_SCHED_AUTO restores the automatic choice. Returns BFP8_ERR_INVALID_ARGUMENT

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 7
+    assert lib.bfp8_abi_version() == 8
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -254,3 +254,30 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(s_stride=-1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ld_as=3), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(s=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(as_=AS + 2), _native.BFP8_ERR_MISALIGNED),
+])
+def test_expand_act_scales_rejections(lib, kw, status):
+    a = dict(s=BS, s_stride=1, M=4, K=256, as_=AS, ld_as=4)
+    a.update(kw)
+    assert lib.bfp8_expand_act_scales(a["s"], a["s_stride"], a["M"], a["K"], a["as_"], a["ld_as"], None) == status
+    assert lib.bfp8_expand_act_scales(BS, 1, 0, 256, None, 0, None) == _native.BFP8_OK  # M = 0: no-op
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(ld_bs=1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(bs=None), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(s=BS + 1), _native.BFP8_ERR_MISALIGNED),
+])
+def test_expand_weight_scale_rejections(lib, kw, status):
+    a = dict(s=BS, N=300, K=256, bs=AS, ld_bs=2)
+    a.update(kw)
+    assert lib.bfp8_expand_weight_scale(a["s"], a["N"], a["K"], a["bs"], a["ld_bs"], None) == status
