@@ -141,10 +141,16 @@ struct LinearLayout {
 };
 LinearLayout linear_layout(int64_t M, int64_t N, int64_t K);
 
-int choose_schedule(int64_t M, int64_t /*N*/, int64_t /*K*/) {
+// Schedule by shape (the M ranges of page "lmdeploy/pull/4830", section "Kernel design",
+// decided here by predicted time): above kSmallMaxM rows the tiled schedule; below, the
+// K-split one unless the tiled one is predicted at least 10 % faster. That happens for wide
+// weights at M of 64 and more (the hidden-5120 gate+up projection, N = 51200: 2.2x at M = 128),
+// where the K-split copies re-read every weight strip once per 32 or 64 activation rows.
+int choose_schedule(int64_t M, int64_t N, int64_t K) {
   const int forced = g_schedule.load(std::memory_order_relaxed);
   if (forced != BFP8_SCHED_AUTO) return forced;
-  return M <= bfp8::kSmallMaxM ? BFP8_SCHED_SMALL_M : BFP8_SCHED_TILED;
+  if (M > bfp8::kSmallMaxM) return BFP8_SCHED_TILED;
+  return bfp8::tiled_time_us(M, N, K) < 0.9 * bfp8::ksplit_time_us(M, N, K) ? BFP8_SCHED_TILED : BFP8_SCHED_SMALL_M;
 }
 
 }  // namespace

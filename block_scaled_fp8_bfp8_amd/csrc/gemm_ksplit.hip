@@ -28,6 +28,7 @@
 //     rounded once to bf16;
 //   * UE8M0 scales (kE8): the scale codes are copied like the float scales, and the scaled
 //     MFMA applies 2^(ea - 127) * 2^(eb - 127) and accumulates into the wave's tile itself.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -245,6 +246,26 @@ hipError_t launch_ksplit_cfg(const GemmArgs& args, hipStream_t stream) {
 // Tile per M, measured on the N = K = 4096 sweep (cold weights): 16x16 up to M = 16 (two
 // slots per wave), 16x32 and 32x32 up to 32 and 64, then 64x32 and 64x64 (one slot per
 // wave). Every choice gives 256 or more workgroups at N = 4096.
+namespace {
+void ksplit_tile(int64_t M, int& bn, int& bm) {
+  bn = M <= 32 ? 16 : M <= 128 ? (M <= 64 ? 32 : 64) : 64;
+  bm = M <= 16 ? 16 : M <= 128 ? 32 : 64;
+}
+}  // namespace
+
+// Every workgroup copies its BN weight rows and its activation rows (at most M distinct ones)
+// of every K block from L2 into LDS; measured across the transformer and N = K = 4096 shapes,
+// those copies run at about 9.5 TB/s in aggregate, the weights stream from HBM at about
+// 5.5 TB/s, and a launch adds about 3.5 us.
+double ksplit_time_us(int64_t M, int64_t N, int64_t K) {
+  int bn, bm;
+  ksplit_tile(M, bn, bm);
+  const double tiles = (double)((N + bn - 1) / bn) * (double)((M + bm - 1) / bm);
+  const double copied = tiles * (double)(bn + (M < bm ? M : bm)) * (double)K;
+  const double weights = (double)N * (double)K;
+  return std::max(copied / 9.5e6, weights / 5.5e6) + 3.5;
+}
+
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream) {
   if (args.M <= 16) return launch_ksplit_cfg<1, 1, 8, 2>(args, stream);
   if (args.M <= 32) return launch_ksplit_cfg<1, 2, 8, 2>(args, stream);

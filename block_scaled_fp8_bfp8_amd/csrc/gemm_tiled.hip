@@ -39,6 +39,12 @@
 #include "device_common.h"
 #include "launch.h"
 
+#ifndef S64
+#define S64 4
+#endif
+#ifndef S128
+#define S128 4
+#endif
 namespace bfp8 {
 
 namespace {
@@ -228,19 +234,40 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   // t = tm * TN + tn multiplies weight fragment tn by activation fragment tm. Block kb is
   // multiplied out of registers while block kb + 1 is read from LDS into the same registers,
   // each fragment right after its last use in block kb (activation fragment tm after row tm,
-  // weight fragment tn in the last row). LDS stage kb % STAGES is free once block kb has been
-  // read (the barrier ending iteration kb - 1), so iteration kb refills it with block
-  // kb + STAGES, one copy per step, and waits at its end for block kb + 2,
-  // which iteration kb + 1 reads.
+  // weight fragment tn in the last row). The promotion of a sub-tile lags its MFMA by two
+  // steps. Where the workgroup barrier goes depends on the tile (kMid):
+  //   * mid-block (tiles below 256 x 256): the barrier of iteration kb sits at step TN - 1,
+  //     just before the first read of block kb + 1, so its first steps multiply fragments
+  //     already in registers while the previous iteration's last LDS reads return and late
+  //     waves catch up. Past it, block kb + 1 has landed (every wave waited for its own copies
+  //     of it first) and every wave has finished reading block kb (read during iteration
+  //     kb - 1), so stage kb % STAGES is refilled with block kb + STAGES, one copy per step
+  //     from the barrier on. The promotions lag across blocks too: the first two steps of
+  //     block kb promote the last two sub-tiles of block kb - 1 with that block's scale;
+  //   * end of block (256 x 256, whose registers cannot keep those promotions live across the
+  //     barrier): iteration kb refills stage kb % STAGES from its first step (the barrier
+  //     that ended iteration kb - 1 follows every read of block kb), promotes its last two
+  //     sub-tiles at its end, waits for block kb + 2, which iteration kb + 1 reads, and ends
+  //     with the barrier.
   v8i fa[TM];
   v8i fb[TN];
   ScaleT sa[TM];
   ScaleT bsv;
   constexpr int kSteps = TN * TM;
+  constexpr bool kMid = BN * BM < 256 * 256;
+  constexpr bool kCarry = kMid;
+  constexpr int kBarStep = kMid ? TN - 1 : -1;
+  static_assert(TM >= 2 && TN >= 2, "the barrier step precedes every read of the next block");
+  // Copy j of a refill goes out at step kFirstCopy + j, or spread over the remaining steps
+  // when there are fewer of them than copies.
+  constexpr int kFirstCopy = kMid ? kBarStep : 0;
+  constexpr int kCopySpan = kSteps - kFirstCopy;
+  auto copy_step = [](int j) constexpr { return kFirstCopy + (kCopies <= kCopySpan ? j : j * kCopySpan / kCopies); };
 
-  // Copies issued per wave per K block; the wait for block kb + 2 at the end of iteration kb
-  // may leave the copies of blocks kb + 3 .. kb + STAGES in flight (waits take immediates).
-  auto wait_block_after_next = [&](bool steady) __attribute__((always_inline)) {
+  // Copies issued per wave per K block. At the mid-block barrier of iteration kb block kb + 1
+  // must have landed, at the end-of-block barrier block kb + 2: either way the copies of the
+  // STAGES - 2 most recently issued blocks may stay in flight (waits take immediates).
+  auto wait_next_block = [&](bool steady) __attribute__((always_inline)) {
     if (!steady || STAGES == 2) {
       wait_copies();
     } else if (copies_as) {
@@ -248,6 +275,23 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     } else {
       wait_copies_upto<(STAGES - 2) * kCopies>();
     }
+  };
+
+  float sc[TM];  // scale products As * Bs of the block's activation rows
+  if constexpr (kCarry) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) sc[tm] = 0.f;
+  }
+  // kMid: the last two MFMA results of the previous block (zero before the first block:
+  // promoting them then adds 0 * 0 to a zero accumulator).
+  v4f p1c = {0.f, 0.f, 0.f, 0.f}, p2c = p1c;
+  auto promote = [&](int u, const v4f& pu, float s) __attribute__((always_inline)) {
+    const int um = u / TN, un = u % TN;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], s, acc[un][um][e]);
+    // Pin the promotion here: otherwise the FMAs are sunk past the loop's branch,
+    // since their results are only read in the next K block.
+    asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
   };
 
   auto iter = [&](int kb, auto steady_c) __attribute__((always_inline)) {
@@ -259,26 +303,22 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     const uint8_t* nstage = &smem[g][nslot][0];
     const bool mask_next = kTail && kb + 1 < KB && gkb(kb + 1) == KB_all - 1;  // uniform
     const ScaleT bs_next = weight_scale(gkb(min(kb + 1, KB - 1)));
-    float sc[TM];
-    if constexpr (!kE8) {
+    // With kMid the scale products live across blocks; otherwise they are this block's alone.
+    float sc_block[TM];
+    float* const scp = kCarry ? sc : sc_block;
+    if constexpr (!kE8 && !kCarry) {
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sc[tm] = sa[tm] * bsv;
+      for (int tm = 0; tm < TM; ++tm) scp[tm] = sa[tm] * bsv;
     }
-    if constexpr (kSteady) issue_scales(cslot, kb + STAGES);
-    // Step t issues the MFMA of sub-tile t, the promotion FMAs of sub-tile t - 2 (whose
-    // result is then at least one MFMA old), its share of the copies and of the next block's
-    // LDS reads; a scheduling barrier per step keeps this order. Copies go out one per step
-    // from the first, so that they have most of the iteration to land.
-    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;
-    auto promote = [&](int u, const v4f& pu) __attribute__((always_inline)) {
-      const int um = u / TN, un = u % TN;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], sc[um], acc[un][um][e]);
-      // Pin the promotion here: otherwise the FMAs are sunk past the loop's branch,
-      // since their results are only read in the next K block.
-      asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
-    };
-    constexpr int kCopySteps = kCopies;  // one copy per step from the first (kCopies <= kSteps)
+    if constexpr (kSteady && !kMid) issue_scales(cslot, kb + STAGES);
+    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;  // MFMA results of the previous two steps
+    if constexpr (kCarry) {
+      p1 = p1c;
+      p2 = p2c;
+    }
+    // Step t issues the MFMA of sub-tile t, the promotion FMAs of the sub-tile two steps back
+    // (its result is then at least one MFMA old), its share of the copies and of the next
+    // block's LDS reads; a scheduling barrier per step keeps this order.
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
       const int tm = t / TN, tn = t % TN;
@@ -290,13 +330,27 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[tn][tm][e] = nxt[e];
       } else {
+        // The scale product of row tm is formed at the row's first step, while sa[tm] still
+        // holds this block's activation scale (the row's last step reloads it). Until then
+        // sc[TM - 1] keeps the previous block's, which its two lagging promotions use (the
+        // last two steps of a block lie in its last row, since TN >= 2).
+        if (kCarry && tn == 0) scp[tm] = sa[tm] * bsv;
         p = mfma_block(fb[tn], fa[tm]);
-        if (t >= 2) promote(t - 2, p2);
+        if (t >= 2) {
+          promote(t - 2, p2, scp[(t - 2) / TN]);
+        } else if constexpr (kCarry) {
+          promote(kSteps - 2 + t, p2, scp[TM - 1]);
+        }
+      }
+      if (kMid && t == kBarStep) {
+        wait_next_block(kSteady);
+        lds_barrier();
+        if constexpr (kSteady) issue_scales(cslot, kb + STAGES);
       }
       if constexpr (kSteady) {
 #pragma unroll
         for (int j = 0; j < kCopies; ++j)
-          if (t == j * kCopySteps / kCopies) issue_piece(cslot, kb + STAGES, j);
+          if (t == copy_step(j)) issue_piece(cslot, kb + STAGES, j);
       }
       if (tn == TN - 1) {
         fa[tm] = frag_a(nstage, tm);
@@ -313,21 +367,34 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
         p1 = p;
       }
     }
-    if constexpr (!kE8) {
-      promote(kSteps - 2, p2);
-      promote(kSteps - 1, p1);
+    if constexpr (!kE8 && !kCarry) {
+      promote(kSteps - 2, p2, scp[TM - 1]);
+      promote(kSteps - 1, p1, scp[TM - 1]);
+    }
+    if constexpr (kCarry) {
+      p1c = p1;
+      p2c = p2;
     }
     bsv = bs_next;
-    // Block kb + 2 is in LDS once every wave's copies of it have landed; the barrier also
-    // orders this iteration's reads of stage (kb + 1) % STAGES before its refill.
-    wait_block_after_next(kSteady);
-    lds_barrier();
+    if constexpr (!kMid) {
+      wait_next_block(kSteady);
+      lds_barrier();
+    }
   };
 
 #pragma unroll
   for (int i = 0; i < STAGES; ++i) issue_copies(i, min(i, KB - 1));
-  // blocks 0 and 1 have landed once the copies of blocks 2 .. STAGES-1 are the only ones left
-  wait_block_after_next(STAGES <= KB);
+  if constexpr (kMid) {
+    // block 0 has landed once the copies of blocks 1 .. STAGES-1 are the only ones left
+    if (copies_as) {
+      wait_copies_upto<(STAGES - 1) * (kCopies + 1)>();
+    } else {
+      wait_copies_upto<(STAGES - 1) * kCopies>();
+    }
+  } else {
+    // blocks 0 and 1 have landed once the copies of blocks 2 .. STAGES-1 are the only ones left
+    wait_next_block(STAGES <= KB);
+  }
   lds_barrier();
   const bool mask_first = kTail && gkb(0) == KB_all - 1;
 #pragma unroll
@@ -342,11 +409,22 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     if (mask_first) fb[tn] = mask_k_tail(fb[tn], k_tail, kc);
   }
   bsv = weight_scale(g);
-  // every wave has read stage 0 before iteration 0 refills it
-  lds_barrier();
+  // every wave has read stage 0 before iteration 0 refills it (with kMid, the refill follows
+  // the barrier of iteration 0 instead)
+  if constexpr (!kMid) lds_barrier();
   int kb = 0;
   for (; kb + STAGES < KB; ++kb) iter(kb, std::true_type{});
   for (; kb < KB; ++kb) iter(kb, std::false_type{});
+  if constexpr (kMid) {
+    if constexpr (!kE8 && kCarry) {
+      promote(kSteps - 2, p2c, sc[TM - 1]);
+      promote(kSteps - 1, p1c, sc[TM - 1]);
+    }
+    // Every wave's LDS reads (the last iteration's stale ones included) are done before the
+    // stages are reused below (the end-of-block barrier already covers them).
+    lds_barrier();
+  }
+  // No copy is in flight: the last iteration waited for all of them.
 
   if constexpr (KG == 2) {
     // Sum of the two groups' tiles, group 0 + group 1: group 1 parks its tile in the stages
@@ -515,8 +593,8 @@ hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t 
   }
   if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, 1, false, false>(args, stream);
   if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, false>(args, stream);
-  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false, false>(args, stream);
-  return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false, false>(args, stream);
+  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, S128, 1, false, false>(args, stream);
+  return launch_tiled_cfg<128, 64, 2, 2, S64, 1, false, false>(args, stream);
 }
 
 // Time of one round of tiles of a shape, from the FLOP rate per CU that each shape reached on
@@ -532,6 +610,13 @@ double plan_us(const TiledPlan& p, int64_t K) { return (double)((p.tiles + kCUs 
 constexpr double kLaunchGapUs = 3.0;  // a second launch on the stream
 
 }  // namespace
+
+// The launch plan's rounds at the measured per-CU rates, or, where the operands take longer to
+// stream from HBM (about 5.5 TB/s, plus 3.5 us for the launch), that.
+double tiled_time_us(int64_t M, int64_t N, int64_t K) {
+  const double stream_us = ((double)N * (double)K + (double)M * (double)K) / 5.5e6 + 3.5;
+  return std::max(plan_us(launched_plan(M, N, K), K), stream_us);
+}
 
 // Wave quantization: when the tiles fill the 256 CUs some whole number of times plus a small
 // fraction, that last round would run a few workgroups on an otherwise idle chip. The columns

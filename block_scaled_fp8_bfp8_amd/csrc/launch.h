@@ -70,9 +70,14 @@ hipError_t launch_fill_weight_scales(const float* s, int64_t NB, int64_t KB, flo
 hipError_t launch_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair, const float* w, int64_t T,
                               int top_k, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream);
 
-// Largest M the automatic choice gives to the K-split schedule (BFP8_SCHED_SMALL_M); the
-// tiled schedule takes larger M.
+// Largest M the K-split schedule (BFP8_SCHED_SMALL_M) takes; the tiled schedule takes larger M
+// always, and smaller M where its predicted time is clearly lower.
 constexpr int kSmallMaxM = 256;
+
+// Predicted time in microseconds of one dense GEMM under each schedule (host arithmetic only),
+// from rates measured on MI355X; the automatic schedule choice compares them.
+double ksplit_time_us(int64_t M, int64_t N, int64_t K);
+double tiled_time_us(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream);

@@ -155,6 +155,23 @@ def test_schedule_override(lib):
         lib.bfp8_set_schedule(0)
 
 
+def test_schedule_by_shape(lib):
+    """Automatic choice: K-split at small M on the square and hidden-5120 down/o_proj weights; the
+    tiled schedule above 256 rows, and at M >= 64 on the 51200-wide gate+up weight, where its
+    predicted time is far lower (the K-split re-reads each weight strip per 32-64 rows)."""
+    small, tiled = 1, 2
+    for m in (1, 16, 64, 128, 256):
+        assert lib.bfp8_gemm_schedule_for(m, 4096, 4096) == small
+        assert lib.bfp8_gemm_schedule_for(m, 5120, 25600) == small
+        assert lib.bfp8_gemm_schedule_for(m, 5120, 8192) == small
+    for m in (1, 16):
+        assert lib.bfp8_gemm_schedule_for(m, 51200, 5120) == small
+    for m in (64, 128, 256):
+        assert lib.bfp8_gemm_schedule_for(m, 51200, 5120) == tiled
+    for n, k in ((4096, 4096), (576, 7168), (51200, 5120)):
+        assert lib.bfp8_gemm_schedule_for(257, n, k) == tiled
+
+
 def _linear(lib, x=A, dt=1, M=8, K=256, ldx=256, b=B, ldb=256, bs=BS, ld_bs=2, bias=None, c=C, ldc=64, N=64,
             ws=0x70000000, wsb=None):
     if wsb is None:
