@@ -112,6 +112,27 @@ def test_square_with_bias_sampled_rows(gpu, m):
     print(tolerance.compare_linear(bits(got)[rows], out_ref, c_ref, mag, k, f"linear square M={m}"))
 
 
+@pytest.mark.parametrize("m", [64, 128])
+def test_wide_gate_up_weight_sampled_rows(gpu, m):
+    """The hidden-5120 gate+up projection (N = 51200, K = 5120), where the automatic choice
+    takes the tiled schedule below 256 rows; sampled rows against the oracle."""
+    n, k = 51200, 5120
+    if "wide" not in _square:
+        w = workloads.weight(n, k, seed=12)
+        _square["wide"] = (w, w.q.to(gpu), w.s.to(gpu))
+    w, wq, ws = _square["wide"]
+    assert bfp8.schedule_for(m, n, k) == "tiled"
+    x = workloads.act_normal_bf16(m, k, seed=80 + m)
+    bias = _bf16_spread(np.random.default_rng(m + 1), (n,), -6, 3)
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).choice(m, 6, replace=False)]))
+    out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy(), rows=rows)
+    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
+    announce("linear wide", m, n, k, "->", bfp8.schedule_for(m, n, k))
+    got = bfp8.linear(x.to(gpu), wq, ws, bias.to(gpu))
+    torch.cuda.synchronize()
+    print(tolerance.compare_linear(bits(got)[rows], out_ref, c_ref, mag, k, f"linear wide M={m}"))
+
+
 def test_without_bias_equals_quantize_then_gemm(gpu):
     """The fused layer is the two entry points back to back: same bits, both schedules."""
     n, k = 1000, 1536
