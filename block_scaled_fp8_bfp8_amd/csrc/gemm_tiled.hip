@@ -239,17 +239,16 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   //     from the barrier on. The promotions lag across blocks too: the first two steps of
   //     block kb promote the last two sub-tiles of block kb - 1 with that block's scale;
   //   * end of block (256 x 256, whose registers cannot keep those promotions live across the
-  //     barrier): iteration kb refills stage kb % STAGES from its first step (the barrier
-  //     that ended iteration kb - 1 follows every read of block kb), promotes its last two
-  //     sub-tiles at its end, waits for block kb + 2, which iteration kb + 1 reads, and ends
-  //     with the barrier.
+  //     barrier): iteration kb refills stage kb % STAGES from its first step on, one copy
+  //     every three steps (the barrier that ended iteration kb - 1 follows every read of
+  //     block kb), promotes its last two sub-tiles at its end, waits for block kb + 2, which
+  //     iteration kb + 1 reads, and ends with the barrier.
   v8i fa[TM];
   v8i fb[TN];
   ScaleT sa[TM];
   ScaleT bsv;
   constexpr int kSteps = TN * TM;
   constexpr bool kMid = BN * BM < 256 * 256;
-  constexpr bool kCarry = kMid;
   constexpr int kBarStep = kMid ? TN - 1 : -1;
   static_assert(TM >= 2 && TN >= 2, "the barrier step precedes every read of the next block");
   // Copy j of a refill goes out at step kFirstCopy + j * kCopyStride, or spread over the
@@ -278,7 +277,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   };
 
   float sc[TM];  // scale products As * Bs of the block's activation rows
-  if constexpr (kCarry) {
+  if constexpr (kMid) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) sc[tm] = 0.f;
   }
@@ -305,14 +304,14 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     const ScaleT bs_next = weight_scale(gkb(min(kb + 1, KB - 1)));
     // With kMid the scale products live across blocks; otherwise they are this block's alone.
     float sc_block[TM];
-    float* const scp = kCarry ? sc : sc_block;
-    if constexpr (!kE8 && !kCarry) {
+    float* const scp = kMid ? sc : sc_block;
+    if constexpr (!kE8 && !kMid) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) scp[tm] = sa[tm] * bsv;
     }
     if constexpr (kSteady && !kMid) issue_scales(cslot, kb + STAGES);
     v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;  // MFMA results of the previous two steps
-    if constexpr (kCarry) {
+    if constexpr (kMid) {
       p1 = p1c;
       p2 = p2c;
     }
@@ -334,11 +333,11 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
         // holds this block's activation scale (the row's last step reloads it). Until then
         // sc[TM - 1] keeps the previous block's, which its two lagging promotions use (the
         // last two steps of a block lie in its last row, since TN >= 2).
-        if (kCarry && tn == 0) scp[tm] = sa[tm] * bsv;
+        if (kMid && tn == 0) scp[tm] = sa[tm] * bsv;
         p = mfma_block(fb[tn], fa[tm]);
         if (t >= 2) {
           promote(t - 2, p2, scp[(t - 2) / TN]);
-        } else if constexpr (kCarry) {
+        } else if constexpr (kMid) {
           promote(kSteps - 2 + t, p2, scp[TM - 1]);
         }
       }
@@ -367,11 +366,11 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
         p1 = p;
       }
     }
-    if constexpr (!kE8 && !kCarry) {
+    if constexpr (!kE8 && !kMid) {
       promote(kSteps - 2, p2, scp[TM - 1]);
       promote(kSteps - 1, p1, scp[TM - 1]);
     }
-    if constexpr (kCarry) {
+    if constexpr (kMid) {
       p1c = p1;
       p2c = p2;
     }
@@ -416,7 +415,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   for (; kb + STAGES < KB; ++kb) iter(kb, std::true_type{});
   for (; kb < KB; ++kb) iter(kb, std::false_type{});
   if constexpr (kMid) {
-    if constexpr (!kE8 && kCarry) {
+    if constexpr (!kE8 && kMid) {
       promote(kSteps - 2, p2c, sc[TM - 1]);
       promote(kSteps - 1, p1c, sc[TM - 1]);
     }
