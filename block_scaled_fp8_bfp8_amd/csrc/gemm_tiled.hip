@@ -559,13 +559,23 @@ hipError_t launch_tiled_cfg(const GemmArgs& args, hipStream_t stream) {
 
 constexpr int64_t kCUs = 256;  // workgroups that fill MI355X once
 
+// Time of one round of tiles of a shape, from the FLOP rate per CU that each shape reached on
+// the N = K = 4096 sweep (one full round, launch included): 256x256 8.5, 256x128 6.3,
+// 128x128 4.9 and 128x64 3.2 TFLOP/s per CU.
+double round_us(const TiledPlan& p, int64_t K) {
+  const double rate = p.bm == 256 ? 8.5 : p.bn == 256 ? 6.3 : p.bm == 128 ? 4.9 : 3.2;
+  return 2.0 * p.bn * p.bm * (double)K / (rate * 1e6);
+}
+
+double plan_us(const TiledPlan& p, int64_t K) { return (double)((p.tiles + kCUs - 1) / kCUs) * round_us(p, K); }
+
 }  // namespace
 
-// Tile shape: the largest that still gives every CU a workgroup, which trades bytes copied
-// per MFMA (fewer with big tiles) against parallelism. Measured on the N = K = 4096 sweep:
-// 256x256 from M = 4096 (8 waves of 128x64, two LDS stages), 256x128 at M = 2048 (three
-// stages), 128x128 at M = 1024 and 128x64 below (4 waves of 64x64 or 64x32, four stages: the
-// fourth took M = 512 from 20.1 to 18.2 us).
+// Base tile shape: the largest that still gives every CU a workgroup, which trades bytes copied
+// per MFMA (fewer with big tiles) against parallelism. On the N = K = 4096 sweep: 256x256 from
+// M = 4096 (8 waves of 128x64, two LDS stages), 256x128 at M = 2048 (three stages), 128x128 at
+// M = 1024 and 128x64 at M = 512 (8 waves of 64x32 or 32x32, four stages: the fourth stage took
+// M = 512 from 20.1 to 18.2 us, and 8 waves instead of 4 a further 3-6 % at M = 512-1536).
 TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K) {
   (void)K;
   auto tiles = [&](int bn, int bm) { return (int)(((N + bn - 1) / bn) * ((M + bm - 1) / bm)); };
@@ -579,10 +589,22 @@ namespace {
 
 // The tile shape a dense launch runs: the plan's, except that with a partial last K block the
 // 256 x 256 plan runs 256 x 128 tiles (its masked kernel would spill).
-TiledPlan launched_plan(int64_t M, int64_t N, int64_t K) {
-  TiledPlan p = plan_tiled(M, N, K);
+TiledPlan no_masked_256(TiledPlan p, int64_t M, int64_t N, int64_t K) {
   if (K % kBlock && p.bn == 256 && p.bm == 256) p = {256, 128, (int)(((N + 255) / 256) * ((M + 127) / 128)), 0};
   return p;
+}
+TiledPlan launched_plan(int64_t M, int64_t N, int64_t K) { return no_masked_256(plan_tiled(M, N, K), M, N, K); }
+
+// The shape whose rounds take the least predicted time (the larger tile on a tie).
+TiledPlan min_time_plan(int64_t M, int64_t N, int64_t K) {
+  auto plan = [&](int bn, int bm) {
+    return no_masked_256(TiledPlan{bn, bm, (int)(((N + bn - 1) / bn) * ((M + bm - 1) / bm)), 0}, M, N, K);
+  };
+  const TiledPlan shapes[] = {plan(256, 256), plan(256, 128), plan(128, 128), plan(128, 64)};
+  TiledPlan best = shapes[0];
+  for (const TiledPlan& p : shapes)
+    if (plan_us(p, K) < plan_us(best, K)) best = p;
+  return best;
 }
 
 hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t stream) {
@@ -593,64 +615,82 @@ hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t 
   }
   if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, 1, false, false>(args, stream);
   if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, false>(args, stream);
-  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 4, 1, false, false>(args, stream);
-  return launch_tiled_cfg<128, 64, 2, 2, 4, 1, false, false>(args, stream);
+  if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 4, 4, 1, false, false>(args, stream);
+  return launch_tiled_cfg<128, 64, 4, 2, 4, 1, false, false>(args, stream);
 }
-
-// Time of one round of tiles of a shape, from the FLOP rate per CU that each shape reached on
-// the N = K = 4096 sweep (one full round, launch included): 256x256 8.5, 256x128 6.3,
-// 128x128 4.9 and 128x64 3.2 TFLOP/s per CU.
-double round_us(const TiledPlan& p, int64_t K) {
-  const double rate = p.bm == 256 ? 8.5 : p.bn == 256 ? 6.3 : p.bm == 128 ? 4.9 : 3.2;
-  return 2.0 * p.bn * p.bm * (double)K / (rate * 1e6);
-}
-
-double plan_us(const TiledPlan& p, int64_t K) { return (double)((p.tiles + kCUs - 1) / kCUs) * round_us(p, K); }
 
 constexpr double kLaunchGapUs = 3.0;  // a second launch on the stream
 
+// What a dense GEMM launches: one plan over all N columns, or (n1 > 0) `lead` over the columns
+// [0, n1) and `tail` over the rest, with the predicted time.
+struct TiledLaunch {
+  TiledPlan lead;
+  int n1;
+  TiledPlan tail;
+  double us;
+};
+
+// Wave quantization: when the base plan's tiles fill the 256 CUs some whole number of times plus
+// a fraction, that last round runs a few workgroups on an otherwise idle chip. Two remedies,
+// each taken only when the per-shape round times predict a gain:
+//   * split: the columns of the whole rounds run with the base plan, the remaining columns as a
+//     second launch of the same GEMM restricted to them (B, its scales, C and the bias offset by
+//     whole 128-column strips) with the tile shape the base rule picks for that narrower problem;
+//     on the hidden-5120 layers at M = 2048 this gave QKV 164-174 -> 145 us, o_proj 151-158 ->
+//     140 us and down 423-433 -> 371 us;
+//   * otherwise, fewer and bigger tiles: the shape with the least predicted time, e.g. 160 tiles
+//     of 128x128 in one round instead of 320 of 128x64 in two at M = 640 (N = K = 4096:
+//     32.6 -> 22.7 us; M = 768 32.4 -> 22.9, M = 1536 44.0 -> 35.1, M = 3072 70.2 -> 56.0 us).
+// The split is preferred when both apply: for o_proj and down at M = 2048 the model ranks one
+// partial round of 256x256 tiles first, but it measured 5-8 % slower than the split.
+// Each output element is computed exactly as by a single launch of either shape.
+TiledLaunch choose_launch(int64_t M, int64_t N, int64_t K) {
+  const TiledPlan p = launched_plan(M, N, K);
+  const double p_us = plan_us(p, K);
+  const int full = p.tiles / (int)kCUs, rest = p.tiles % (int)kCUs;
+  if (full >= 1 && rest > 0) {
+    const int m_tiles = (int)((M + p.bm - 1) / p.bm);
+    const int n1 = (int)(full * kCUs / m_tiles) * p.bn;  // columns of the whole rounds
+    if (n1 >= p.bn && n1 < N) {
+      TiledPlan lead = p;
+      lead.tiles = (n1 / p.bn) * m_tiles;
+      const TiledPlan tail = launched_plan(M, N - n1, K);
+      const double split_us = plan_us(lead, K) + plan_us(tail, K) + kLaunchGapUs;
+      if (split_us < p_us) return {lead, n1, tail, split_us};
+    }
+  }
+  if (rest > 0) {
+    const TiledPlan q = min_time_plan(M, N, K);
+    if (plan_us(q, K) < p_us) return {q, 0, q, plan_us(q, K)};
+  }
+  return {p, 0, p, p_us};
+}
+
 }  // namespace
 
-// The launch plan's rounds at the measured per-CU rates, or, where the operands take longer to
+// The chosen launch's rounds at the measured per-CU rates, or, where the operands take longer to
 // stream from HBM (about 5.5 TB/s, plus 3.5 us for the launch), that.
 double tiled_time_us(int64_t M, int64_t N, int64_t K) {
   const double stream_us = ((double)N * (double)K + (double)M * (double)K) / 5.5e6 + 3.5;
-  return std::max(plan_us(launched_plan(M, N, K), K), stream_us);
+  return std::max(choose_launch(M, N, K).us, stream_us);
 }
 
-// Wave quantization: when the tiles fill the 256 CUs some whole number of times plus a small
-// fraction, that last round would run a few workgroups on an otherwise idle chip. The columns
-// those tiles cover then run as a second launch of the same GEMM restricted to them (B, its
-// scales, C and the bias offset by whole 128-column strips), with the tile shape the plan picks
-// for that narrower problem; each output element is computed exactly as before. The split is
-// taken only when the per-shape round times above predict a gain.
 hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
   (void)workspace;
-  const TiledPlan p = launched_plan(args.M, args.N, args.K);
-  const int full = p.tiles / (int)kCUs, rest = p.tiles % (int)kCUs;
-  if (full >= 1 && rest > 0) {
-    const int m_tiles = (args.M + p.bm - 1) / p.bm;
-    const int n1 = (int)(full * kCUs / m_tiles) * p.bn;  // columns of the whole rounds
-    if (n1 >= p.bn && n1 < args.N) {
-      TiledPlan lead = p;
-      lead.tiles = (n1 / p.bn) * m_tiles;
-      const TiledPlan tail = launched_plan(args.M, args.N - n1, args.K);
-      if (plan_us(lead, args.K) + plan_us(tail, args.K) + kLaunchGapUs < plan_us(p, args.K)) {
-        GemmArgs a1 = args;
-        a1.N = n1;
-        GemmArgs a2 = args;
-        a2.N = args.N - n1;
-        a2.b = args.b + (int64_t)n1 * args.ldb;
-        a2.bs = static_cast<const uint8_t*>(args.bs) + (int64_t)(n1 / kBlock) * args.ld_bs * (args.e8 ? 1 : 4);
-        a2.c = args.c + n1;
-        if (args.bias) a2.bias = args.bias + n1;
-        const hipError_t e = launch_planned(a1, lead, stream);
-        if (e != hipSuccess) return e;
-        return launch_planned(a2, tail, stream);
-      }
-    }
-  }
-  return launch_planned(args, p, stream);
+  const TiledLaunch l = choose_launch(args.M, args.N, args.K);
+  if (l.n1 == 0) return launch_planned(args, l.lead, stream);
+  const int n1 = l.n1;
+  GemmArgs a1 = args;
+  a1.N = n1;
+  GemmArgs a2 = args;
+  a2.N = args.N - n1;
+  a2.b = args.b + (int64_t)n1 * args.ldb;
+  a2.bs = static_cast<const uint8_t*>(args.bs) + (int64_t)(n1 / kBlock) * args.ld_bs * (args.e8 ? 1 : 4);
+  a2.c = args.c + n1;
+  if (args.bias) a2.bias = args.bias + n1;
+  const hipError_t e = launch_planned(a1, l.lead, stream);
+  if (e != hipSuccess) return e;
+  return launch_planned(a2, l.tail, stream);
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
