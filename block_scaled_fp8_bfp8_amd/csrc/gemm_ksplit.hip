@@ -29,6 +29,7 @@
 //   * UE8M0 scales (kE8): the scale codes are copied like the float scales, and the scaled
 //     MFMA applies 2^(ea - 127) * 2^(eb - 127) and accumulates into the wave's tile itself.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "device_common.h"
@@ -243,35 +244,76 @@ hipError_t launch_ksplit_cfg(const GemmArgs& args, hipStream_t stream) {
 
 }  // namespace
 
-// Tile per M, measured on the N = K = 4096 sweep (cold weights): 16x16 up to M = 16 (two
-// slots per wave), 16x32 and 32x32 up to 32 and 64, then 64x32 and 64x64 (one slot per
-// wave). Every choice gives 256 or more workgroups at N = 4096.
+// Tiles (BN x BM, 8 waves each) and how many workgroups of each fit on a CU (LDS bound).
+struct KsplitCfg {
+  int bn, bm, per_cu;
+};
+constexpr KsplitCfg kKsplitCfgs[] = {
+    {16, 16, 2},  // two slots per wave
+    {16, 32, 1},
+    {32, 32, 1},
+    {64, 32, 1},  // one slot per wave from here
+    {64, 64, 1},
+};
+constexpr int kKsplitCfgCount = sizeof(kKsplitCfgs) / sizeof(kKsplitCfgs[0]);
+
 namespace {
-void ksplit_tile(int64_t M, int& bn, int& bm) {
-  bn = M <= 32 ? 16 : M <= 128 ? (M <= 64 ? 32 : 64) : 64;
-  bm = M <= 16 ? 16 : M <= 128 ? 32 : 64;
+
+// Predicted time of one configuration. Every workgroup copies its BN weight rows and its
+// activation rows (at most M distinct ones) of every K block from L2 into LDS, at about 50 GB/s
+// per CU when all workgroups run at once, about 33 GB/s when they need several rounds (each
+// round then also streams its own part of the weights from HBM); the copies of all workgroups
+// together run at up to 9.5 TB/s, the weights stream from HBM at about 5.5 TB/s, and a launch
+// adds about 3.5 us. Workgroups beyond what the CUs hold at once (per_cu each) run in further
+// rounds. Fitted to the N = K = 4096 and hidden-5120 shapes at M = 16-256, where it ranks the
+// measured best tile first or within 5 % of it (the 51200-wide gate+up weight at M = 64, four
+// rounds of 64x64 tiles: 79 us predicted, 82 us measured).
+double cfg_time_us(const KsplitCfg& c, int64_t M, int64_t N, int64_t K) {
+  const double wgs = (double)((N + c.bn - 1) / c.bn) * (double)((M + c.bm - 1) / c.bm);
+  const double per_wg = (double)(c.bn + (M < c.bm ? M : c.bm)) * (double)K;
+  const double rounds = std::ceil(wgs / (256.0 * c.per_cu));
+  const double per_cu_rate = rounds > 1.0 ? 3.3e4 : 5.0e4;  // bytes per us
+  return std::max({rounds * per_wg / per_cu_rate, wgs * per_wg / 9.5e6, (double)N * (double)K / 5.5e6}) + 3.5;
 }
+
+// The tile measured best on the N = K = 4096 sweep (cold weights) for each M: 16x16 up to
+// M = 16, 16x32 and 32x32 up to 32 and 64, then 64x32 and 64x64; every choice gives 256 or
+// more workgroups at N = 4096.
+int default_cfg(int64_t M) { return M <= 16 ? 0 : M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 3 : 4; }
+
+// The default tile, unless the model predicts another at least 10 % faster. That happens where
+// K is long and N not much wider than 4096 (hidden-5120 o_proj and down, QKV), where fewer,
+// larger tiles copy fewer bytes: down (N = 5120, K = 25600) at M = 128 takes 67 us with 64x64
+// tiles against 94 us with 64x32, o_proj at M = 64 19 us with 64x32 against 21 us with 32x32.
+int choose_cfg(int64_t M, int64_t N, int64_t K) {
+  const int d = default_cfg(M);
+  int best = d;
+  double best_us = cfg_time_us(kKsplitCfgs[d], M, N, K);
+  const double bar = 0.9 * best_us;
+  for (int i = 0; i < kKsplitCfgCount; ++i) {
+    const double us = cfg_time_us(kKsplitCfgs[i], M, N, K);
+    if (us < bar && us < best_us) {
+      best = i;
+      best_us = us;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
-// Every workgroup copies its BN weight rows and its activation rows (at most M distinct ones)
-// of every K block from L2 into LDS; measured across the transformer and N = K = 4096 shapes,
-// those copies run at about 9.5 TB/s in aggregate, the weights stream from HBM at about
-// 5.5 TB/s, and a launch adds about 3.5 us.
 double ksplit_time_us(int64_t M, int64_t N, int64_t K) {
-  int bn, bm;
-  ksplit_tile(M, bn, bm);
-  const double tiles = (double)((N + bn - 1) / bn) * (double)((M + bm - 1) / bm);
-  const double copied = tiles * (double)(bn + (M < bm ? M : bm)) * (double)K;
-  const double weights = (double)N * (double)K;
-  return std::max(copied / 9.5e6, weights / 5.5e6) + 3.5;
+  return cfg_time_us(kKsplitCfgs[choose_cfg(M, N, K)], M, N, K);
 }
 
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream) {
-  if (args.M <= 16) return launch_ksplit_cfg<1, 1, 8, 2>(args, stream);
-  if (args.M <= 32) return launch_ksplit_cfg<1, 2, 8, 2>(args, stream);
-  if (args.M <= 64) return launch_ksplit_cfg<2, 2, 8, 2>(args, stream);
-  if (args.M <= 128) return launch_ksplit_cfg<4, 2, 8, 1>(args, stream);
-  return launch_ksplit_cfg<4, 4, 8, 1>(args, stream);
+  switch (choose_cfg(args.M, args.N, args.K)) {
+    case 0: return launch_ksplit_cfg<1, 1, 8, 2>(args, stream);
+    case 1: return launch_ksplit_cfg<1, 2, 8, 2>(args, stream);
+    case 2: return launch_ksplit_cfg<2, 2, 8, 2>(args, stream);
+    case 3: return launch_ksplit_cfg<4, 2, 8, 1>(args, stream);
+    default: return launch_ksplit_cfg<4, 4, 8, 1>(args, stream);
+  }
 }
 
 }  // namespace bfp8

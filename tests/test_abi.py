@@ -156,18 +156,22 @@ def test_schedule_override(lib):
 
 
 def test_schedule_by_shape(lib):
-    """Automatic choice: K-split at small M on the square and hidden-5120 down/o_proj weights; the
-    tiled schedule above 256 rows, and at M >= 64 on the 51200-wide gate+up weight, where its
-    predicted time is far lower (the K-split re-reads each weight strip per 32-64 rows)."""
+    """Automatic choice, from the two schedules' time models: K-split at small M on the square
+    weight and on the hidden-5120 o_proj / down weights up to M = 128; the tiled schedule above
+    256 rows, on o_proj / down at M = 256, and at M >= 64 on the 51200-wide gate+up weight, where
+    the K-split copies re-read each weight strip per 32-64 rows (measured 1.1-2.2x slower)."""
     small, tiled = 1, 2
     for m in (1, 16, 64, 128, 256):
         assert lib.bfp8_gemm_schedule_for(m, 4096, 4096) == small
+    for m in (1, 16, 64, 128):
         assert lib.bfp8_gemm_schedule_for(m, 5120, 25600) == small
         assert lib.bfp8_gemm_schedule_for(m, 5120, 8192) == small
     for m in (1, 16):
         assert lib.bfp8_gemm_schedule_for(m, 51200, 5120) == small
     for m in (64, 128, 256):
         assert lib.bfp8_gemm_schedule_for(m, 51200, 5120) == tiled
+    assert lib.bfp8_gemm_schedule_for(256, 5120, 25600) == tiled
+    assert lib.bfp8_gemm_schedule_for(256, 5120, 8192) == tiled
     for n, k in ((4096, 4096), (576, 7168), (51200, 5120)):
         assert lib.bfp8_gemm_schedule_for(257, n, k) == tiled
 
