@@ -295,7 +295,9 @@ def main() -> int:
                 for _ in range(n):
                     bfp8.quant_act(xs[m], q=qs[m], scales=ss[m])
 
-            calls = copies if m <= 2048 else max(copies // 4, 4)
+            # back-to-back calls per replay (independent of the copies, so warm mode times
+            # launches, not the replay of a one-call graph)
+            calls = 33 if m <= 2048 else 8
             res = {"gemm": graph_time_us(gemm_calls, calls), "quant": graph_time_us(quant_calls, min(calls, 32)),
                    "gemm_ue8m0": graph_time_us(gemm8_calls, calls)}
             us = res["gemm"]
