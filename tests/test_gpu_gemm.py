@@ -78,8 +78,20 @@ def test_square_large_m_sampled_rows(gpu, m, sched):
     tolerance.compare(bits(c)[rows], ref_bits, mag, 4096, f"square M={m} {sched}")
 
 
+@pytest.mark.parametrize("m", [640, 768, 1536, 3072])
+def test_square_between_sweep_sizes(gpu, m):
+    """M between the sweep's powers of two, where the automatic plan runs one partial round of
+    bigger tiles (128x128, 256x128 or 256x256) instead of two rounds of smaller ones."""
+    w, bq, bs = _weight_on(gpu, "square", workloads.square_weight)
+    q, s, q_ref, s_ref = quant_gpu_checked(workloads.square_act(m), gpu, f"square M={m}")
+    c = _run("auto", q, s, bq, bs, f"square M={m}")
+    rows = _sample_rows(m, 40, seed=m + 1)
+    _, cols, ref_bits, mag = tolerance.reference(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows=rows)
+    tolerance.compare(bits(c)[rows], ref_bits, mag, 4096, f"square M={m} auto")
+
+
 @pytest.mark.parametrize("layer", list(workloads.TRANSFORMER_LAYERS))
-@pytest.mark.parametrize("m", workloads.TRANSFORMER_M)
+@pytest.mark.parametrize("m", sorted(set(workloads.TRANSFORMER_M) | {32, 64, 256}))
 def test_transformer_linears(gpu, layer, m):
     n, k = workloads.TRANSFORMER_LAYERS[layer]
     w, bq, bs = _weight_on(gpu, layer, lambda: workloads.transformer_weight(layer))
