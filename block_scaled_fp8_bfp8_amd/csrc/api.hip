@@ -107,6 +107,11 @@ bfp8_status_t check_gemm_args(const uint8_t* a, int64_t lda, const void* as, int
   // byte offset from the operand's base.
   if ((N - 1) * ldb + Kp > kMaxOperandSpan || (M > 0 && (M - 1) * lda + Kp > kMaxOperandSpan))
     return fail(BFP8_ERR_UNSUPPORTED, "A (M x lda) and each weight matrix (N x ldb) must span less than 4 GiB");
+  // One workgroup per output tile, and the smallest tile (64 activation rows x 128 weight rows)
+  // must leave the tile count within a 32-bit grid.
+  if (((M + 63) / 64) * ((N + 127) / 128) > (int64_t)INT32_MAX)
+    return fail(BFP8_ERR_UNSUPPORTED, "M x N = %lld x %lld has more output tiles than one launch grid holds",
+                (long long)M, (long long)N);
   const size_t need = grouped ? 0 : bfp8_gemm_workspace_bytes(M, N, K);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);

@@ -85,6 +85,9 @@ def _gemm(lib, a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=2, c=C,
     (dict(c=C + 1), _native.BFP8_ERR_MISALIGNED),
     (dict(N=(1 << 24) + 1, ldb=256, ldc=(1 << 24) + 1), _native.BFP8_ERR_UNSUPPORTED),  # B spans 4 GiB + 256 B
     (dict(M=(1 << 24) + 1, lda=256, ld_as=(1 << 24) + 1), _native.BFP8_ERR_UNSUPPORTED),  # A likewise
+    # 2^18 x 2^17 output tiles of 64 x 128: more than a 32-bit grid, though A and B span 2 GiB each
+    (dict(M=1 << 24, N=1 << 24, K=128, lda=128, ldb=128, ld_as=1 << 24, ld_bs=1, ldc=1 << 24),
+     _native.BFP8_ERR_UNSUPPORTED),
 ])
 def test_gemm_rejections(lib, kw, status):
     st = _gemm(lib, **kw)
