@@ -7,8 +7,10 @@
 //   * the problem is computed transposed, C^T = B . A^T: the 16 rows of an MFMA's first
 //     operand are weight rows and its 16 columns activation rows; one 16x16x128 FP8 MFMA
 //     covers one 128-wide K block of a 16x16 sub-tile;
-//   * a workgroup owns a BN x BM tile of C^T (BN weight rows, BM activation rows), small
-//     enough that the grid has a workgroup for every CU; its WAVES waves split the tile's
+//   * a workgroup owns a BN x BM tile of C^T (BN weight rows, BM activation rows), from
+//     16 x 16 to 64 x 64, chosen per shape by a model of the bytes each CU copies (small
+//     tiles give every CU a workgroup; larger ones copy fewer bytes where K is long); its
+//     WAVES waves split the tile's
 //     K blocks round-robin (kb = w, w + WAVES, ...), each wave accumulating the whole tile
 //     over its own blocks, so waves never wait for one another inside the K loop;
 //   * each wave copies its K blocks (BN + BM rows of 128 bytes, and the block's BM
