@@ -14,13 +14,17 @@
 // exponent byte.
 //
 // HBM-bound: per element it reads 4 (fp32) or 2 (bf16, fp16) bytes and writes 1, plus
-// 4 bytes of scale per 128 elements. Mapping: 16 lanes per group, 8 consecutive
-// elements per lane (one or two 16-byte loads), 4 groups per wave, so one wave
-// streams 512 consecutive elements of a row. The group's amax is reduced with
-// lane shuffles inside each 16-lane quarter; the division is the correctly
-// rounded IEEE divide (HIP's default, no fast-math), and the e4m3 encoding uses
-// the hardware's round-to-nearest-even OCP e4m3fn conversion on values already
-// clamped to +-448 (the conversion itself does not saturate).
+// 4 bytes of scale per 128 elements. Mapping: L lanes per group, 128 / L consecutive
+// elements per lane, 16-byte loads issued together and one store of the lane's codes.
+// Inputs of 32768 groups and more take L = 8 (16 elements, 32 or 64 bytes in flight per
+// lane): with 16 lanes the bf16 path reached only 3.4-4.0 TB/s at M = 2048 on the
+// hidden-5120 shapes, and 8 lanes took K = 25600 from 40.1 to 31.7 us and the fp32
+// M = 8192 sweep input from 30.1 to 27.9 us. Smaller inputs keep L = 16 (twice the lanes,
+// half the latency per lane: M = 1 2.2 against 2.5 us). The group's amax is reduced with
+// lane shuffles inside its L lanes; the division is the correctly rounded IEEE divide
+// (HIP's default, no fast-math), and the e4m3 encoding uses the hardware's
+// round-to-nearest-even OCP e4m3fn conversion on values already clamped to +-448 (the
+// conversion itself does not saturate).
 #include "device_common.h"
 #include "launch.h"
 
@@ -29,85 +33,107 @@ namespace bfp8 {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kGroupsPerBlock = kQuantThreads / 16;
+// Groups below this count take 16 lanes per group, others 8.
+constexpr int64_t kWideGroups = 32768;
 
 // Gather variant (kGather): output row m quantizes input row src_rows[m] / src_div, and rows
 // whose entry is negative are left unwritten (the MoE dispatch's padded buffer: entry = pair
 // index, src_div = top_k, so the input row is the pair's token).
-template <int kIn, bool kE8, bool kGather>
+template <int kIn, bool kE8, bool kGather, int kLanesPerGroup>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
                                                                   void* __restrict__ as, int64_t ld_as,
                                                                   int groups_per_row, int64_t total_groups,
                                                                   const int32_t* __restrict__ src_rows, int src_div,
                                                                   int64_t K) {
-  const int sub = threadIdx.x & 15;  // which 8-element slice of the group
-  const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
+  constexpr int kPerLane = kBlock / kLanesPerGroup;  // consecutive elements per lane
+  constexpr int kGroupsPerBlock = kQuantThreads / kLanesPerGroup;
+  static_assert(kLanesPerGroup == 8 || kLanesPerGroup == 16, "8 or 16 lanes per group");
+  const int sub = threadIdx.x & (kLanesPerGroup - 1);  // which slice of the group
+  const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x / kLanesPerGroup;
   const bool valid = gid < total_groups;
-  // Out-of-range quarters redo the last group (all 16 lanes of a group agree on
-  // `valid`, so shuffles only ever pair lanes of the same state) and store nothing.
+  // Out-of-range groups redo the last group (all lanes of a group agree on `valid`, so
+  // shuffles only ever pair lanes of the same state) and store nothing.
   const int64_t g_lin = valid ? gid : total_groups - 1;
   const int64_t m = g_lin / groups_per_row;
   const int g = (int)(g_lin - m * groups_per_row);
-  const int64_t col = (int64_t)g * kBlock + sub * 8;
-  // A partial last group (K % 128 != 0; K is a multiple of 16) has lanes past K: they load
-  // nothing, count as zeros in the amax and store nothing.
+  const int64_t col = (int64_t)g * kBlock + sub * kPerLane;
+  // A partial last group (K % 128 != 0; K is a multiple of 16, so a lane's 8 or 16 elements
+  // lie wholly before or wholly past K) has lanes past K: they load nothing, count as zeros
+  // in the amax and store nothing.
   const bool in_k = col < K;
   int64_t src = m;
   bool store = valid && in_k;
   if constexpr (kGather) {
-    const int32_t p = src_rows[m];  // the same for the group's 16 lanes
+    const int32_t p = src_rows[m];  // the same for all lanes of the group
     // An unwritten row is not computed: the group's lanes exchange values only among
     // themselves, so leaving it early does not affect the other groups of the wave.
     if (p < 0) return;
     src = p / src_div;
   }
 
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float v[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) v[i] = 0.f;
   if (!in_k) {
-  } else if constexpr (kIn == kInBf16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  } else if constexpr (kIn == kInBf16 || kIn == kInF16) {
+    constexpr int kLoads = kPerLane / 8;  // 16-byte loads of 8 elements
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
+    uint4 r[kLoads];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int j = 0; j < kLoads; ++j) r[j] = p[j];
+    uint32_t w[4 * kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      w[4 * j] = r[j].x; w[4 * j + 1] = r[j].y; w[4 * j + 2] = r[j].z; w[4 * j + 3] = r[j].w;
     }
-  } else if constexpr (kIn == kInF16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + src * ldx + col);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = f16_value(w[i] & 0xffffu);  // exact widening
-      v[2 * i + 1] = f16_value(w[i] >> 16);
+    for (int i = 0; i < 4 * kLoads; ++i) {
+      if constexpr (kIn == kInBf16) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      } else {
+        v[2 * i] = f16_value(w[i] & 0xffffu);  // exact widening
+        v[2 * i + 1] = f16_value(w[i] >> 16);
+      }
     }
   } else {
-    const float* p = static_cast<const float*>(x) + src * ldx + col;
-    const float4 lo = *reinterpret_cast<const float4*>(p);
-    const float4 hi = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    constexpr int kLoads = kPerLane / 4;  // 16-byte loads of 4 elements
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + src * ldx + col);
+    float4 f[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) f[j] = p[j];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      v[4 * i] = f[i].x; v[4 * i + 1] = f[i].y; v[4 * i + 2] = f[i].z; v[4 * i + 3] = f[i].w;
+    }
   }
 
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < kPerLane; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
-  for (int mask = 1; mask < 16; mask <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mask));
+  for (int mask = 1; mask < kLanesPerGroup; mask <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mask));
 
   float s = fmaxf(amax, 1e-10f) / 448.0f;  // correctly rounded divide
   if constexpr (kE8) s = __uint_as_float((__float_as_uint(s) + 0x7fffffu) & ~0x7fffffu);
-  float y[8];
+  float y[kPerLane];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
+  for (int i = 0; i < kPerLane; ++i) y[i] = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
 
-  uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-  uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  uint32_t wq[kPerLane / 4];
+#pragma unroll
+  for (int i = 0; i < kPerLane / 4; ++i) {
+    wq[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i], y[4 * i + 1], 0, false);
+    wq[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i + 2], y[4 * i + 3], wq[i], true);
+  }
 
   if (store) {
-    *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(w0, w1);
+    if constexpr (kPerLane == 16) {
+      *reinterpret_cast<uint4*>(q + m * ldq + col) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+    } else {
+      *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(wq[0], wq[1]);
+    }
     if (sub == 0) {
       if constexpr (kE8) {
         static_cast<uint8_t*>(as)[(int64_t)g * ld_as + m] = (uint8_t)(__float_as_uint(s) >> 23);
@@ -122,16 +148,28 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
 
 namespace {
 
+template <int kIn, bool kE8, int L>
+void launch_quant_lanes(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as,
+                        int groups_per_row, int64_t total, const int32_t* src_rows, int src_div, int64_t K,
+                        hipStream_t stream) {
+  constexpr int kGroupsPerBlock = kQuantThreads / L;
+  const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  if (src_rows) {
+    hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, true, L>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
+  } else {
+    hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, false, L>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
+  }
+}
+
 template <int kIn, bool kE8>
 void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as, int groups_per_row,
                       int64_t total, const int32_t* src_rows, int src_div, int64_t K, hipStream_t stream) {
-  const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  if (src_rows) {
-    hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, true>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
+  if (total < kWideGroups) {
+    launch_quant_lanes<kIn, kE8, 16>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
   } else {
-    hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, false>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
+    launch_quant_lanes<kIn, kE8, 8>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
   }
 }
 

@@ -33,6 +33,41 @@ def test_moe_activations_bf16(gpu):
     quant_gpu_checked(case.act, gpu, f"moe M_pad={case.act.shape[0]} K=7168 bf16")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_wide_mapping_partial_group_and_strided_rows(gpu, dtype):
+    """32768 groups and more take 8 lanes per group (16 elements per lane): here with a partial
+    last group (K = 16400 = 128 * 128 + 16) and rows 48 elements wider than K."""
+    m, k = 300, 16400
+    assert m * -(-k // 128) >= 32768
+    rng = np.random.default_rng(31)
+    full = torch.from_numpy((rng.standard_normal((m, k + 48)) * 3).astype(np.float32)).to(dtype)
+    announce("quant_act wide", dtype, m, k, "strided")
+    x_dev = full.to(gpu)[:, :k]
+    assert x_dev.stride(0) == k + 48
+    q, s = bfp8.quant_act(x_dev)
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.quant_act_ref(full[:, :k].float().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy()[:, :k], q_ref)
+    np.testing.assert_array_equal(s.cpu().contiguous().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_wide_mapping_gather(gpu):
+    """The gathered quantizer (MoE dispatch rows) on 4800 rows x 8 groups, with skipped rows."""
+    t, top_k, h = 600, 8, 1024
+    x = workloads.act_normal_bf16(t, h, seed=41)
+    rows = t * top_k
+    rng = np.random.default_rng(42)
+    src = rng.permutation(rows).astype(np.int32)
+    src[rng.choice(rows, 300, replace=False)] = -1
+    used = src >= 0
+    announce("quant_act_gather wide", rows, h)
+    q, s = bfp8.quant_act_gather(x.to(gpu), torch.from_numpy(src).to(gpu), top_k)
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.quant_act_ref(x.float().numpy()[src[used] // top_k])
+    np.testing.assert_array_equal(q.cpu().numpy()[used], q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy()[used].view(np.uint32), s_ref.view(np.uint32))
+
+
 def test_near_e4m3_ties(gpu):
     """Quotients within a few float32 ulps of e4m3 rounding midpoints: a reciprocal-multiply
     or a wrongly rounded divide changes codes here."""

@@ -38,7 +38,7 @@ def quant_e8_checked(x_cpu, dev, what=""):
     return q, e, q_ref, e_ref
 
 
-@pytest.mark.parametrize("m", [1, 37, 300])
+@pytest.mark.parametrize("m", [1, 37, 300, 4096])  # 4096 x 8 groups: the 8-lanes-per-group mapping
 def test_quant_fp32_uniform(gpu, m):
     quant_e8_checked(workloads.act_uniform(m, 1024, seed=400 + m), gpu, f"uniform M={m}")
 
