@@ -136,6 +136,32 @@ def test_ragged_tails_with_padded_strides(gpu, m, n, k, sched):
     assert (c_full[:, n:].float().cpu() == -7.0).all()
 
 
+@pytest.mark.parametrize("m,n,k", [(640, 4000, 512), (769, 4112, 256), (1536, 4040, 512), (1583, 1320, 1024),
+                                   (3000, 2056, 512), (2953, 5416, 1024)])
+def test_tiled_launch_choices_ragged(gpu, m, n, k):
+    """Shapes whose base plan leaves a partial last round, with ragged M and N and padded strides:
+    the first five run fewer, bigger tiles (128x128 or 256x128) in one round, the last splits its
+    columns (256x256 whole rounds, then the remaining 40 columns). Sampled rows, every column."""
+    rng = np.random.default_rng(m + 3 * n + k)
+    a = _random_codes(rng, (m, k + 32))
+    b = _random_codes(rng, (n, k + 16))
+    a_s = torch.from_numpy(rng.uniform(0.01, 2, (k // 128, m + 3)).astype(np.float32))
+    b_s = torch.from_numpy(rng.uniform(1e-3, 1e-2, (-(-n // 128), k // 128 + 1)).astype(np.float32))
+    ad, bd = a.to(gpu)[:, :k], b.to(gpu)[:, :k]
+    asd = a_s.to(gpu)[:, :m].t()
+    bsd = b_s.to(gpu)[:, :k // 128]
+    c_full = torch.full((m, n + 8), -7.0, dtype=torch.bfloat16, device=gpu)
+    c = _run("auto", ad, asd, bd, bsd, f"launch choice M={m} N={n} K={k}", out=c_full[:, :n])
+    a_np, b_np = a[:, :k].numpy(), b[:, :k].numpy()
+    as_np = a_s[:, :m].t().contiguous().numpy()
+    bs_np = b_s[:, :k // 128].contiguous().numpy()
+    rows = _sample_rows(m, 20, seed=m)
+    _, cols, ref_bits, mag = tolerance.reference(a_np, as_np, b_np, bs_np, rows=rows)
+    mmax = tolerance.block_max_mass(a_np, as_np, b_np, bs_np, rows, cols)
+    tolerance.compare(bits(c)[rows], ref_bits, mag, k, f"launch choice {m}x{n}x{k}", hw_block=mmax)
+    assert (c_full[:, n:].float().cpu() == -7.0).all()
+
+
 def _code(v):
     return int(torch.tensor([v], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)[0])
 
