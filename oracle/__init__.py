@@ -35,8 +35,11 @@ What is computed, and where it is defined on the pages:
   and the blockwise GEMM of operands carrying such scales.
 
 Every function is pinned by tests under ``tests/test_oracle_*.py`` (library
-routines, brute force with exact rationals, closed forms and invariants); none
-is "parity unpinned".
+routines, brute force with exact rationals, closed forms and invariants),
+including the spacing helpers ``bf16.ulp``, ``e4m3.ulp`` and ``f16.ulp`` that
+set the acceptance bounds (``tests/test_oracle_ulp.py``: the distance to the
+next value as torch and numpy decode neighbouring bit patterns); none is
+"parity unpinned".
 """
 
 from . import bf16, e4m3, f16, gemm, linear, moe, quant, scales, ue8m0  # noqa: F401

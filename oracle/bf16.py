@@ -52,5 +52,7 @@ def ulp(x) -> np.ndarray:
     """Spacing of bf16 values at |x| (float64): 2**(floor(log2|x|) - 7), at least 2**-133."""
     mag = np.abs(np.asarray(x, dtype=np.float64))
     _, e2 = np.frexp(mag)
-    exp = np.maximum(e2.astype(np.int64) - 1, -126)
+    # zero lies in the subnormal range, whose spacing is the smallest normal binade's (frexp
+    # gives 0 the exponent 0, which would make its spacing 2**-8)
+    exp = np.where(mag == 0.0, -126, np.maximum(e2.astype(np.int64) - 1, -126))
     return np.ldexp(1.0, (exp - 7).astype(np.int32))

@@ -92,5 +92,6 @@ def ulp(codes: np.ndarray) -> np.ndarray:
     """
     v = np.abs(decode(codes))
     _, e2 = np.frexp(v)
-    exp = np.maximum(e2.astype(np.int64) - 1, _MIN_NORMAL_EXP)
+    # zero is subnormal: its spacing is 2**-9 (frexp gives 0 the exponent 0)
+    exp = np.where(v == 0.0, _MIN_NORMAL_EXP, np.maximum(e2.astype(np.int64) - 1, _MIN_NORMAL_EXP))
     return np.ldexp(1.0, (exp - 3).astype(np.int32))

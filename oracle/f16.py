@@ -46,5 +46,6 @@ def ulp(x) -> np.ndarray:
     """Spacing of fp16 values at |x| (float64): 2**(floor(log2|x|) - 10), at least 2**-24."""
     mag = np.abs(np.asarray(x, dtype=np.float64))
     _, e2 = np.frexp(mag)
-    exp = np.maximum(e2.astype(np.int64) - 1, -14)
+    # zero is subnormal: its spacing is 2**-24 (frexp gives 0 the exponent 0)
+    exp = np.where(mag == 0.0, -14, np.maximum(e2.astype(np.int64) - 1, -14))
     return np.ldexp(1.0, (exp - 10).astype(np.int32))

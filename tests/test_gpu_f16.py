@@ -50,7 +50,7 @@ def test_gemm_f16_output(gpu, m, sched):
     q_ref, s_ref = quant.quant_act_ref(x.float().numpy())
     rows = np.arange(m) if m <= 64 else np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).choice(m, 40, replace=False)]))
     acc, _ = gemm.gemm_acc_ref(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows=rows)
-    mag = tolerance.abs_product_mass(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
+    mag = tolerance.masses(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
     tolerance.compare_f16(_bits16(c)[rows], f16.to_bits(acc), mag, k, f"gemm_f16 M={m} {sched}")
 
 
@@ -93,9 +93,5 @@ def test_linear_fp16_transformer_shape(gpu):
     got = bfp8.linear(x.to(gpu), w.q.to(gpu), w.s.to(gpu), bias.to(gpu))
     torch.cuda.synchronize()
     out_ref, c_ref, q, s = linear.linear_f16_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy())
-    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
-    d = np.abs(f16.from_bits(_bits16(got)) - f16.from_bits(out_ref))
-    c = f16.from_bits(c_ref)
-    bound = 2 * f16.ulp(c) + 1e-3 * np.abs(c) + (k / 128 + 130) * 2.0**-24 * mag + f16.ulp(f16.from_bits(out_ref))
-    assert (d <= bound).all()
-    assert d.mean() / np.abs(f16.from_bits(out_ref)).mean() <= 1e-3
+    mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
+    tolerance.compare_linear(_bits16(got), out_ref, c_ref, mag, k, "linear fp16 o_proj", fmt=f16)

@@ -142,8 +142,8 @@ def test_nn_weights_converted_once(gpu):
     c = _grouped(q, s, w_nt, s_nt, torch.from_numpy(layout).to(gpu), "nn weights")
     rows, acc = gemm.grouped_gemm_contiguous_nn_acc_ref(q_ref, s_ref, w_nn.numpy(), s_nn.numpy(), layout)
     from oracle import bf16
-    mag = np.zeros_like(acc)
+    mag = tolerance.Mass.zeros(acc.shape)
     for g in range(g_count):
         sel = np.nonzero(layout[rows] == g)[0]
-        mag[sel] = tolerance.abs_product_mass(q_ref, s_ref, ws[g].q.numpy(), ws[g].s.numpy(), rows[sel], np.arange(n))
+        mag[sel] = tolerance.masses(q_ref, s_ref, ws[g].q.numpy(), ws[g].s.numpy(), rows[sel], np.arange(n))
     tolerance.compare(bits(c)[rows], bf16.to_bits(acc), mag, k, "grouped nn")

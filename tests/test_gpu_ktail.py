@@ -106,7 +106,7 @@ def test_gemm_f16_partial_last_block(gpu, sched):
     from oracle import f16, gemm
 
     acc, _ = gemm.gemm_acc_ref(q_ref, s_ref, w.q.numpy(), w.s.numpy())
-    mag = tolerance.abs_product_mass(q_ref, s_ref, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
+    mag = tolerance.masses(q_ref, s_ref, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
     got = c.cpu().view(torch.int16).numpy().view(np.uint16)
     tolerance.compare_f16(got, f16.to_bits(acc), mag, k, f"gemm_f16 tail {sched}")
 
@@ -165,7 +165,7 @@ def test_linear_partial_last_block(gpu, m):
     y = bfp8.linear(x.to(gpu), _nan_padded(w.q, gpu), w.s.to(gpu), bias.to(gpu))
     torch.cuda.synchronize()
     out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy())
-    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
+    mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
     tolerance.compare_linear(bits(y), out_ref, c_ref, mag, k, f"linear tail m={m}")
 
 
@@ -201,8 +201,8 @@ def test_nn_weights_partial_last_block(gpu):
 
     rows, acc = gemm.grouped_gemm_contiguous_nn_acc_ref(q_ref, s_ref, w_nn.numpy(), s_nn.numpy(), layout)
     got = bits(c)[rows]
-    mag = np.zeros_like(acc)
+    mag = tolerance.Mass.zeros(acc.shape)
     for e in range(g):
         sel = layout[rows] == e
-        mag[sel] = tolerance.abs_product_mass(q_ref, s_ref, ws[e].q.numpy(), ws[e].s.numpy(), rows[sel], np.arange(n))
+        mag[sel] = tolerance.masses(q_ref, s_ref, ws[e].q.numpy(), ws[e].s.numpy(), rows[sel], np.arange(n))
     tolerance.compare(got, bf16.to_bits(acc), mag, k, "grouped nn tail")

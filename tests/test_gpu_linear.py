@@ -84,7 +84,7 @@ def test_page2_shapes_with_bias(gpu):
     x = workloads.act_normal_bf16(m, k, seed=6)
     bias = _bf16_spread(np.random.default_rng(7), (n,), -4, 2)
     out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy())
-    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
+    mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
     announce("linear page2 shapes", m, n, k)
     got = bfp8.linear(x.to(gpu), w.q.to(gpu), w.s.to(gpu), bias.to(gpu))
     torch.cuda.synchronize()
@@ -105,7 +105,7 @@ def test_square_with_bias_sampled_rows(gpu, m):
     bias = _bf16_spread(np.random.default_rng(m), (n,), -6, 3)
     rows = np.arange(m) if m <= 16 else np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).choice(m, 14, replace=False)]))
     out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy(), rows=rows)
-    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
+    mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
     announce("linear square", m, n, k, "->", bfp8.schedule_for(m, n, k))
     got = bfp8.linear(x.to(gpu), wq, ws, bias.to(gpu))
     torch.cuda.synchronize()
@@ -126,7 +126,7 @@ def test_wide_gate_up_weight_sampled_rows(gpu, m):
     bias = _bf16_spread(np.random.default_rng(m + 1), (n,), -6, 3)
     rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).choice(m, 6, replace=False)]))
     out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy(), rows=rows)
-    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
+    mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
     announce("linear wide", m, n, k, "->", bfp8.schedule_for(m, n, k))
     got = bfp8.linear(x.to(gpu), wq, ws, bias.to(gpu))
     torch.cuda.synchronize()
@@ -163,7 +163,7 @@ def test_caller_workspace_back_to_back(gpu):
         xs = workloads.act_normal_bf16(m, k + 72, seed=70 + m)
         x = xs[:, :k]
         out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy())
-        mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
+        mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), np.arange(m), np.arange(n))
         announce("linear caller workspace", m, n, k)
         got = bfp8.linear(xs.to(gpu)[:, :k], wq, ws, bias.to(gpu), workspace=work)
         torch.cuda.synchronize()

@@ -76,7 +76,7 @@ def test_gemm_on_expanded_scales(gpu, m, n, k, per_token):
     a_s_ref = scales.expand_act_scales_ref(s_a, m, k)
     b_s_ref = scales.expand_weight_scale_ref(s_b, n, k)
     cols = np.arange(n)
-    mag = tolerance.abs_product_mass(a, a_s_ref, b, b_s_ref, rows, cols)
+    mag = tolerance.masses(a, a_s_ref, b, b_s_ref, rows, cols)
     # codes drawn over the whole e4m3 range: the hardware block-dot term of the tolerance applies
     mmax = tolerance.block_max_mass(a, a_s_ref, b, b_s_ref, rows, cols)
     st = tolerance.compare(bits(c)[rows], want, mag, k, f"expanded scales {m}x{n}x{k}", hw_block=mmax)

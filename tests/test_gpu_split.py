@@ -56,7 +56,7 @@ def test_split_gemm_f16(gpu):
     torch.cuda.synchronize()
     rows, cols = _rows_cols(m, n, seed=5)
     acc, _ = gemm.gemm_acc_ref(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows=rows, cols=cols)
-    mag = tolerance.abs_product_mass(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, cols)
+    mag = tolerance.masses(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, cols)
     got = c.cpu().view(torch.int16).numpy().view(np.uint16)[np.ix_(rows, cols)]
     tolerance.compare_f16(got, f16.to_bits(acc), mag, k, "split f16")
 
@@ -89,7 +89,7 @@ def test_split_linear_with_bias(gpu):
     rows, cols = _rows_cols(m, n, seed=12)
     out_ref, c_ref, q, s = linear.linear_ref(x[rows].float().numpy(), w.q.numpy(), w.s.numpy(),
                                              bias=bias.float().numpy(), cols=cols)
-    mag = tolerance.abs_product_mass(q, s, w.q.numpy(), w.s.numpy(), np.arange(rows.size), cols)
+    mag = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), np.arange(rows.size), cols)
     tolerance.compare_linear(bits(y)[np.ix_(rows, cols)], out_ref, c_ref, mag, k, "split linear")
 
 

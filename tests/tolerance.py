@@ -27,9 +27,45 @@ of the largest and are held to the bound without this term.
 
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 from oracle import bf16, e4m3, gemm
+
+# Size of the floor SURVEY-style reading A13 proposes: 2**-20 of the absolute sum of the block
+# terms, sum_kb |P_kb As Bs| (the oracle's second output).
+A13_ETA = 2.0**-20
+
+# One entry per comparison: the test, what was compared and how close it came to each floor.
+RECORDS: list[dict] = []
+
+
+class Mass:
+    """Sizes of the terms of each compared output (float64 arrays of one shape):
+    absum = sum_kb |P_kb As Bs| (the oracle's absolute block sum) and
+    mag = sum_kb |As Bs| sum_k |a_k b_k| (every product's size, before any cancellation)."""
+
+    def __init__(self, absum, mag):
+        self.absum = np.asarray(absum, dtype=np.float64)
+        self.mag = np.asarray(mag, dtype=np.float64)
+        assert self.absum.shape == self.mag.shape
+
+    @classmethod
+    def zeros(cls, shape):
+        return cls(np.zeros(shape), np.zeros(shape))
+
+    def __getitem__(self, idx):
+        return Mass(self.absum[idx], self.mag[idx])
+
+    def __setitem__(self, idx, other):
+        self.absum[idx] = other.absum
+        self.mag[idx] = other.mag
+
+    @property
+    def shape(self):
+        return self.absum.shape
 
 
 def abs_product_mass(a_q, a_s, b_q, b_s, rows, cols):
@@ -65,63 +101,104 @@ def block_max_mass(a_q, a_s, b_q, b_s, rows, cols):
     return out
 
 
+def masses(a_q, a_s, b_q, b_s, rows, cols) -> Mass:
+    """Mass of the outputs [rows x cols]: absum from the oracle, mag from abs_product_mass."""
+    _, absum = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, np.asarray(rows), np.asarray(cols))
+    return Mass(absum, abs_product_mass(a_q, a_s, b_q, b_s, rows, cols))
+
+
 def reference(a_q, a_s, b_q, b_s, rows=None, cols=None):
-    """(rows, cols, ref_bits, mag) from the oracle."""
+    """(rows, cols, ref_bits, Mass) from the oracle."""
     m, n = np.asarray(a_q).shape[0], np.asarray(b_q).shape[0]
     rows = np.arange(m) if rows is None else np.asarray(rows)
     cols = np.arange(n) if cols is None else np.asarray(cols)
-    acc, _ = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, rows, cols)
-    mag = abs_product_mass(a_q, a_s, b_q, b_s, rows, cols)
-    return rows, cols, bf16.to_bits(acc), mag
+    acc, absum = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, rows, cols)
+    mass = Mass(absum, abs_product_mass(a_q, a_s, b_q, b_s, rows, cols))
+    return rows, cols, bf16.to_bits(acc), mass
 
 
-def compare(got_bits, ref_bits, mag, k, what="", hw_block=None):
+def fp32_floor(mass: Mass, k) -> np.ndarray:
+    """Worst-case error of float32 accumulation in any order: (K/128 + 130) 2**-24 mag."""
+    return (k / 128 + 130) * 2.0**-24 * mass.mag
+
+
+def e8_floor(mass: Mass, k) -> np.ndarray:
+    """UE8M0 GEMMs: (K/128 + 1) 2**-17 mag (the scaled MFMA's measured accumulation error)."""
+    return (k / 128 + 1) * E8_STEP_ETA * mass.mag
+
+
+def _record(what, d, stated, mass: Mass, floor, extra=None):
+    """Ratios of each element's excess over the stated bound to the floor in force and to
+    A13's 2**-20 absum (plus the hardware block term where the test adds one)."""
+    excess = np.maximum(d - stated, 0.0)
+    a13 = A13_ETA * mass.absum + (extra if extra is not None else 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r_floor = np.where(excess > 0, excess / floor, 0.0)
+        r_a13 = np.where(excess > 0, excess / a13, 0.0)
+    rec = {
+        "test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
+        "what": what,
+        "n": int(d.size),
+        "over_stated": int((excess > 0).sum()),
+        "worst_over_floor": float(r_floor.max()) if d.size else 0.0,
+        "worst_over_a13": float(r_a13.max()) if d.size else 0.0,
+    }
+    RECORDS.append(rec)
+    return rec
+
+
+def write_report(path):
+    """The recorded ratios as JSON (one object per comparison)."""
+    with open(path, "w") as f:
+        json.dump(RECORDS, f, indent=1)
+
+
+def _finish(what, got, ref, d, stated, floor, mass, rel_mean, exact_frac, extra=None):
+    rec = _record(what, d, stated, mass, floor, extra)
+    stats = {"rel_mean": float(rel_mean), "max_abs": float(d.max()) if d.size else 0.0,
+             "exact_frac": float(exact_frac), "over_stated": rec["over_stated"], "n": rec["n"],
+             "worst_over_floor": rec["worst_over_floor"], "worst_over_a13": rec["worst_over_a13"]}
+    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3 ({stats})"
+    bad = d > stated + floor
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {d.size} elements over the bound, first at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r} bound {(stated + floor)[i]!r} ({stats})")
+    return stats
+
+
+def _rel_mean(d, ref):
+    return d.mean() / max(np.abs(ref).mean(), 1e-300) if d.size else 0.0
+
+
+def compare(got_bits, ref_bits, mass: Mass, k, what="", hw_block=None):
     """Assert the bounds above; returns a dict of statistics. `hw_block` is mmax for tests
     whose codes span the whole e4m3 range (adds HW_BLOCK_ETA * mmax)."""
     got = bf16.from_bits(got_bits)
     ref = bf16.from_bits(ref_bits)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert got.shape == ref.shape == mass.shape, (got.shape, ref.shape, mass.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     d = np.abs(got - ref)
-    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
     stated = 2 * bf16.ulp(ref) + 1e-3 * np.abs(ref)
-    floor = (k / 128 + 130) * 2.0**-24 * mag
-    if hw_block is not None:
-        floor = floor + HW_BLOCK_ETA * hw_block
-    bad = d > stated + floor
-    stats = {
-        "rel_mean": float(rel_mean),
-        "max_abs": float(d.max()) if d.size else 0.0,
-        "exact_frac": float(np.mean(got_bits == ref_bits)) if d.size else 1.0,
-        "over_stated": int((d > stated).sum()),
-        "n": int(d.size),
-    }
-    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3 ({stats})"
-    if bad.any():
-        i = np.argwhere(bad)[0]
-        raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {tuple(i)}: "
-                             f"got {got[tuple(i)]!r} ref {ref[tuple(i)]!r} ({stats})")
-    return stats
+    extra = HW_BLOCK_ETA * hw_block if hw_block is not None else None
+    floor = fp32_floor(mass, k) + (extra if extra is not None else 0.0)
+    exact = np.mean(got_bits == ref_bits) if d.size else 1.0
+    return _finish(what, got, ref, d, stated, floor, mass, _rel_mean(d, ref), exact, extra)
 
 
-def compare_linear(got_bits, ref_out_bits, ref_c_bits, mag, k, what=""):
+def compare_linear(got_bits, ref_out_bits, ref_c_bits, mass: Mass, k, what="", fmt=bf16):
     """Linear layer: out = bf16(bf16(C) + bias). The GEMM's bound applies to C (at ref_c);
-    the bias addition then rounds once more, adding at most one bf16 ulp of the output."""
-    got = bf16.from_bits(got_bits)
-    ref = bf16.from_bits(ref_out_bits)
-    ref_c = bf16.from_bits(ref_c_bits)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
+    the bias addition then rounds once more, adding at most one ulp of the output. `fmt` is
+    the output format's oracle module (bf16, or f16 for fp16 layers)."""
+    got = fmt.from_bits(got_bits)
+    ref = fmt.from_bits(ref_out_bits)
+    ref_c = fmt.from_bits(ref_c_bits)
+    assert got.shape == ref.shape == mass.shape, (got.shape, ref.shape, mass.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     d = np.abs(got - ref)
-    bound = 2 * bf16.ulp(ref_c) + 1e-3 * np.abs(ref_c) + (k / 128 + 130) * 2.0**-24 * mag + bf16.ulp(ref)
-    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
-    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3"
-    bad = d > bound
-    if bad.any():
-        i = tuple(np.argwhere(bad)[0])
-        raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {i}: "
-                             f"got {got[i]!r} ref {ref[i]!r}")
-    return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_out_bits))}
+    stated = 2 * fmt.ulp(ref_c) + 1e-3 * np.abs(ref_c) + fmt.ulp(ref)
+    exact = np.mean(got_bits == ref_out_bits) if d.size else 1.0
+    return _finish(what, got, ref, d, stated, fp32_floor(mass, k), mass, _rel_mean(d, ref), exact)
 
 
 # UE8M0 GEMMs: the scaled MFMA adds each K block's product to the running FP32 tile inside
@@ -133,51 +210,37 @@ def compare_linear(got_bits, ref_out_bits, ref_c_bits, mag, k, what=""):
 E8_STEP_ETA = 2.0**-17
 
 
-def compare_e8(got_bits, ref_bits, mag, k, what="", hw_block=None):
+def compare_e8(got_bits, ref_bits, mass: Mass, k, what="", hw_block=None):
     """compare() for the UE8M0 GEMMs: the stated bound plus the hardware accumulation floor."""
     got = bf16.from_bits(got_bits)
     ref = bf16.from_bits(ref_bits)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert got.shape == ref.shape == mass.shape, (got.shape, ref.shape, mass.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     d = np.abs(got - ref)
-    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
     stated = 2 * bf16.ulp(ref) + 1e-3 * np.abs(ref)
-    floor = (k / 128 + 1) * E8_STEP_ETA * mag
-    if hw_block is not None:
-        floor = floor + HW_BLOCK_ETA * hw_block
-    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3"
-    bad = d > stated + floor
-    if bad.any():
-        i = tuple(np.argwhere(bad)[0])
-        raise AssertionError(f"{what}: {int(bad.sum())} of {d.size} elements over the bound, first at {i}: "
-                             f"got {got[i]!r} ref {ref[i]!r} bound {(stated + floor)[i]!r}")
-    return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_bits)) if d.size else 1.0,
-            "over_stated": int((d > stated).sum()), "n": int(d.size)}
+    extra = HW_BLOCK_ETA * hw_block if hw_block is not None else None
+    floor = e8_floor(mass, k) + (extra if extra is not None else 0.0)
+    exact = np.mean(got_bits == ref_bits) if d.size else 1.0
+    return _finish(what, got, ref, d, stated, floor, mass, _rel_mean(d, ref), exact, extra)
 
 
 def reference_e8(a_q, a_e, b_q, b_e, rows=None, cols=None):
-    """(rows, cols, ref_bits, mag) from the oracle, UE8M0 scale codes."""
+    """(rows, cols, ref_bits, Mass) from the oracle, UE8M0 scale codes."""
     from oracle import ue8m0
 
     return reference(a_q, ue8m0.decode(np.asarray(a_e)).astype(np.float32), b_q,
                      ue8m0.decode(np.asarray(b_e)).astype(np.float32), rows, cols)
 
 
-def compare_f16(got_bits, ref_bits, mag, k, what=""):
+def compare_f16(got_bits, ref_bits, mass: Mass, k, what=""):
     """compare() for fp16 outputs: the same bound with fp16's ulp (rounded once, to nearest even)."""
     from oracle import f16
 
     got = f16.from_bits(got_bits)
     ref = f16.from_bits(ref_bits)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert got.shape == ref.shape == mass.shape, (got.shape, ref.shape, mass.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     d = np.abs(got - ref)
-    rel_mean = d.mean() / max(np.abs(ref).mean(), 1e-300)
-    assert rel_mean <= 1e-3, f"{what}: mean relative error {rel_mean:.3e} > 1e-3"
-    bound = 2 * f16.ulp(ref) + 1e-3 * np.abs(ref) + (k / 128 + 130) * 2.0**-24 * mag
-    bad = d > bound
-    if bad.any():
-        i = tuple(np.argwhere(bad)[0])
-        raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound, first at {i}: "
-                             f"got {got[i]!r} ref {ref[i]!r}")
-    return {"rel_mean": float(rel_mean), "exact_frac": float(np.mean(got_bits == ref_bits))}
+    stated = 2 * f16.ulp(ref) + 1e-3 * np.abs(ref)
+    exact = np.mean(got_bits == ref_bits) if d.size else 1.0
+    return _finish(what, got, ref, d, stated, fp32_floor(mass, k), mass, _rel_mean(d, ref), exact)
