@@ -58,6 +58,22 @@ def test_moe_config(gpu):
     assert (c[torch.from_numpy(pad).to(gpu)].float().cpu() == 1536.0).all()
 
 
+def test_down_projection_shape(gpu):
+    """The MoE chain's down projection: 16 experts with weights [N = 7168, K = 2048], the grouped
+    configuration's Dirichlet(1) counts over 4096 tokens, 128-row padding."""
+    case = workloads.moe_case(n=7168, k=2048, seed=6)
+    bq = torch.stack([w.q for w in case.weights])
+    bs = torch.stack([w.s for w in case.weights])
+    q, s, q_ref, s_ref = quant_gpu_checked(case.act, gpu, "moe down activations")
+    layout = case.layout.numpy()
+    out = torch.full((layout.size, 7168), 1536.0, dtype=torch.bfloat16, device=gpu)
+    c = _grouped(q, s, bq.to(gpu), bs.to(gpu), case.layout.to(gpu), "moe down", out=out)
+    rng = np.random.default_rng(7)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(7104, 7168), rng.choice(7168, 400, replace=False)]))
+    _check_rows(bits(c), q_ref, s_ref, bq.numpy(), bs.numpy(), layout, 6, cols, "moe down")
+    assert (c[torch.from_numpy(layout < 0).to(gpu)].float().cpu() == 1536.0).all()
+
+
 def test_poisoned_padding_rows_and_empty_blocks(gpu):
     """Padding rows full of NaN codes and NaN scales, plus a trailing all-padding block: valid rows
     are bitwise unchanged and no padding row is written."""

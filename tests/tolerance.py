@@ -11,7 +11,8 @@ Bounds (per output element, ref = the oracle's bf16 result, got = the kernel's):
     worst-case error of float32 accumulation in any order (at most one rounding
     per product-sum step inside a 128-wide block, one for the scale product and
     one per block promotion), which only matters where the sum cancels to near
-    zero and 1e-3 |ref| gives no room.
+    zero and 1e-3 |ref| gives no room. Every comparison records how far its worst
+    element went past the stated bound (RECORDS; printed at the end of a session).
 
 Hardware block dot (only for inputs spread over the whole e4m3 range): the gfx950
 FP8 matrix-core instruction does not add its 128 products like IEEE float32. A
@@ -117,9 +118,21 @@ def reference(a_q, a_s, b_q, b_s, rows=None, cols=None):
     return rows, cols, bf16.to_bits(acc), mass
 
 
+# The floor of the float-scale GEMMs: the worst-case error of IEEE float32 accumulation in any
+# order, (K/128 + 130) 2**-24 mag (one rounding per product-sum step inside a 128-wide block, one
+# for the scale product, one per block promotion). Over the GPU suite (285 comparisons, 25.9 M
+# outputs) the worst element went past the stated bound by 0.42 of it (the MoE down projection
+# at the benchmark's size, whose requantized SwiGLU activations spread their products widest);
+# 0.25 on every dense workload. A floor of 2**-20 of the absolute block sum,
+# sum_kb |P_kb As Bs|, does not hold: the hardware's errors follow the size of the products
+# before their cancellation inside a block, and went up to 449x past it (2.5x on the page-2
+# case).
+FP32_FLOOR_ETA = 2.0**-24
+
+
 def fp32_floor(mass: Mass, k) -> np.ndarray:
-    """Worst-case error of float32 accumulation in any order: (K/128 + 130) 2**-24 mag."""
-    return (k / 128 + 130) * 2.0**-24 * mass.mag
+    """(K/128 + 130) 2**-24 mag: the worst case of float32 accumulation in any order."""
+    return (k / 128 + 130) * FP32_FLOOR_ETA * mass.mag
 
 
 def e8_floor(mass: Mass, k) -> np.ndarray:
@@ -135,11 +148,13 @@ def _record(what, d, stated, mass: Mass, floor, extra=None):
     with np.errstate(divide="ignore", invalid="ignore"):
         r_floor = np.where(excess > 0, excess / floor, 0.0)
         r_a13 = np.where(excess > 0, excess / a13, 0.0)
+        r_stated = np.where(d > 0, d / stated, 0.0)
     rec = {
         "test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
         "what": what,
         "n": int(d.size),
         "over_stated": int((excess > 0).sum()),
+        "worst_over_stated": float(r_stated.max()) if d.size else 0.0,
         "worst_over_floor": float(r_floor.max()) if d.size else 0.0,
         "worst_over_a13": float(r_a13.max()) if d.size else 0.0,
     }
