@@ -292,6 +292,42 @@ def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Te
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # BFP8_NOALLOC_SCRATCH_BYTES
+
+
+def linear_noalloc(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out: torch.Tensor,
+                   bias: torch.Tensor | None = None) -> torch.Tensor:
+    """linear() through bfp8_linear_noalloc: no workspace, the quantized activations are staged in
+    the library's fixed device array (at most NOALLOC_SCRATCH_BYTES of staging). The caller passes
+    the output, so the call allocates nothing; calls that overlap in time on one device race on the
+    array."""
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise NotImplementedError(f"linear takes bfloat16 or float16 activations, got {x.dtype}")
+    _require(x, "x", x.dtype, 2)
+    w_q = _as_u8(w_q, "w_q")
+    _require(w_q, "w_q", torch.uint8, 2)
+    _require(w_s, "w_s", torch.float32, 2)
+    _require(out, "out", x.dtype, 2)
+    if x.stride(1) != 1 or w_q.stride(1) != 1 or w_s.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("x, w_q, w_s and out must be contiguous along their last dimension")
+    m, k = x.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k or tuple(out.shape) != (m, n):
+        raise ValueError(f"shapes disagree: x {tuple(x.shape)}, w_q {tuple(w_q.shape)}, out {tuple(out.shape)}")
+    if tuple(w_s.shape) != (-(-n // 128), -(-k // 128)):
+        raise ValueError(f"w_s shape {tuple(w_s.shape)} does not match N={n}, K={k}")
+    if bias is not None:
+        _require(bias, "bias", x.dtype, 1)
+        if bias.shape[0] != n or bias.stride(0) != 1:
+            raise ValueError("bias must be a contiguous vector of length N")
+    st = _native.lib().bfp8_linear_noalloc(
+        x.data_ptr(), _IN_DTYPES[x.dtype], m, k, x.stride(0), w_q.data_ptr(), w_q.stride(0), w_s.data_ptr(),
+        w_s.stride(0), bias.data_ptr() if bias is not None else None, out.data_ptr(), out.stride(0), n,
+        _stream(x.device))
+    _check(st, "bfp8_linear_noalloc")
+    return out
+
+
 def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
     """UE8M0 scale codes as uint8 (float8_e8m0fnu tensors are viewed as their bytes)."""
     if t.dtype == torch.float8_e8m0fnu:

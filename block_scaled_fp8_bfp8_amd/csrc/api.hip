@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "bfp8.h"
@@ -234,6 +235,75 @@ LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+namespace {
+
+// The linear layer on a given workspace (validation, then the quantizer and the GEMM).
+bfp8_status_t linear_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
+                          int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
+                          int64_t ldc, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x_dtype != BFP8_IN_BF16 && x_dtype != BFP8_IN_F16)
+    return fail(BFP8_ERR_UNSUPPORTED,
+                "the linear layer takes bf16 or fp16 activations (its output has their dtype), got x_dtype %d", x_dtype);
+  if (!aligned(bias, 2)) return fail(BFP8_ERR_MISALIGNED, "bias must be 2-byte aligned");
+  if (workspace && !aligned(workspace, 256)) return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  // Shapes first (a negative or oversized size must not reach the workspace arithmetic).
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
+  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
+  if (K % 16 != 0) return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 16", (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(BFP8_ERR_UNSUPPORTED, "M, N and K must each be at most 2^30");
+  const size_t need = bfp8_linear_workspace_bytes(M, N, K);
+  const int64_t Kp = (K + bfp8::kBlock - 1) / bfp8::kBlock * bfp8::kBlock;  // row stride of the codes
+  if (M > 0 && (!workspace || workspace_bytes < need))
+    return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  bfp8_status_t st = BFP8_OK;
+  const LinearLayout L = linear_layout(M, N, K);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* q = M > 0 ? ws : nullptr;
+  float* as = M > 0 ? reinterpret_cast<float*>(ws + L.as_off) : nullptr;
+  void* gws = M > 0 ? static_cast<void*>(ws + L.gemm_off) : nullptr;
+  const size_t gws_bytes = M > 0 ? workspace_bytes - L.gemm_off : 0;
+  st = check_quant_args(x, x_dtype, M, K, ldx, q, Kp, as, M);
+  if (st != BFP8_OK) return st;
+  st = check_gemm_args(q, Kp, as, M, b, ldb, bs, ld_bs, c, ldc, M, N, K, gws, gws_bytes, false);
+  if (st != BFP8_OK) return st;
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, Kp, as, M, false, (hipStream_t)stream), "quant_act");
+  if (st != BFP8_OK) return st;
+  return launch_dense(q, Kp, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream, false,
+                      x_dtype == BFP8_IN_F16);
+}
+
+// Staging of bfp8_linear_noalloc: one array per device, resolved once per device with that
+// device current. The array's name is only a host-side handle; kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[BFP8_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+bfp8_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BFP8_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BFP8_ERR_DEVICE, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(BFP8_ERR_DEVICE, "hipGetSymbolAddress of the staging array failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BFP8_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b, int64_t ldb,
@@ -329,40 +399,31 @@ size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
                           int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
                           int64_t ldc, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
-  if (x_dtype != BFP8_IN_BF16 && x_dtype != BFP8_IN_F16)
+  return linear_impl(x, x_dtype, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, workspace, workspace_bytes, stream);
+}
+
+bfp8_status_t bfp8_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
+                                  int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
+                                  int64_t ldc, int64_t N, void* stream) {
+  // Sizes first, on the host: a layer whose staging does not fit the device array is rejected
+  // before any HIP call.
+  if (M < 0 || N < 1 || K < 1 || K % 16 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return linear_impl(x, x_dtype, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, nullptr, 0, stream);
+  const size_t need = M > 0 ? linear_layout(M, N, K).total : 0;
+  if (need > BFP8_NOALLOC_SCRATCH_BYTES)
     return fail(BFP8_ERR_UNSUPPORTED,
-                "the linear layer takes bf16 or fp16 activations (its output has their dtype), got x_dtype %d", x_dtype);
-  if (!aligned(bias, 2)) return fail(BFP8_ERR_MISALIGNED, "bias must be 2-byte aligned");
-  if (workspace && !aligned(workspace, 256)) return fail(BFP8_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-  // Shapes first (a negative or oversized size must not reach the workspace arithmetic).
-  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
-  if (N < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "N = %lld must be >= 1", (long long)N);
-  if (K < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "K = %lld must be >= 1", (long long)K);
-  if (K % 16 != 0) return fail(BFP8_ERR_UNSUPPORTED, "K = %lld is not a multiple of 16", (long long)K);
-  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
-    return fail(BFP8_ERR_UNSUPPORTED, "M, N and K must each be at most 2^30");
-  const size_t need = bfp8_linear_workspace_bytes(M, N, K);
-  const int64_t Kp = (K + bfp8::kBlock - 1) / bfp8::kBlock * bfp8::kBlock;  // row stride of the codes
-  if (M > 0 && (!workspace || workspace_bytes < need))
-    return fail(BFP8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-  bfp8_status_t st = BFP8_OK;
-  const LinearLayout L = linear_layout(M, N, K);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* q = M > 0 ? ws : nullptr;
-  float* as = M > 0 ? reinterpret_cast<float*>(ws + L.as_off) : nullptr;
-  void* gws = M > 0 ? static_cast<void*>(ws + L.gemm_off) : nullptr;
-  const size_t gws_bytes = M > 0 ? workspace_bytes - L.gemm_off : 0;
-  st = check_quant_args(x, x_dtype, M, K, ldx, q, Kp, as, M);
+                "M x K = %lld x %lld needs %zu bytes of staging; bfp8_linear_noalloc holds at most %zu "
+                "(use bfp8_linear with a caller workspace)",
+                (long long)M, (long long)K, need, (size_t)BFP8_NOALLOC_SCRATCH_BYTES);
+  if (M == 0)
+    return linear_impl(x, x_dtype, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, nullptr, 0, stream);
+  bfp8_status_t st = check_device();
   if (st != BFP8_OK) return st;
-  st = check_gemm_args(q, Kp, as, M, b, ldb, bs, ld_bs, c, ldc, M, N, K, gws, gws_bytes, false);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
   if (st != BFP8_OK) return st;
-  if (M == 0) return ok();
-  st = check_device();
-  if (st != BFP8_OK) return st;
-  st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, Kp, as, M, false, (hipStream_t)stream), "quant_act");
-  if (st != BFP8_OK) return st;
-  return launch_dense(q, Kp, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream, false,
-                      x_dtype == BFP8_IN_F16);
+  return linear_impl(x, x_dtype, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, ws, BFP8_NOALLOC_SCRATCH_BYTES,
+                     stream);
 }
 
 // ---- MoE chain ------------------------------------------------------------------------------

@@ -29,7 +29,9 @@
  * Conventions shared by all entry points
  *   - Ownership: the caller allocates and owns every buffer (inputs, outputs,
  *     workspace). The library never allocates, frees or copies between host
- *     and device; it keeps only per-device cached properties.
+ *     and device; it keeps only per-device cached properties and the fixed
+ *     staging array of bfp8_linear_noalloc (BFP8_NOALLOC_SCRATCH_BYTES on each
+ *     device the library is loaded on, held until the process ends).
  *   - Asynchrony: work is enqueued on `stream`; BFP8_OK means "enqueued".
  *     Errors in the arguments are found on the host before any HIP call and
  *     leave every buffer untouched.
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 8
+#define BFP8_ABI_VERSION 9
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -219,6 +221,30 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
                           const uint16_t* bias, uint16_t* c, int64_t ldc, int64_t N,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the device array that bfp8_linear_noalloc stages the quantized activations in. */
+#define BFP8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * bfp8_linear without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * same computation and kernels as bfp8_linear, bit for bit; the quantized activations are
+ * staged in a file-scope device array of BFP8_NOALLOC_SCRATCH_BYTES bytes that every device
+ * holds once the library is loaded (its address is looked up once per device, on the first
+ * call on that device). Nothing is allocated or freed by the call.
+ *   Limit: the staging must fit the array, i.e. bfp8_linear_workspace_bytes(M, N, K) <=
+ *          BFP8_NOALLOC_SCRATCH_BYTES (e.g. M = 2048 at K <= 30720); larger layers return
+ *          BFP8_ERR_UNSUPPORTED (checked on the host before any HIP call) and should call
+ *          bfp8_linear with a workspace.
+ *   Sharing: all calls on one device share its array and leave their staging in it (no part
+ *          of it needs clearing: each call writes every byte it reads). Calls that overlap in
+ *          time on one device (different streams or host threads without ordering) race on it;
+ *          calls ordered on one stream do not.
+ * Arguments, validation and errors otherwise as bfp8_linear.
+ */
+bfp8_status_t bfp8_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                  const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                                  const uint16_t* bias, uint16_t* c, int64_t ldc, int64_t N, void* stream);
 
 /*
  * bfp8_gemm with an fp16 output: C[m, n] = fp16(sum_kb P_kb * As * Bs), rounded to nearest even

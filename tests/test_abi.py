@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 8
+    assert lib.bfp8_abi_version() == 9
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -216,6 +216,29 @@ def test_linear_rejections(lib, kw, status):
 
 def test_linear_m_zero_ok_without_device(lib):
     assert _linear(lib, M=0, x=None, ws=None, wsb=0) == _native.BFP8_OK
+
+
+def _linear_noalloc(lib, x=A, dt=1, M=8, K=256, ldx=256, b=B, ldb=256, bs=BS, ld_bs=2, bias=None, c=C, ldc=64, N=64):
+    return lib.bfp8_linear_noalloc(x, dt, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=2048, K=40960, ldx=40960, ldb=40960, ld_bs=320), _native.BFP8_ERR_UNSUPPORTED),  # staging > 64 MiB
+    (dict(M=-1), _native.BFP8_ERR_INVALID_ARGUMENT),
+    (dict(K=200, ldx=256, ldb=256), _native.BFP8_ERR_UNSUPPORTED),
+    (dict(dt=0, M=0), _native.BFP8_ERR_UNSUPPORTED),
+])
+def test_linear_noalloc_rejections_on_the_host(lib, kw, status):
+    assert _linear_noalloc(lib, **kw) == status, lib.bfp8_last_error_message()
+    assert len(lib.bfp8_last_error_message()) > 0
+
+
+def test_linear_noalloc_limit(lib):
+    # the largest layer at M = 2048 whose staging fits 64 MiB, and one K block more
+    assert lib.bfp8_linear_workspace_bytes(2048, 64, 30720) <= 64 << 20
+    assert lib.bfp8_linear_workspace_bytes(2048, 64, 32768) > 64 << 20
+    assert _linear_noalloc(lib, M=2048, K=32768, ldx=32768, ldb=32768, ld_bs=256) == _native.BFP8_ERR_UNSUPPORTED
+    assert _linear_noalloc(lib, M=0, x=None) == _native.BFP8_OK
 
 
 def _gemm_e8(lib, a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=4, c=C, ldc=64, M=8, N=64, K=256):
