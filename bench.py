@@ -125,6 +125,74 @@ def cpu_baseline(rows_cap: int = 8192):
     }
 
 
+def measure_ceilings(torch, np, dev, stream, graph_time_us) -> dict:
+    """Ceilings measured on this device in this run (libbfp8_probes.so):
+      * fp8_mfma_loop_tflops: 256 workgroups of 8 waves (the GEMMs' occupancy, 2 waves per SIMD)
+        issuing independent 16x16x128 FP8 MFMAs from registers; fp8_mfma_promote_tflops: the same
+        with the four promotion FMAs per MFMA of the float-scale method;
+      * hbm_read_1gib_gbs: one launch streaming 1 GiB (4x the last-level cache);
+      * hbm_read_16mib_cold_us: one launch streaming 16 MiB (the N = K = 4096 weight) that is not in
+        the last-level cache (40 buffers read in turn), the floor of a small-M GEMM launch;
+      * l2_to_lds_copy_gbs: 256 workgroups copying L2-resident rows into LDS with the direct-to-LDS
+        loads the GEMMs stage their operands with (8 rows x 128 bytes per copy, 8 per wave in flight)."""
+    from block_scaled_fp8_bfp8_amd import _native
+
+    pr = _native.probes()
+    wgs, iters = 256, 2000
+    out = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    res = {}
+    # each launch runs about half a millisecond: timed one by one with events on the launch stream
+    for mode, key in ((0, "fp8_mfma_loop_tflops"), (1, "fp8_mfma_promote_tflops"), (2, "fp8_mfma_zero_c_tflops")):
+        times = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if pr.bfp8_probe_mfma_loop(out.data_ptr(), wgs, iters, mode, stream.cuda_stream):
+                raise RuntimeError("mfma probe launch failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(times[1:]))
+        res[key] = round(pr.bfp8_probe_mfma_loop_flops(wgs, iters) / (us * 1e-6) / 1e12, 1)
+    sink = torch.empty(2048 * 512, dtype=torch.int32, device=dev)
+    big = torch.zeros(2**30 // 4, dtype=torch.int32, device=dev)
+
+    def read_big(n):
+        for _ in range(n):
+            if pr.bfp8_probe_stream_read(big.data_ptr(), 2**30, sink.data_ptr(), 2048,
+                                         torch.cuda.current_stream(dev).cuda_stream):
+                raise RuntimeError("read probe launch failed")
+    res["hbm_read_1gib_gbs"] = round(2**30 / (graph_time_us(read_big, 2) * 1e-6) / 1e9, 1)
+    del big
+    small = [torch.zeros(2**24 // 4, dtype=torch.int32, device=dev) for _ in range(40)]
+
+    def read_small(n):
+        for j in range(n):
+            if pr.bfp8_probe_stream_read(small[j % len(small)].data_ptr(), 2**24, sink.data_ptr(), 1024,
+                                         torch.cuda.current_stream(dev).cuda_stream):
+                raise RuntimeError("read probe launch failed")
+    us16 = graph_time_us(read_small, 40)
+    res["hbm_read_16mib_cold_us"] = round(us16, 2)
+    res["hbm_read_16mib_cold_gbs"] = round(2**24 / (us16 * 1e-6) / 1e9, 1)
+    del small
+    # direct-to-LDS copies (the GEMMs' operand path) of 8 rows x 128 bytes, 8 per wave in flight,
+    # from a 2 MiB window that stays in the L2 caches
+    win = torch.zeros(2**21, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if pr.bfp8_probe_copy_lds(win.data_ptr(), 64, 1024, 8, 1, sink.data_ptr(), 256, stream.cuda_stream):
+            raise RuntimeError("copy probe launch failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    res["l2_to_lds_copy_gbs"] = round(256 * 8 * 1024 * 1024 / (float(np.median(times[1:])) * 1e-6) / 1e9, 1)
+    del win
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +206,12 @@ def main() -> int:
                     help="skip the transformer-linear and MoE grouped-GEMM configurations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (for counter calibration under rocprofv3)")
+    ap.add_argument("--only-config", choices=["transformer_linear", "moe_grouped", "moe_chain"], default=None,
+                    help="profile helper: run only this configuration (no sweep, no table)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and HBM-read ceilings")
+    ap.add_argument("--ceilings-only", action="store_true", help="profile helper: only the ceiling probes")
+    ap.add_argument("--schedule", choices=["auto", "small_m", "tiled"], default="auto",
+                    help="profile helper: force one GEMM schedule")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -156,8 +230,9 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    bfp8.set_schedule(args.schedule)
     stream = torch.cuda.current_stream(dev)
-    sweep = (args.only_m,) if args.only_m else SWEEP_M
+    sweep = (args.only_m,) if args.only_m else () if args.only_config or args.ceilings_only else SWEEP_M
 
     # ---- inputs, resident in HBM before any timing -------------------------------------
     w = workloads.square_weight()
@@ -193,15 +268,17 @@ def main() -> int:
 
     capture_stream = torch.cuda.Stream(dev)
     step_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(capture_stream):
-        graph_part()
-        capture_stream.synchronize()
-        with torch.cuda.graph(step_graph, stream=capture_stream):
+    if sweep:
+        with torch.cuda.stream(capture_stream):
             graph_part()
+            capture_stream.synchronize()
+            with torch.cuda.graph(step_graph, stream=capture_stream):
+                graph_part()
     torch.cuda.synchronize()
 
     def step(dom_events=None):
-        step_graph.replay()
+        if sweep:
+            step_graph.replay()
         if DOMINANT_M in sweep:
             i = rot[0] % copies
             rot[0] += 1
@@ -274,7 +351,7 @@ def main() -> int:
         return float(np.median(trials))
 
     per_m = {}
-    if not args.no_table:
+    if not args.no_table and sweep:
 
         w8 = workloads.weight_ue8m0(N, K, seed=1)  # the same e4m3 codes as the sweep's weight
         if not torch.equal(w8.q, w.q):
@@ -321,9 +398,12 @@ def main() -> int:
     # ---- the other workload configurations (not part of the step): the FP8 linear layer on the
     # hidden-5120 transformer shapes, and the M-grouped contiguous MoE GEMM ----
     configs = {}
-    if not args.no_configs and not args.only_m:
+    want = ((lambda name: args.only_config in (None, name)) if not args.no_configs and not args.only_m and not args.ceilings_only
+            else (lambda name: False))
+    if want("transformer_linear") or want("moe_grouped") or want("moe_chain"):
         del bq, bsc  # the sweep's weight copies
         torch.cuda.empty_cache()
+    if want("transformer_linear"):
         lin = {}
         for layer, (n_l, k_l) in workloads.TRANSFORMER_LAYERS.items():
             wl = workloads.transformer_weight(layer)
@@ -351,6 +431,7 @@ def main() -> int:
         configs["transformer_linear"] = {"what": "bfp8_linear (bf16 x quantized per 1x128 group, blockwise FP8 GEMM, "
                                                  "bf16 out), graph replay of back-to-back calls",
                                          "layers": lin}
+    if want("moe_grouped"):
         case = workloads.moe_case()
         bq_g = torch.stack([w_.q for w_ in case.weights]).to(dev)
         bs_g = torch.stack([w_.s for w_ in case.weights]).to(dev)
@@ -376,6 +457,7 @@ def main() -> int:
         del bq_g, bs_g
         torch.cuda.empty_cache()
 
+    if want("moe_chain"):
         # MoE expert chain: 512 tokens, top-8 of 16 experts (4096 pairs, like the grouped
         # configuration), hidden 7168, intermediate 2048 (gate+up weights [16, 4096, 7168]).
         t_c, k_c, e_c, h_c, i_c = 512, 8, 16, 7168, 2048
@@ -420,8 +502,21 @@ def main() -> int:
         del wts_c, ws_c, proj_c, out_c, q_c, q2_c
         torch.cuda.empty_cache()
 
+    ceilings = None
+    if args.ceilings_only or (not args.no_ceilings and not args.only_m and not args.only_config):
+        ceilings = measure_ceilings(torch, np, dev, stream, graph_time_us)
+        log("ceilings: " + json.dumps(ceilings))
+        if roofline is not None:
+            roofline["peak_measured"] = ceilings["fp8_mfma_loop_tflops"]
+            roofline["frac_measured"] = round(roofline["achieved"] / ceilings["fp8_mfma_loop_tflops"], 4)
+        for m_, e_ in per_m.items():
+            if e_["bound"] == "hbm":  # against one launch streaming the weight's 16 MiB from HBM
+                e_["frac_measured"] = round(ceilings["hbm_read_16mib_cold_us"] / e_["gemm_us"], 4)
+            else:
+                e_["frac_measured"] = round(e_["tflops"] / ceilings["fp8_mfma_loop_tflops"], 4)
+
     cpu = None
-    if not args.no_cpu_baseline and not args.only_m:
+    if not args.no_cpu_baseline and not args.only_m and not args.only_config and not args.ceilings_only:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline()
         log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
@@ -443,6 +538,7 @@ def main() -> int:
                                "quantization + GEMM per M",
                    "n": N, "k": K, "m": list(sweep), "mode": args.mode, "weight_copies": copies},
         "roofline": roofline,
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
         "per_m": per_m,
         "configs": configs,

@@ -86,3 +86,30 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = argtypes
         _lib = handle
     return _lib
+
+
+# The benchmark's measurement probes (libbfp8_probes.so, include/bfp8_probes.h).
+PROBES_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbfp8_probes.so")
+PROBE_SIGNATURES = [
+    ("bfp8_probe_mfma_loop", ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    ("bfp8_probe_mfma_loop_flops", ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
+    ("bfp8_probe_stream_read", ctypes.c_int, [_vp, _sz, _vp, ctypes.c_int, _vp]),
+    ("bfp8_probe_copy_lds", ctypes.c_int,
+     [_vp, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_int, _vp]),
+]
+_probes = None
+
+
+def probes() -> ctypes.CDLL:
+    """The loaded libbfp8_probes.so (raises LibraryMissing if it has not been built)."""
+    global _probes
+    if _probes is None:
+        if not os.path.exists(PROBES_LIB_PATH):
+            raise LibraryMissing(f"{PROBES_LIB_PATH} is missing: build it with `python -m block_scaled_fp8_bfp8_amd.build`")
+        handle = ctypes.CDLL(PROBES_LIB_PATH)
+        for name, restype, argtypes in PROBE_SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = restype
+            fn.argtypes = argtypes
+        _probes = handle
+    return _probes

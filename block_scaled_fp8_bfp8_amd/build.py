@@ -41,10 +41,21 @@ def hipcc() -> str:
     return path
 
 
+PROBES_LIB_NAME = "libbfp8_probes.so"
+PROBES_LIB_PATH = os.path.join(PKG_DIR, PROBES_LIB_NAME)
+PROBES_SOURCES = ["probes.hip"]
+
+
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every HIP source into libbfp8.so; returns the library path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    """Compile every HIP source into libbfp8.so (and the benchmark's probes into
+    libbfp8_probes.so); returns the library path."""
+    _compile(PROBES_SOURCES, PROBES_LIB_PATH, verbose, extra_flags)
+    return _compile(SOURCES, LIB_PATH, verbose, extra_flags)
+
+
+def _compile(sources: list[str], lib_path: str, verbose: bool, extra_flags: list[str] | None) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -55,8 +66,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -328,3 +328,28 @@ def test_expand_weight_scale_rejections(lib, kw, status):
     a = dict(s=BS, N=300, K=256, bs=AS, ld_bs=2)
     a.update(kw)
     assert lib.bfp8_expand_weight_scale(a["s"], a["N"], a["K"], a["bs"], a["ld_bs"], None) == status
+
+
+PROBES_HEADER = os.path.join(ROOT, "include", "bfp8_probes.h")
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's probe library (its own .so, outside the GEMM path) exports and binds every
+    function its header declares, and rejects bad arguments before launching anything."""
+    text = re.sub(r"/\*.*?\*/", "", open(PROBES_HEADER).read(), flags=re.S)
+    names = set(re.findall(r"\b(bfp8_probe_\w+)\s*\(", text))
+    pr = _native.probes()
+    assert names == {n for n, _, _ in _native.PROBE_SIGNATURES}
+    for n in names:
+        assert hasattr(pr, n), f"{n} not exported"
+    assert pr.bfp8_probe_mfma_loop_flops(256, 2000) == 256 * 8 * 2000 * 8 * 2.0 * 16 * 16 * 128
+    fake = 1 << 40
+    assert pr.bfp8_probe_mfma_loop(fake, 256, 10, 3, None) == 1  # unknown mode
+    assert pr.bfp8_probe_mfma_loop(None, 256, 10, 0, None) == 1
+    assert pr.bfp8_probe_stream_read(fake + 8, 1 << 20, fake, 64, None) == 1  # misaligned source
+    assert pr.bfp8_probe_stream_read(fake, 1000, fake, 64, None) == 1  # not whole 16-byte words
+    assert pr.bfp8_probe_copy_lds(fake, 3, 64, 8, 1, fake, 1, None) == 1  # groups not a power of two
+    assert pr.bfp8_probe_copy_lds(fake, 4, 60, 8, 1, fake, 1, None) == 1  # iters not a multiple of inflight
+    assert pr.bfp8_probe_copy_lds(fake, 4, 64, 16, 2, fake, 1, None) == 1  # wide rows need inflight 8
+    assert pr.bfp8_probe_copy_lds(fake, 4, 64, 8, 5, fake, 1, None) == 1
+    assert pr.bfp8_probe_copy_lds(fake, 4, 64, 8, -1, fake, 1, None) == 1

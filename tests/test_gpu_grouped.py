@@ -102,6 +102,41 @@ def test_poisoned_padding_rows_and_empty_blocks(gpu):
     _check_rows(bits(c_clean), q_ref, s_ref, bq.numpy(), bs.numpy(), layout, 200, np.arange(n), "grouped small")
 
 
+def test_mixed_expert_blocks_equal_dense(gpu):
+    """Experts of 256, 128, 384, 0 and 200 rows, then a block of padding only: 128-row blocks e0 e0
+    e1 e2 e2 e2 e4 e4 (the last 72 rows + padding) and one skipped block, so that the expert changes
+    inside a 256-row tile, one expert is empty and the last tiles are part or all padding. Every
+    valid row against the oracle, padding rows unwritten, and each expert's rows bit-equal to a
+    dense GEMM of those rows with its weights."""
+    g_count, n, k = 5, 512, 1024
+    counts = np.array([256, 128, 384, 0, 200])
+    layout = np.concatenate([workloads.moe_layout(counts), np.full(128, -1, np.int32)])
+    m = layout.size
+    assert m == 9 * 128
+    ws = [workloads.weight(n, k, seed=950 + g) for g in range(g_count)]
+    bq = torch.stack([w.q for w in ws])
+    bs = torch.stack([w.s for w in ws])
+    x = workloads.act_normal_bf16(m, k, seed=951)
+    x[torch.from_numpy(layout < 0)] = 0
+    q, s, q_ref, s_ref = quant_gpu_checked(x, gpu, "mixed blocks")
+    out = torch.full((m, n), -7.0, dtype=torch.bfloat16, device=gpu)
+    c = _grouped(q, s, bq.to(gpu), bs.to(gpu), torch.from_numpy(layout).to(gpu), "mixed blocks", out=out)
+    cb = bits(c)
+    assert (c[torch.from_numpy(layout < 0).to(gpu)].float() == -7.0).all()
+    _check_rows(cb, q_ref, s_ref, bq.numpy(), bs.numpy(), layout, 400, np.arange(n), "mixed blocks")
+    # the tiled dense kernel adds every output's K blocks in the same order as the grouped one
+    bfp8.set_schedule("tiled")
+    try:
+        for g in np.unique(layout[layout >= 0]):
+            rows = torch.from_numpy(np.nonzero(layout == g)[0]).to(gpu)
+            s_g = s[rows].t().contiguous().t()  # group-major, as quant_act lays scales out
+            d = bfp8.gemm(q[rows].contiguous(), s_g, ws[g].q.to(gpu), ws[g].s.to(gpu))
+            torch.cuda.synchronize()
+            assert torch.equal(d.view(torch.int16), c[rows].view(torch.int16)), f"expert {g}"
+    finally:
+        bfp8.set_schedule("auto")
+
+
 def test_single_group_equals_dense_tiled(gpu):
     """G = 1 with no padding is the dense product. At 2048 x 2048 the dense tiled plan fills the
     chip without splitting K, so both sum every output block by block in the same order and
