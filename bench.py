@@ -423,7 +423,8 @@ def main() -> int:
                 us = graph_time_us(lin_calls, 2 * n_copies if m < 2048 else n_copies)
                 kb_l = k_l // 128
                 alg = 2 * m * k_l + n_l * k_l + (-(-n_l // 128)) * kb_l * 4 + 2 * m * n_l
-                lin[layer][str(m)] = {"n": n_l, "k": k_l, **roofline_entry(us, 2.0 * m * n_l * k_l, alg)}
+                lin[layer][str(m)] = {"n": n_l, "k": k_l, "one_launch": bfp8.linear_fuses(m, n_l, k_l),
+                                      **roofline_entry(us, 2.0 * m * n_l * k_l, alg)}
                 log(f"linear {layer:8s} M={m:5d} N={n_l} K={k_l}: {us:8.2f} us  {lin[layer][str(m)]['tflops']:8.1f} "
                     f"TFLOP/s  {lin[layer][str(m)]['bound']} frac {lin[layer][str(m)]['frac']:.3f}")
             del wq_l, ws_l

@@ -23,7 +23,7 @@ from . import _native
 from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
-    "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes",
+    "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes", "linear_fuses",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
     "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
     "moe_forward_workspace_bytes", "nn_to_nt_weights", "pad_k", "expand_act_scales", "expand_weight_scale", "set_schedule", "get_schedule", "schedule_for",
@@ -647,6 +647,12 @@ def expand_weight_scale(s: torch.Tensor, n: int, k: int) -> torch.Tensor:
 def linear_workspace_bytes(m: int, n: int, k: int) -> int:
     """Bytes of device workspace that linear() needs for an [m, k] x [n, k] layer."""
     return _native.lib().bfp8_linear_workspace_bytes(m, n, k)
+
+
+def linear_fuses(m: int, n: int, k: int, ldx: int | None = None) -> bool:
+    """Whether linear() with these sizes runs one kernel that quantizes the activations inside
+    the GEMM (small M), rather than the quantizer and then the GEMM."""
+    return bool(_native.lib().bfp8_linear_fuses(m, n, k, k if ldx is None else ldx))
 
 
 def set_schedule(name: str) -> None:

@@ -57,6 +57,7 @@ SIGNATURES = [
     ("bfp8_linear_workspace_bytes", _sz, [_i64, _i64, _i64]),
     ("bfp8_linear", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_linear_fuses", ctypes.c_int, [_i64, _i64, _i64, _i64]),
     ("bfp8_linear_noalloc", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _vp]),
     ("bfp8_set_schedule", ctypes.c_int, [ctypes.c_int]),

@@ -237,6 +237,15 @@ LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {
 
 namespace {
 
+// Whether the linear layer takes the one-launch path (bfp8_linear_fuses). The kernel's copies
+// address the activation rows with a 32-bit byte offset, like A's.
+bool linear_fuses(int64_t M, int64_t N, int64_t K, int64_t ldx) {
+  if (M < 1 || N < 1 || K < 1 || K % 16 || ldx < K || M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
+  const int64_t Kp = (K + bfp8::kBlock - 1) / bfp8::kBlock * bfp8::kBlock;
+  return choose_schedule(M, N, K) == BFP8_SCHED_SMALL_M && bfp8::ksplit_fused_shape(M, N, K) &&
+         (M - 1) * ldx * 2 + 2 * Kp <= kMaxOperandSpan;
+}
+
 // The linear layer on a given workspace (validation, then the quantizer and the GEMM).
 bfp8_status_t linear_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
                           int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,
@@ -271,6 +280,15 @@ bfp8_status_t linear_impl(const void* x, int x_dtype, int64_t M, int64_t K, int6
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
+  // Small M on the K-split schedule's 16 x 16 tile: one launch that quantizes the activations
+  // itself (bit-identical to the two launches below; the workspace is then not touched).
+  if (linear_fuses(M, N, K, ldx)) {
+    const bfp8::GemmArgs args{static_cast<const uint8_t*>(x), ldx, nullptr, 0, b, ldb, bs, ld_bs, c, ldc,
+                              (int)M, (int)N, (int)K, nullptr, 1, bias, false, x_dtype == BFP8_IN_F16};
+    return launched(bfp8::launch_gemm_ksplit_fused(args, x_dtype == BFP8_IN_F16 ? bfp8::kInF16 : bfp8::kInBf16,
+                                                   (hipStream_t)stream),
+                    "gemm_ksplit (fused quantization)");
+  }
   st = launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, Kp, as, M, false, (hipStream_t)stream), "quant_act");
   if (st != BFP8_OK) return st;
   return launch_dense(q, Kp, as, M, b, ldb, bs, ld_bs, bias, c, ldc, M, N, K, gws, stream, false,
@@ -401,6 +419,8 @@ bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int6
                           int64_t ldc, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
   return linear_impl(x, x_dtype, M, K, ldx, b, ldb, bs, ld_bs, bias, c, ldc, N, workspace, workspace_bytes, stream);
 }
+
+int bfp8_linear_fuses(int64_t M, int64_t N, int64_t K, int64_t ldx) { return linear_fuses(M, N, K, ldx) ? 1 : 0; }
 
 bfp8_status_t bfp8_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* b,
                                   int64_t ldb, const float* bs, int64_t ld_bs, const uint16_t* bias, uint16_t* c,

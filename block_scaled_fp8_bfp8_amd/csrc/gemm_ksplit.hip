@@ -29,7 +29,23 @@
 //     results bitwise reproducible without atomics or a global workspace, and each sum is
 //     rounded once to bf16;
 //   * UE8M0 scales (kE8): the scale codes are copied like the float scales, and the scaled
-//     MFMA applies 2^(ea - 127) * 2^(eb - 127) and accumulates into the wave's tile itself.
+//     MFMA applies 2^(ea - 127) * 2^(eb - 127) and accumulates into the wave's tile itself;
+//   * fused activation quantization (kFuse = kInBf16 or kInF16, 16-row tiles, M <= kQRows):
+//     the linear layer's bf16/fp16 activations are copied instead of codes, the wave's 64
+//     lanes covering only the kQRows (1, 4 or 8) rows quantized: 64 / kQRows lanes per row
+//     and 2 * kQRows consecutive elements per lane. Each lane quantizes its elements in
+//     registers (1x128 groups, the group's amax reduced over the row's lanes) with the
+//     per-token-group quantizer's arithmetic, so codes and scales are bit-identical to
+//     quantizing first, and writes the codes into the slot's kQRows rows of codes (the
+//     swizzled layout the fragment reads expect) and the scale beside them; fragment rows past
+//     kQRows read row r % kQRows (their results are never stored). The division by the group
+//     scale s is done as q0 = x * r, r = 1 / s correctly rounded, then q0 + (x - q0 * s) * r
+//     with fused multiply-adds and x's sign: that is the correctly rounded x / s for every
+//     bf16 and fp16 x and every scale the quantizer can produce, except quotients below 2^-10
+//     in magnitude, which all encode as zero of x's sign (checked exhaustively against the
+//     division); groups whose scale is infinite divide. Every workgroup of the grid repeats
+//     this for its M rows (about (N / 16) x kQRows x K element steps in all), which pays only
+//     where a separate quantizer launch costs more: small M, N and K.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -41,25 +57,39 @@ namespace bfp8 {
 
 namespace {
 
-template <int TN, int TM, int WAVES, int SLOTS, bool kE8>
+template <int TN, int TM, int WAVES, int SLOTS, bool kE8, int kFuse = 0, int kQRows = 16>
 __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) {
+  constexpr bool kFused = kFuse != 0;  // args.a holds bf16/fp16 activations (lda in elements)
+  static_assert(!kFused || (!kE8 && TM == 1 && (kFuse == kInBf16 || kFuse == kInF16)),
+                "fused quantization: float scales, 16 activation rows, bf16 or fp16 input");
+  static_assert(kQRows == 1 || kQRows == 4 || kQRows == 8 || kQRows == 16, "1, 4, 8 or 16 quantized rows");
+
   constexpr int BN = 16 * TN, BM = 16 * TM;
-  constexpr int kRows = BN + BM;
-  constexpr int kSlot = kRows * kBlock;           // bytes per slot
+  constexpr int kRows = kFused ? BN : BN + BM;    // 128-byte rows copied per K block
+  constexpr int kQLanes = 64 / kQRows;             // fused: lanes per quantized row
+  constexpr int kQElems = kBlock / kQLanes;        // fused: consecutive elements per lane
+  // fused: the lane's elements arrive as 16-byte pieces (8 elements), or for one row as one
+  // 4-byte piece (2 elements)
+  constexpr int kXPiece = kQRows == 1 ? 4 : 16;
+  constexpr int kXCopies = kFused ? kQElems * 2 / kXPiece : 0;
+  // bytes per slot: copied rows; fused: then the kQRows rows of codes and the staged 16-bit
+  // activations (kXCopies pieces of 64 lanes x kXPiece bytes)
+  constexpr int kSlot = kRows * kBlock + (kFused ? kQRows * kBlock + kXCopies * 64 * kXPiece : 0);
   constexpr int kPieces = kRows / 8;              // 1 KB (8-row) copies per K block
   // 64-lane scale copies per K block: 64 float scales each, or 256 UE8M0 codes (4 per lane).
-  constexpr int kAsCopies = kE8 ? 1 : (BM + 63) / 64;
+  constexpr int kAsCopies = kFused ? 0 : kE8 ? 1 : (BM + 63) / 64;
   constexpr int kScaleBytes = kE8 ? 1 : 4;
   static_assert(!kE8 || BM <= 256, "one copy holds the codes of 256 activation rows");
   using ScaleT = std::conditional_t<kE8, int, float>;
-  constexpr int kPerBlock = kPieces + kAsCopies;  // copies issued per K block
+  constexpr int kPerBlock = kPieces + kAsCopies + kXCopies;  // copies issued per K block
   constexpr int kTileFloats = BN * BM;
   static_assert(kBlock % BN == 0, "a wave's weight rows must share one scale strip");
   static_assert(kTileFloats * 4 <= SLOTS * kSlot, "the reduction reuses the wave's slots");
   static_assert(SLOTS >= 1 && SLOTS <= 3 && (SLOTS - 1) * kPerBlock < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t slots[WAVES][SLOTS][kSlot];
-  __shared__ __attribute__((aligned(16))) float as_slots[WAVES][SLOTS][kAsCopies * 64];
+  __shared__ __attribute__((aligned(16))) float as_slots[WAVES][SLOTS][(kAsCopies > 0 ? kAsCopies : 1) * 64];
+
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -84,11 +114,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
   }
   // Float scales: row m0 + 64 c + lane, clamped. UE8M0 codes: the dword of rows m0 + 4 lane ..,
   // clamped to the one holding row M - 1 (inside the row of codes: its length is a multiple of 4).
-  uint32_t as_voff[kAsCopies];
+  uint32_t as_voff[kAsCopies > 0 ? kAsCopies : 1];
 #pragma unroll
   for (int c = 0; c < kAsCopies; ++c)
     as_voff[c] = kE8 ? (uint32_t)min(m0 + 4 * lane, (M - 1) & ~3) : (uint32_t)min(m0 + c * 64 + lane, M - 1) * 4u;
   const uint8_t* asmat = static_cast<const uint8_t*>(args.as);
+  // Fused: lane l quantizes row qr = l / kQLanes, elements [qc, qc + kQElems) of each K block,
+  // copied in pieces of kXPiece bytes (piece j lands at stage byte 64 kXPiece j + kXPiece l). A
+  // piece past M or past K is not needed; it copies the block's first piece of row m0 instead
+  // (in bounds) and is zeroed after the read, so that every copy instruction is issued with
+  // the same count in flight (the waits below count them).
+  const int qr = lane / kQLanes, qc = (lane % kQLanes) * kQElems;
+  const bool x_row_ok = kFused && m0 + qr < M;
+  const uint32_t x_off = (uint32_t)((int64_t)(x_row_ok ? m0 + qr : m0) * args.lda * 2) + (x_row_ok ? 2u * qc : 0u);
+  const uint32_t x_off_spare = (uint32_t)((int64_t)m0 * args.lda * 2);
+  const uint32_t x_delta = x_off - x_off_spare;  // offset of the lane's piece 0 past the spare
+  auto x_piece_ok = [&](int kb, int j) __attribute__((always_inline)) {
+    return x_row_ok && qc + (kXPiece / 2) * j < (kb == KB - 1 ? k_tail : kBlock);
+  };
 
   auto issue = [&](int slot, int kb) __attribute__((always_inline)) {
     const uint8_t* bsrc = args.b + (int64_t)kb * kBlock;
@@ -99,6 +142,87 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
 #pragma unroll
     for (int c = 0; c < kAsCopies; ++c)
       copy4_to_lds(asmat + (int64_t)kb * args.ld_as * kScaleBytes, as_voff[c], lds_addr(&as_slots[w][slot][c * 64]));
+    if constexpr (kFused) {
+      const uint8_t* xsrc = args.a + (int64_t)kb * kBlock * 2;
+      const uint32_t xdst = dst + (uint32_t)((kRows + kQRows) * kBlock);
+#pragma unroll
+      for (int j = 0; j < kXCopies; ++j) {
+        const uint32_t voff = x_off_spare + (x_piece_ok(kb, j) ? x_delta + (uint32_t)(kXPiece * j) : 0u);
+        if constexpr (kXPiece == 16) {
+          copy16_to_lds(xsrc, voff, xdst + (uint32_t)(j * 64 * kXPiece));
+        } else {
+          copy4_to_lds(xsrc, voff, xdst + (uint32_t)(j * 64 * kXPiece));
+        }
+      }
+    }
+  };
+
+  // Fused: the lane's kQElems staged activations of a block (`raw`) -> e4m3 codes written to
+  // its row of the slot's activation rows (swizzled), and the row's group scale to `as_row`
+  // (the per-token-group quantizer's arithmetic).
+  auto quantize = [&](const uint32_t (&raw)[kXCopies > 0 ? kXCopies * kXPiece / 4 : 1], int kb, uint8_t* arows,
+                      float* as_row) __attribute__((always_inline)) {
+    float v[kQElems];
+#pragma unroll
+    for (int j = 0; j < kXCopies; ++j) {
+      const bool ok = x_piece_ok(kb, j);
+#pragma unroll
+      for (int i = 0; i < kXPiece / 4; ++i) {
+        const uint32_t p = ok ? raw[j * (kXPiece / 4) + i] : 0u;
+        const int e = (kXPiece / 2) * j + 2 * i;
+        if constexpr (kFuse == kInBf16) {
+          v[e] = __uint_as_float(p << 16);
+          v[e + 1] = __uint_as_float(p & 0xffff0000u);
+        } else {
+          v[e] = f16_value(p & 0xffffu);
+          v[e + 1] = f16_value(p >> 16);
+        }
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < kQElems; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int mask = 1; mask < kQLanes; mask <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mask));
+    const float s = fmaxf(amax, 1e-10f) / 448.0f;  // correctly rounded divide
+    float y[kQElems];
+    if (s < __builtin_huge_valf()) {
+      const float rcp = 1.0f / s;  // correctly rounded
+#pragma unroll
+      for (int i = 0; i < kQElems; ++i) {
+        const float q0 = v[i] * rcp;
+        const float e = fmaf(-q0, s, v[i]);  // exact
+        y[i] = fminf(fmaxf(copysignf(fmaf(e, rcp, q0), v[i]), -448.0f), 448.0f);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQElems; ++i) y[i] = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
+    }
+    uint32_t wq[(kQElems + 3) / 4];
+    if constexpr (kQElems == 2) {
+      wq[0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    } else {
+#pragma unroll
+      for (int d = 0; d < kQElems / 4; ++d) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * d], y[4 * d + 1], 0, false);
+        wq[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * d + 2], y[4 * d + 3], lo, true);
+      }
+    }
+    // codes of elements [qc, qc + kQElems): 2 or 8 bytes inside a 16-byte column, or whole columns
+    uint8_t* row = arows + qr * kBlock;
+    const int sw = lds_swizzle(BN + qr);
+    if constexpr (kQElems == 2) {
+      *reinterpret_cast<uint16_t*>(row + (((qc >> 4) ^ sw) << 4) + (qc & 15)) = (uint16_t)wq[0];
+    } else if constexpr (kQElems == 8) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2*>(row + (((qc >> 4) ^ sw) << 4) + (qc & 15)) = u32x2{wq[0], wq[1]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < kQElems / 16; ++c)
+        *reinterpret_cast<u32x4*>(row + ((((qc >> 4) + c) ^ sw) << 4)) =
+            u32x4{wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]};
+    }
+    as_row[qr] = s;  // every lane of the row stores the same value
   };
 
   // Fragment rows come in 16-row blocks, so every row a lane reads has row % 16 == r.
@@ -164,19 +288,47 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
       fb[tn] = frag_at(sl, tn * 16);
       if (tail) fb[tn] = mask_k_tail(fb[tn], k_tail, kc);
     }
+    if constexpr (kFused) {
+      // The staged activations are read and the slot refilled (its copied rows and stage; the
+      // activation rows of codes are not copied) before the quantization, which then runs while
+      // the next blocks' copies are in flight. The wave reads back its own LDS writes.
+      uint32_t raw[kXCopies * kXPiece / 4];
+      const uint8_t* stage = sl + (kRows + kQRows) * kBlock;
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      fa[tm] = frag_at(sl, BN + tm * 16);
-      if (tail) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
-      if constexpr (kE8) {
-        ea[tm] = reinterpret_cast<const uint8_t*>(&as_slots[w][slot][0])[tm * 16 + r];
-      } else {
-        sc[tm] = as_slots[w][slot][tm * 16 + r] * bs_kb;
+      for (int j = 0; j < kXCopies; ++j) {
+        if constexpr (kXPiece == 16) {
+          const u32x4 p = *reinterpret_cast<const u32x4*>(stage + j * 64 * kXPiece + lane * 16);
+          raw[4 * j] = p[0]; raw[4 * j + 1] = p[1]; raw[4 * j + 2] = p[2]; raw[4 * j + 3] = p[3];
+        } else {
+          raw[j] = *reinterpret_cast<const uint32_t*>(stage + j * 64 * kXPiece + lane * 4);
+        }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (i + SLOTS < nkb) issue(slot, block_of(i + SLOTS));
+      float* as_w = &as_slots[w][slot][0];
+      quantize(raw, kb, const_cast<uint8_t*>(sl) + kRows * kBlock, as_w);
+      // fragment row r reads code row r % kQRows
+      const int ra = r % kQRows, fsa = lds_swizzle(ra);
+      const uint8_t* ar = sl + (kRows + ra) * kBlock;
+      const v4i lo = *reinterpret_cast<const v4i*>(ar + (((2 * kc) ^ fsa) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(ar + (((2 * kc + 1) ^ fsa) << 4));
+      fa[0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      sc[0] = as_w[ra] * bs_kb;
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        fa[tm] = frag_at(sl, BN + tm * 16);
+        if (tail) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
+        if constexpr (kE8) {
+          ea[tm] = reinterpret_cast<const uint8_t*>(&as_slots[w][slot][0])[tm * 16 + r];
+        } else {
+          sc[tm] = as_slots[w][slot][tm * 16 + r] * bs_kb;
+        }
+      }
+      // The slot is refilled only after this wave's reads of it have returned.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (i + SLOTS < nkb) issue(slot, block_of(i + SLOTS));
     }
-    // The slot is refilled only after this wave's reads of it have returned.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (i + SLOTS < nkb) issue(slot, block_of(i + SLOTS));
     // Multiply, promoting sub-tile t - 2 after issuing the MFMA of sub-tile t (the result
     // is then at least one MFMA old); a scheduling barrier per step keeps this order.
     v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;
@@ -306,6 +458,37 @@ int choose_cfg(int64_t M, int64_t N, int64_t K) {
 
 double ksplit_time_us(int64_t M, int64_t N, int64_t K) {
   return cfg_time_us(kKsplitCfgs[choose_cfg(M, N, K)], M, N, K);
+}
+
+// Where the one-launch linear layer is faster than the quantizer launch followed by the GEMM
+// (interleaved graph timings on MI355X, N x K from 2048 x 4096 to 5120 x 25600): every
+// workgroup quantizes all M rows, which at M = 1 (64 lanes on one row) costs less than a launch
+// on every shape measured (1.2-2.4 us saved), at M <= 4 while N * K <= 2^25 (0.7-1.6 us), at
+// M <= 8 while N * K <= 2^24 (0.1-1.5 us); beyond that it loses up to 40 us at M = 16.
+bool ksplit_fused_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kFusedMaxM || choose_cfg(M, N, K) != 0) return false;
+  const double nk = (double)N * (double)K;
+  return M == 1 || (M <= 4 && nk <= 33554432.0) || nk <= 16777216.0;
+}
+
+namespace {
+template <int kIn>
+hipError_t launch_fused_rows(const GemmArgs& args, hipStream_t stream) {
+  const dim3 grid((unsigned)((args.N + 15) / 16), 1u);
+  if (args.M == 1) {
+    hipLaunchKernelGGL((gemm_ksplit_kernel<1, 1, 8, 2, false, kIn, 1>), grid, dim3(8 * 64), 0, stream, args);
+  } else if (args.M <= 4) {
+    hipLaunchKernelGGL((gemm_ksplit_kernel<1, 1, 8, 2, false, kIn, 4>), grid, dim3(8 * 64), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((gemm_ksplit_kernel<1, 1, 8, 2, false, kIn, 8>), grid, dim3(8 * 64), 0, stream, args);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_ksplit_fused(const GemmArgs& args, int x_dtype, hipStream_t stream) {
+  if (args.M < 1 || args.M > kFusedMaxM) return hipErrorInvalidValue;
+  return x_dtype == kInF16 ? launch_fused_rows<kInF16>(args, stream) : launch_fused_rows<kInBf16>(args, stream);
 }
 
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream) {

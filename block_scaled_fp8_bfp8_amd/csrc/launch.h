@@ -80,6 +80,13 @@ double ksplit_time_us(int64_t M, int64_t N, int64_t K);
 double tiled_time_us(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream);
+// The linear layer at small M: the K-split kernel's 16 x 16 tile quantizing the bf16/fp16
+// activations (args.a, args.lda in elements; args.as unused) itself, bit-identical to
+// launch_quant_act followed by launch_gemm_ksplit. Taken for the shapes ksplit_fused_shape
+// accepts (M <= kFusedMaxM, on the K-split schedule's 16 x 16 tile, where it is faster).
+constexpr int kFusedMaxM = 8;
+bool ksplit_fused_shape(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_ksplit_fused(const GemmArgs& args, int x_dtype, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream);
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream);
 

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 9
+#define BFP8_ABI_VERSION 10
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -215,12 +215,24 @@ size_t bfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *          256-byte aligned (BFP8_ERR_WORKSPACE if smaller); it holds the quantized
  *          activations, which the call overwrites.
  * Two kernels are enqueued on stream: the quantizer, then the GEMM with the bias in its
- * output conversion. Validation, ownership and errors as for bfp8_quant_act and bfp8_gemm.
+ * output conversion; except where bfp8_linear_fuses(M, N, K, ldx) is 1 (small M), where one
+ * GEMM kernel quantizes the activations itself, with the same codes and scales bit for bit,
+ * and the workspace is not touched. Validation, ownership and errors as for bfp8_quant_act
+ * and bfp8_gemm.
  */
 bfp8_status_t bfp8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                           const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
                           const uint16_t* bias, uint16_t* c, int64_t ldc, int64_t N,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* 1 if bfp8_linear (and bfp8_linear_noalloc) with these sizes enqueues one kernel that
+ * quantizes the activations inside the GEMM, else 0. That kernel runs on the K-split
+ * schedule's 16 x 16 tile (under the current bfp8_set_schedule override) and every workgroup
+ * quantizes all M rows itself, which is faster than a separate quantizer launch only at
+ * small sizes: M == 1, or M <= 4 with N * K <= 2^25, or M <= 8 with N * K <= 2^24; and the
+ * activation rows must be addressable with 32-bit offsets ((M - 1) * ldx * 2 +
+ * 2 * ceil(K/128) * 128 < 2^32). Host arithmetic only. */
+int bfp8_linear_fuses(int64_t M, int64_t N, int64_t K, int64_t ldx);
 
 /* Size of the device array that bfp8_linear_noalloc stages the quantized activations in. */
 #define BFP8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 9
+    assert lib.bfp8_abi_version() == 10
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -353,3 +353,30 @@ def test_probe_library_exports_its_header():
     assert pr.bfp8_probe_copy_lds(fake, 4, 64, 16, 2, fake, 1, None) == 1  # wide rows need inflight 8
     assert pr.bfp8_probe_copy_lds(fake, 4, 64, 8, 5, fake, 1, None) == 1
     assert pr.bfp8_probe_copy_lds(fake, 4, 64, 8, -1, fake, 1, None) == 1
+
+
+def test_linear_fusion_choice(lib):
+    """The linear layer quantizes inside the GEMM at small M, N and K on the K-split 16 x 16 tile,
+    and only while the activation rows fit 32-bit copy offsets; a forced tiled schedule never
+    fuses."""
+    assert lib.bfp8_linear_fuses(1, 4096, 4096, 4096) == 1
+    assert lib.bfp8_linear_fuses(1, 51200, 5120, 5120) == 1  # M = 1: every shape
+    assert lib.bfp8_linear_fuses(1, 5120, 25600, 25600) == 1
+    assert lib.bfp8_linear_fuses(4, 4096, 8192, 8192) == 1  # N * K = 2^25
+    assert lib.bfp8_linear_fuses(4, 5120, 8192, 8192) == 0
+    assert lib.bfp8_linear_fuses(8, 4096, 4096, 4096) == 1  # N * K = 2^24
+    assert lib.bfp8_linear_fuses(8, 5120, 4096, 4096) == 0
+    assert lib.bfp8_linear_fuses(9, 64, 1024, 1024) == 0
+    assert lib.bfp8_linear_fuses(16, 4096, 4096, 4096) == 0
+    assert lib.bfp8_linear_fuses(4, 4096, 4096, (1 << 30) + 64) == 0  # 3 rows of 2 GiB past row 0
+    assert lib.bfp8_linear_fuses(1, 4096, 4096, (1 << 30) + 64) == 1  # one row: no row offset
+    assert lib.bfp8_linear_fuses(0, 4096, 4096, 4096) == 0
+    assert lib.bfp8_linear_fuses(4, 4096, 4100, 4100) == 0  # K not a multiple of 16
+    assert lib.bfp8_linear_fuses(4, 4096, 4096, 4000) == 0  # ldx < K
+    try:
+        assert lib.bfp8_set_schedule(2) == _native.BFP8_OK  # tiled
+        assert lib.bfp8_linear_fuses(1, 4096, 4096, 4096) == 0
+        assert lib.bfp8_set_schedule(1) == _native.BFP8_OK  # small_m
+        assert lib.bfp8_linear_fuses(1, 4096, 4096, 4096) == 1
+    finally:
+        lib.bfp8_set_schedule(0)
