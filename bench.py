@@ -210,7 +210,7 @@ def main() -> int:
                     help="profile helper: run only this configuration (no sweep, no table)")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and HBM-read ceilings")
     ap.add_argument("--ceilings-only", action="store_true", help="profile helper: only the ceiling probes")
-    ap.add_argument("--schedule", choices=["auto", "small_m", "tiled"], default="auto",
+    ap.add_argument("--schedule", choices=["auto", "small_m", "tiled", "persistent"], default="auto",
                     help="profile helper: force one GEMM schedule")
     args = ap.parse_args()
 

@@ -656,7 +656,9 @@ def linear_fuses(m: int, n: int, k: int, ldx: int | None = None) -> bool:
 
 
 def set_schedule(name: str) -> None:
-    """Force a GEMM schedule ('small_m', 'tiled') or restore the automatic choice ('auto')."""
+    """Force a GEMM schedule ('small_m', 'tiled', 'persistent') or restore the automatic choice
+    ('auto'). 'persistent' is the tiled schedule with its 256 x 256 launches on the persistent
+    kernel; the automatic choice never takes it (it measured slower)."""
     if name not in SCHEDULES:
         raise ValueError(f"unknown schedule {name!r}; choose from {sorted(SCHEDULES)}")
     _check(_native.lib().bfp8_set_schedule(SCHEDULES[name]), "bfp8_set_schedule")

@@ -20,7 +20,7 @@ BFP8_IN_F32 = 0
 BFP8_IN_BF16 = 1
 BFP8_IN_F16 = 2
 
-SCHEDULES = {"auto": 0, "small_m": 1, "tiled": 2}
+SCHEDULES = {"auto": 0, "small_m": 1, "tiled": 2, "persistent": 3}
 
 # Every symbol include/bfp8.h declares: (name, restype, argtypes)
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t

@@ -220,7 +220,8 @@ bfp8_status_t launch_dense(const uint8_t* a, int64_t lda, const void* as, int64_
                             ldc,    (int)M, (int)N, (int)K,  nullptr, 1, bias, e8, out_f16};
   const int sched = choose_schedule(M, N, K);
   if (sched == BFP8_SCHED_SMALL_M) return launched(bfp8::launch_gemm_ksplit(args, (hipStream_t)stream), "gemm_ksplit");
-  return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream), "gemm_tiled");
+  return launched(bfp8::launch_gemm_tiled(args, workspace, (hipStream_t)stream, sched == BFP8_SCHED_PERSISTENT),
+                  "gemm_tiled");
 }
 
 LinearLayout linear_layout(int64_t M, int64_t N, int64_t K) {

@@ -169,6 +169,22 @@ __device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voff, u
       : "s"(sbase), "v"(voff), "s"(lds)
       : "memory");
 }
+// The same copies for kernels whose register pressure lets the compiler spill the (wave-uniform)
+// base or LDS address: a value reloaded from a spill lands in a vector register, which the
+// scalar moves above cannot read, so these pass both through readfirstlane (free for values
+// already in scalar registers).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void copy16_to_lds_u(const void* sbase, uint32_t voff, uint32_t lds) {
+  copy16_to_lds(uniform_ptr(sbase), voff, __builtin_amdgcn_readfirstlane(lds));
+}
+__device__ __forceinline__ void copy4_to_lds_u(const void* sbase, uint32_t voff, uint32_t lds) {
+  copy4_to_lds(uniform_ptr(sbase), voff, __builtin_amdgcn_readfirstlane(lds));
+}
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // s_waitcnt vmcnt(N): all but this wave's N most recent copies have landed.
 template <int N>

@@ -607,7 +607,8 @@ TiledPlan min_time_plan(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
-hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t stream) {
+hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t stream, int persistent) {
+  if (persistent && p.bn == 256 && p.bm == 256 && persistent_supported(args)) return launch_gemm_persistent(args, stream);
   if (args.K % kBlock) {
     if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, true>(args, stream);
     if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 2, 3, 1, false, true>(args, stream);
@@ -675,10 +676,10 @@ double tiled_time_us(int64_t M, int64_t N, int64_t K) {
   return std::max(choose_launch(M, N, K).us, stream_us);
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream) {
+hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream, int persistent) {
   (void)workspace;
   const TiledLaunch l = choose_launch(args.M, args.N, args.K);
-  if (l.n1 == 0) return launch_planned(args, l.lead, stream);
+  if (l.n1 == 0) return launch_planned(args, l.lead, stream, persistent);
   const int n1 = l.n1;
   GemmArgs a1 = args;
   a1.N = n1;
@@ -688,9 +689,9 @@ hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t 
   a2.bs = static_cast<const uint8_t*>(args.bs) + (int64_t)(n1 / kBlock) * args.ld_bs * (args.e8 ? 1 : 4);
   a2.c = args.c + n1;
   if (args.bias) a2.bias = args.bias + n1;
-  const hipError_t e = launch_planned(a1, l.lead, stream);
+  const hipError_t e = launch_planned(a1, l.lead, stream, persistent);
   if (e != hipSuccess) return e;
-  return launch_planned(a2, l.tail, stream);
+  return launch_planned(a2, l.tail, stream, persistent);
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.

@@ -87,7 +87,13 @@ hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream);
 constexpr int kFusedMaxM = 8;
 bool ksplit_fused_shape(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_ksplit_fused(const GemmArgs& args, int x_dtype, hipStream_t stream);
-hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream);
+// persistent != 0 (the forced persistent schedule): launches whose plan runs 256 x 256 tiles take
+// the persistent kernel where it supports the arguments.
+hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t stream, int persistent = 0);
+// Persistent 256 x 256 kernel (gemm_persistent.hip): float scales, K % 128 == 0, bf16 output in
+// 16-byte aligned rows.
+bool persistent_supported(const GemmArgs& args);
+hipError_t launch_gemm_persistent(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream);
 
 }  // namespace bfp8

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 10
+#define BFP8_ABI_VERSION 11
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -91,7 +91,14 @@ typedef enum bfp8_schedule {
   BFP8_SCHED_AUTO = 0,
   BFP8_SCHED_SMALL_M = 1, /* small/mid M: K blocks split across the waves of a workgroup */
   BFP8_SCHED_TILED = 2,   /* LDS-tiled MFMA kernel, one output tile per workgroup */
-  BFP8_SCHED_COUNT_ = 3
+  BFP8_SCHED_PERSISTENT = 3, /* the tiled schedule, except that launches planned with 256 x 256
+                                tiles run a persistent kernel: each workgroup takes two tiles and
+                                issues the second tile's first copies before storing the first
+                                (float scales, K % 128 == 0, bf16 output in 16-byte aligned rows;
+                                otherwise the tiled kernel). Only by override: timed interleaved
+                                with the tiled kernel on MI355X it was slower (e.g. 129 vs 120 us
+                                at M = 8192, N = K = 4096), so BFP8_SCHED_AUTO never takes it. */
+  BFP8_SCHED_COUNT_ = 4
 } bfp8_schedule_t;
 
 /* Returns BFP8_ABI_VERSION of the loaded library. */

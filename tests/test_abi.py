@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 10
+    assert lib.bfp8_abi_version() == 11
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -154,8 +154,15 @@ def test_schedule_override(lib):
         assert lib.bfp8_gemm_schedule_for(4096, 4096, 4096) == 2
         assert lib.bfp8_set_schedule(2) == 0
         assert lib.bfp8_gemm_schedule_for(1, 4096, 4096) == 2
+        assert lib.bfp8_set_schedule(4) == _native.BFP8_ERR_INVALID_ARGUMENT
+        assert lib.bfp8_set_schedule(3) == 0  # persistent: only by override
+        assert lib.bfp8_gemm_schedule_for(8192, 4096, 4096) == 3
+        assert lib.bfp8_gemm_workspace_bytes(8192, 4096, 4096) == 0
+        assert lib.bfp8_linear_fuses(1, 4096, 4096, 4096) == 0
     finally:
         lib.bfp8_set_schedule(0)
+    for m in (8192, 7680, 16384, 2048):  # the automatic choice never runs the persistent kernel
+        assert lib.bfp8_gemm_schedule_for(m, 4096, 4096) == 2
 
 
 def test_schedule_by_shape(lib):
