@@ -19,6 +19,9 @@ What is computed, and where it is defined on the pages:
 * blockwise GEMM (``gemm``): C[m,n] = sum_kb (A_q[m,kb] . B_q[n,kb]) * As[m,kb] * Bs[n//128,kb],
   the ``native_w8a8_block_matmul`` reference of the vLLM test, with the
   1x128 / 128x128 block contract of its "实现拆解" list item 2.
+* 1x64 / 128x64 layout (``quant.quant_act_ref(x, group=64)``, ``gemm.gemm_acc_ref(...,
+  k_block=64)``): the next block-scale layouts named on the vLLM torch-backend page (section
+  "风险与影响"), read as the same definitions over 64-wide K groups with 128-row weight blocks.
 * M-grouped contiguous GEMM (``gemm.grouped_gemm_contiguous_ref``): page
   "transformers/integrations/deepgemm.py", ``_build_deepgemm_contiguous_layout``
   (per-row expert id, -1 on padding rows) and ``deepgemm_fp8_fp4_experts_forward``.

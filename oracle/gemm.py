@@ -20,6 +20,12 @@ product As*Bs of two float32 values is exact in float64; only the final sum
 over blocks (at most a few hundred terms) rounds, at 2**-53 relative, far
 below the bf16 output rounding.
 
+1x64 / 128x64 layout (``k_block=64``): the vLLM torch-backend page ("实现拆解" lists the
+1x128 / 128x128 contract; "风险与影响" names 1x64 activation groups and 128x64 weight blocks as
+the next layouts). Read plainly, the same sum over K blocks of 64: As is [M, ceil(K/64)], Bs is
+[ceil(N/128), ceil(K/64)] (weight blocks stay 128 rows tall), and P_kb sums 64 products, which
+the exactness argument above covers a fortiori.
+
 Grouped contiguous (page "transformers/integrations/deepgemm.py",
 ``_build_deepgemm_contiguous_layout`` and ``deepgemm_fp8_fp4_experts_forward``):
 each row r carries a group id g = layout[r]; rows with g >= 0 are the dense
@@ -36,12 +42,14 @@ from . import bf16, e4m3
 BLOCK = 128
 
 
-def _check_shapes(a_q, a_s, b_q, b_s):
+def _check_shapes(a_q, a_s, b_q, b_s, k_block=BLOCK):
     m, k = a_q.shape
     n, k2 = b_q.shape
     if k != k2:
         raise ValueError("A and B disagree on K")
-    kb = -(-k // BLOCK)
+    if k_block not in (64, 128):
+        raise ValueError("k_block must be 128 or 64")
+    kb = -(-k // k_block)
     if a_s.shape != (m, kb):
         raise ValueError(f"As must be [{m}, {kb}], got {a_s.shape}")
     if b_s.shape != (-(-n // BLOCK), kb):
@@ -49,20 +57,21 @@ def _check_shapes(a_q, a_s, b_q, b_s):
     return m, n, k, kb
 
 
-def gemm_acc_ref(a_q, a_s, b_q, b_s, rows=None, cols=None) -> tuple[np.ndarray, np.ndarray]:
+def gemm_acc_ref(a_q, a_s, b_q, b_s, rows=None, cols=None, k_block=BLOCK) -> tuple[np.ndarray, np.ndarray]:
     """Unrounded float64 result and the matching sum of absolute block terms.
 
     Returns (acc, absum), each [len(rows), len(cols)]:
       acc   = sum_kb P_kb * As * Bs
       absum = sum_kb |P_kb * As * Bs|   (size of the terms, for error bounds)
     ``rows``/``cols`` select a subset of output rows/columns (default: all); rows
-    are independent of each other, so a subset is the same definition.
+    are independent of each other, so a subset is the same definition. ``k_block``
+    is the K width of a scale block: 128, or 64 for the 1x64 / 128x64 layout.
     """
     a_q = np.asarray(a_q)
     b_q = np.asarray(b_q)
     a_s = np.asarray(a_s, dtype=np.float32)
     b_s = np.asarray(b_s, dtype=np.float32)
-    m, n, k, n_kb = _check_shapes(a_q, a_s, b_q, b_s)
+    m, n, k, n_kb = _check_shapes(a_q, a_s, b_q, b_s, k_block)
     rows = np.arange(m) if rows is None else np.asarray(rows)
     cols = np.arange(n) if cols is None else np.asarray(cols)
     a_val = e4m3.decode(a_q[rows])  # float64
@@ -72,7 +81,7 @@ def gemm_acc_ref(a_q, a_s, b_q, b_s, rows=None, cols=None) -> tuple[np.ndarray, 
     acc = np.zeros((rows.size, cols.size), dtype=np.float64)
     absum = np.zeros_like(acc)
     for kb in range(n_kb):
-        ks = slice(kb * BLOCK, min((kb + 1) * BLOCK, k))
+        ks = slice(kb * k_block, min((kb + 1) * k_block, k))
         p = a_val[:, ks] @ b_val[:, ks].T  # exact (see module docstring)
         term = p * (a_sc[:, kb][:, None] * b_sc[:, kb][None, :])
         acc += term
@@ -80,9 +89,9 @@ def gemm_acc_ref(a_q, a_s, b_q, b_s, rows=None, cols=None) -> tuple[np.ndarray, 
     return acc, absum
 
 
-def gemm_ref(a_q, a_s, b_q, b_s, rows=None, cols=None) -> np.ndarray:
+def gemm_ref(a_q, a_s, b_q, b_s, rows=None, cols=None, k_block=BLOCK) -> np.ndarray:
     """bf16 bit patterns (uint16) of C = bf16(sum_kb P_kb * As * Bs)."""
-    acc, _ = gemm_acc_ref(a_q, a_s, b_q, b_s, rows, cols)
+    acc, _ = gemm_acc_ref(a_q, a_s, b_q, b_s, rows, cols, k_block)
     return bf16.to_bits(acc)
 
 

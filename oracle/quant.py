@@ -17,6 +17,11 @@ justification in the design notes):
     rounded float32 division (not a multiply by 1/s);
   * dequantized value x ~ q * s (s is the multiplier, like ``weight_scale_inv``).
 The input is widened to float32 first (exact for bf16 and fp16 inputs).
+
+Group width. The pages define 1x128 groups; the vLLM torch-backend page ("prhub.com.cn ...
+vllm/pull/49932", section "风险与影响") names 1x64 activation groups (with 128x64 weight
+blocks) as the next layouts to support. ``group=64`` is that layout, read plainly: the same
+scale and code definition over groups of 64 consecutive columns (ceil(K/64) scales per row).
 """
 
 from __future__ import annotations
@@ -30,24 +35,26 @@ FP8_MAX = np.float32(448.0)
 AMAX_FLOOR = np.float32(1e-10)
 
 
-def quant_act_ref(x) -> tuple[np.ndarray, np.ndarray]:
-    """Quantize x[M, K] per 1x128 group.
+def quant_act_ref(x, group: int = GROUP) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize x[M, K] per 1 x ``group`` group (128, or 64 for the 1x64 layout).
 
-    Returns (q, s): q uint8 e4m3fn codes [M, K]; s float32 scales [M, ceil(K/128)]
+    Returns (q, s): q uint8 e4m3fn codes [M, K]; s float32 scales [M, ceil(K/group)]
     in row-major (m, group) order. The kernel ABI stores the same values
     group-major; that is a layout choice, not a different result.
     """
     x = np.asarray(x)
     if x.ndim != 2:
         raise ValueError("x must be 2-D [M, K]")
+    if group not in (64, 128):
+        raise ValueError("group must be 128 or 64")
     x32 = x.astype(np.float32)  # bf16/fp16 -> fp32 is exact
     m, k = x32.shape
-    n_groups = -(-k // GROUP)
+    n_groups = -(-k // group)
     q = np.empty((m, k), dtype=np.uint8)
     s = np.empty((m, n_groups), dtype=np.float32)
     with np.errstate(divide="raise", invalid="raise", over="raise"):
         for g in range(n_groups):
-            cols = slice(g * GROUP, min((g + 1) * GROUP, k))
+            cols = slice(g * group, min((g + 1) * group, k))
             xg = x32[:, cols]
             amax = np.abs(xg).max(axis=1) if m else np.zeros(0, np.float32)
             sg = np.maximum(amax, AMAX_FLOOR) / FP8_MAX  # IEEE float32 division
@@ -58,10 +65,10 @@ def quant_act_ref(x) -> tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
-def dequant_ref(q, s) -> np.ndarray:
+def dequant_ref(q, s, group: int = GROUP) -> np.ndarray:
     """q * s per group, in float64 (for round-trip checks)."""
     q = np.asarray(q)
     s = np.asarray(s, dtype=np.float64)
     k = q.shape[1]
-    scale_full = np.repeat(s, GROUP, axis=1)[:, :k]
+    scale_full = np.repeat(s, group, axis=1)[:, :k]
     return e4m3.decode(q) * scale_full
