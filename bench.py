@@ -206,7 +206,7 @@ def main() -> int:
                     help="skip the transformer-linear and MoE grouped-GEMM configurations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (for counter calibration under rocprofv3)")
-    ap.add_argument("--only-config", choices=["transformer_linear", "moe_grouped", "moe_chain"], default=None,
+    ap.add_argument("--only-config", choices=["transformer_linear", "moe_grouped", "moe_chain", "gemm_1x64"], default=None,
                     help="profile helper: run only this configuration (no sweep, no table)")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and HBM-read ceilings")
     ap.add_argument("--ceilings-only", action="store_true", help="profile helper: only the ceiling probes")
@@ -400,7 +400,7 @@ def main() -> int:
     configs = {}
     want = ((lambda name: args.only_config in (None, name)) if not args.no_configs and not args.only_m and not args.ceilings_only
             else (lambda name: False))
-    if want("transformer_linear") or want("moe_grouped") or want("moe_chain"):
+    if want("transformer_linear") or want("moe_grouped") or want("moe_chain") or want("gemm_1x64"):
         del bq, bsc  # the sweep's weight copies
         torch.cuda.empty_cache()
     if want("transformer_linear"):
@@ -456,6 +456,32 @@ def main() -> int:
             f"{configs['moe_grouped']['tflops']:8.1f} TFLOP/s  {configs['moe_grouped']['bound']} "
             f"frac {configs['moe_grouped']['frac']:.3f}")
         del bq_g, bs_g
+        torch.cuda.empty_cache()
+
+    if want("gemm_1x64"):
+        # 1x64 activation groups / 128x64 weight blocks on the sweep's N = K = 4096 (the same
+        # weight codes with 128x64 scales), cold weights
+        g64 = {}
+        w64 = workloads.weight_1x64(N, K, seed=1)
+        n_copies = max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+        wq64 = [w64.q.to(dev) for _ in range(n_copies)]
+        ws64 = [w64.s.to(dev) for _ in range(n_copies)]
+        for m in (1, 16, 256, 2048, 8192):
+            q64, s64 = bfp8.quant_act_1x64(workloads.square_act(m).to(dev))
+            c64 = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+
+            def g64_calls(n, q64=q64, s64=s64, c64=c64):
+                for j in range(n):
+                    bfp8.gemm_1x64(q64, s64, wq64[j % n_copies], ws64[j % n_copies], out=c64)
+
+            us = graph_time_us(g64_calls, 33 if m <= 2048 else 8)
+            alg = m * K + 4 * m * (K // 64) + N * K + 4 * (N // 128) * (K // 64) + 2 * m * N
+            g64[str(m)] = roofline_entry(us, 2.0 * m * N * K, alg)
+            log(f"gemm_1x64 M={m:5d}: {us:8.2f} us  {g64[str(m)]['tflops']:8.1f} TFLOP/s  {g64[str(m)]['bound']} "
+                f"frac {g64[str(m)]['frac']:.3f}")
+        configs["gemm_1x64"] = {"what": "bfp8_gemm_1x64 (1x64 activation groups, 128x64 weight blocks), N = K = 4096, "
+                                        "graph replay of back-to-back calls, cold weights", "per_m": g64}
+        del wq64, ws64
         torch.cuda.empty_cache()
 
     if want("moe_chain"):

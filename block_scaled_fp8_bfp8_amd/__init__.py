@@ -24,6 +24,7 @@ from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
     "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes", "linear_fuses",
+    "quant_act_1x64", "gemm_1x64",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
     "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
     "moe_forward_workspace_bytes", "nn_to_nt_weights", "pad_k", "expand_act_scales", "expand_weight_scale", "set_schedule", "get_schedule", "schedule_for",
@@ -174,6 +175,50 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Ten
     workspace: optional caller-owned uint8 buffer on the same device (at least
     bfp8_gemm_workspace_bytes(M, N, K) bytes); by default one buffer per (device, stream) is kept."""
     return _gemm(a_q, a_s, b_q, b_s, out, workspace, torch.bfloat16)
+
+
+def quant_act_1x64(x: torch.Tensor):
+    """quant_act with 1x64 groups: returns (q [M, K] codes in rows padded to ceil(K/128) * 128
+    bytes, s float32 [M, ceil(K/64)] stored group-major)."""
+    dt = _in_dtype(x, "quant_act_1x64")
+    _require(x, "x", x.dtype, 2)
+    if x.stride(1) != 1:
+        raise ValueError("x must be K-contiguous")
+    m, k = x.shape
+    q = torch.empty((m, -(-k // 128) * 128), dtype=torch.uint8, device=x.device)[:, :k]
+    scales = torch.empty((-(-k // 64), m), dtype=torch.float32, device=x.device).t()
+    st = _native.lib().bfp8_quant_act_1x64(x.data_ptr(), dt, m, k, x.stride(0), q.data_ptr(), q.stride(0),
+                                           scales.data_ptr(), m if m > 0 else 1, _stream(x.device))
+    _check(st, "bfp8_quant_act_1x64")
+    return q, scales
+
+
+def gemm_1x64(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] (bf16) with 1x64 activation groups and 128x64 weight blocks: a_s [M, ceil(K/64)]
+    (group-major, as quant_act_1x64 returns), b_s [ceil(N/128), ceil(K/64)]; operands as for gemm."""
+    a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
+    _require(a_q, "a_q", torch.uint8, 2)
+    _require(b_q, "b_q", torch.uint8, 2)
+    _require(a_s, "a_s", torch.float32, 2)
+    _require(b_s, "b_s", torch.float32, 2)
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    if b_q.shape[1] != k:
+        raise ValueError(f"a_q and b_q disagree on K: {k} vs {b_q.shape[1]}")
+    if a_q.stride(1) != 1 or b_q.stride(1) != 1 or b_s.stride(1) != 1:
+        raise ValueError("a_q, b_q and b_s must be contiguous along K")
+    if tuple(a_s.shape) != (m, -(-k // 64)) or tuple(b_s.shape) != (-(-n // 128), -(-k // 64)):
+        raise ValueError(f"scale shapes {tuple(a_s.shape)}, {tuple(b_s.shape)} do not match M={m}, N={n}, K={k} "
+                         "with 1x64 / 128x64 blocks")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    _require(out, "out", torch.bfloat16, 2)
+    st = _native.lib().bfp8_gemm_1x64(a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m),
+                                      b_q.data_ptr(), b_q.stride(0), b_s.data_ptr(), b_s.stride(0), out.data_ptr(),
+                                      out.stride(0), m, n, k, _stream(a_q.device))
+    _check(st, "bfp8_gemm_1x64")
+    return out
 
 
 def gemm_f16(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,

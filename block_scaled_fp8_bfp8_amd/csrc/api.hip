@@ -337,6 +337,32 @@ bfp8_status_t bfp8_gemm(const uint8_t* a, int64_t lda, const float* as, int64_t 
   return launch_dense(a, lda, as, ld_as, b, ldb, bs, ld_bs, nullptr, c, ldc, M, N, K, workspace, stream);
 }
 
+bfp8_status_t bfp8_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                  int64_t ldq, float* as, int64_t ld_as, void* stream) {
+  bfp8_status_t st = check_quant_args(x, x_dtype, M, K, ldx, q, ldq, as, ld_as);
+  if (st != BFP8_OK || M == 0) return st;
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_quant_act_1x64(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, (hipStream_t)stream),
+                  "quant_act_1x64");
+}
+
+bfp8_status_t bfp8_gemm_1x64(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
+                             int64_t ldb, const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
+                             int64_t N, int64_t K, void* stream) {
+  bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, nullptr, 0, false);
+  if (st != BFP8_OK) return st;
+  if (ld_bs < (K + 63) / 64)
+    return fail(BFP8_ERR_INVALID_ARGUMENT, "ld_bs = %lld < ceil(K/64) = %lld", (long long)ld_bs,
+                (long long)((K + 63) / 64));
+  if (M == 0) return ok();
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  const bfp8::GemmArgs args{a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, (int)M, (int)N, (int)K, nullptr, 1, nullptr,
+                            false, false};
+  return launched(bfp8::launch_gemm_ksplit_1x64(args, (hipStream_t)stream), "gemm_ksplit_1x64");
+}
+
 bfp8_status_t bfp8_gemm_f16(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, const uint8_t* b,
                             int64_t ldb, const float* bs, int64_t ld_bs, uint16_t* c, int64_t ldc, int64_t M,
                             int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {

@@ -30,6 +30,12 @@
 //     rounded once to bf16;
 //   * UE8M0 scales (kE8): the scale codes are copied like the float scales, and the scaled
 //     MFMA applies 2^(ea - 127) * 2^(eb - 127) and accumulates into the wave's tile itself;
+//   * 1x64 activation groups with 128x64 weight blocks (kG64; the next block-scale layouts
+//     named on the vLLM torch-backend page, section "风险与影响"): each 128-wide K block holds
+//     two scale groups. The lanes of an MFMA operand fragment hold K bytes [32 kc, 32 kc + 32),
+//     so the activation fragment is split into its kc < 2 half (K 0-63) and its kc >= 2 half,
+//     each multiplied by a full MFMA with the other half zeroed and promoted with its own
+//     As * Bs (groups 2 kb and 2 kb + 1, in that order); twice the MFMAs and promotions;
 //   * fused activation quantization (kFuse = kInBf16 or kInF16, 16-row tiles, M <= kQRows):
 //     the linear layer's bf16/fp16 activations are copied instead of codes, the wave's 64
 //     lanes covering only the kQRows (1, 4 or 8) rows quantized: 64 / kQRows lanes per row
@@ -57,8 +63,10 @@ namespace bfp8 {
 
 namespace {
 
-template <int TN, int TM, int WAVES, int SLOTS, bool kE8, int kFuse = 0, int kQRows = 16>
+template <int TN, int TM, int WAVES, int SLOTS, bool kE8, int kFuse = 0, int kQRows = 16, bool kG64 = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) {
+  static_assert(!kG64 || (!kE8 && kFuse == 0), "1x64 groups: float scales, quantized activations");
+  constexpr int kScaleGroups = kG64 ? 2 : 1;  // activation scale groups per 128-wide K block
   constexpr bool kFused = kFuse != 0;  // args.a holds bf16/fp16 activations (lda in elements)
   static_assert(!kFused || (!kE8 && TM == 1 && (kFuse == kInBf16 || kFuse == kInF16)),
                 "fused quantization: float scales, 16 activation rows, bf16 or fp16 input");
@@ -81,14 +89,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
   constexpr int kScaleBytes = kE8 ? 1 : 4;
   static_assert(!kE8 || BM <= 256, "one copy holds the codes of 256 activation rows");
   using ScaleT = std::conditional_t<kE8, int, float>;
-  constexpr int kPerBlock = kPieces + kAsCopies + kXCopies;  // copies issued per K block
+  constexpr int kPerBlock = kPieces + kScaleGroups * kAsCopies + kXCopies;  // copies issued per K block
   constexpr int kTileFloats = BN * BM;
   static_assert(kBlock % BN == 0, "a wave's weight rows must share one scale strip");
   static_assert(kTileFloats * 4 <= SLOTS * kSlot, "the reduction reuses the wave's slots");
   static_assert(SLOTS >= 1 && SLOTS <= 3 && (SLOTS - 1) * kPerBlock < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t slots[WAVES][SLOTS][kSlot];
-  __shared__ __attribute__((aligned(16))) float as_slots[WAVES][SLOTS][(kAsCopies > 0 ? kAsCopies : 1) * 64];
+  __shared__ __attribute__((aligned(16))) float as_slots[WAVES][SLOTS][kScaleGroups * (kAsCopies > 0 ? kAsCopies : 1) * 64];
 
 
   const int lane = threadIdx.x & 63;
@@ -98,6 +106,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
   const int M = args.M, N = args.N;
   const int KB = (args.K + kBlock - 1) / kBlock;  // the last block may be partial (K % 128 != 0)
   const int k_tail = args.K - (KB - 1) * kBlock;   // bytes of the last block that exist
+  const int G64 = (args.K + 63) / 64;               // kG64: scale groups along K
   const int nkb = KB > w ? (KB - w + WAVES - 1) / WAVES : 0;  // this wave's blocks: w + i * WAVES
 
   // Copy plan: piece j is slot rows [8j, 8j + 8); lane l lands at row 8j + l/8, physical
@@ -139,9 +148,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     const uint32_t dst = lds_addr(&slots[w][slot][0]);
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) copy16_to_lds(j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
+    if constexpr (kG64) {
+      // groups 2 kb and 2 kb + 1 (clamped to the last group, which a partial last block may end
+      // before: that copy is then a duplicate whose scale is never used)
 #pragma unroll
-    for (int c = 0; c < kAsCopies; ++c)
-      copy4_to_lds(asmat + (int64_t)kb * args.ld_as * kScaleBytes, as_voff[c], lds_addr(&as_slots[w][slot][c * 64]));
+      for (int h = 0; h < 2; ++h) {
+        const int grp = min(2 * kb + h, G64 - 1);
+#pragma unroll
+        for (int c = 0; c < kAsCopies; ++c)
+          copy4_to_lds(asmat + (int64_t)grp * args.ld_as * 4, as_voff[c], lds_addr(&as_slots[w][slot][(h * kAsCopies + c) * 64]));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kAsCopies; ++c)
+        copy4_to_lds(asmat + (int64_t)kb * args.ld_as * kScaleBytes, as_voff[c], lds_addr(&as_slots[w][slot][c * 64]));
+    }
     if constexpr (kFused) {
       const uint8_t* xsrc = args.a + (int64_t)kb * kBlock * 2;
       const uint32_t xdst = dst + (uint32_t)((kRows + kQRows) * kBlock);
@@ -279,9 +300,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
     }
     const uint8_t* sl = &slots[w][slot][0];
     v8i fb[TN], fa[TM];
-    float sc[TM];
+    float sc[TM], sc_hi[TM];
     ScaleT ea[TM];
-    const ScaleT bs_kb = weight_scale(kb);
+    const ScaleT bs_kb = weight_scale(kG64 ? 2 * kb : kb);
+    // kG64: the second group's weight scale, 0 where a partial last block has no second group
+    const bool has_hi = kG64 && 2 * kb + 1 < G64;  // wave-uniform
+    const float bs_hi = has_hi ? (float)weight_scale(2 * kb + 1) : 0.f;
     const bool tail = kb == KB - 1 && k_tail < kBlock;  // wave-uniform
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
@@ -323,6 +347,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
           ea[tm] = reinterpret_cast<const uint8_t*>(&as_slots[w][slot][0])[tm * 16 + r];
         } else {
           sc[tm] = as_slots[w][slot][tm * 16 + r] * bs_kb;
+          if constexpr (kG64) sc_hi[tm] = as_slots[w][slot][kAsCopies * 64 + tm * 16 + r] * bs_hi;
         }
       }
       // The slot is refilled only after this wave's reads of it have returned.
@@ -338,7 +363,42 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_ksplit_kernel(GemmArgs args) 
       for (int e = 0; e < 4; ++e) acc[un][um][e] = fmaf(pu[e], sc[um], acc[un][um][e]);
       asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
     };
-    if constexpr (kE8) {
+    if constexpr (kG64) {
+      // Halves of each activation fragment: K 0-63 in the lanes with kc < 2, K 64-127 in the
+      // others. The two products of a sub-tile are promoted in group order, two steps behind.
+      const bool lo_lane = kc < 2;
+      v8i fa_lo[TM], fa_hi[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          fa_lo[tm][d] = lo_lane ? fa[tm][d] : 0;
+          fa_hi[tm][d] = lo_lane ? 0 : fa[tm][d];
+        }
+      v4f l1 = {0.f, 0.f, 0.f, 0.f}, l2 = l1, h1 = l1, h2 = l1;
+      auto promote2 = [&](int u, const v4f& pl, const v4f& ph) __attribute__((always_inline)) {
+        const int un = u / TM, um = u % TM;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[un][um][e] = fmaf(pl[e], sc[um], acc[un][um][e]);
+          acc[un][um][e] = fmaf(ph[e], sc_hi[um], acc[un][um][e]);
+        }
+        asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
+      };
+#pragma unroll
+      for (int t = 0; t < TN * TM; ++t) {
+        const v4f pl = mfma_block(fb[t / TM], fa_lo[t % TM]);
+        const v4f ph = mfma_block(fb[t / TM], fa_hi[t % TM]);
+        if (t >= 2) promote2(t - 2, l2, h2);
+        __builtin_amdgcn_sched_barrier(0);
+        l2 = l1;
+        h2 = h1;
+        l1 = pl;
+        h1 = ph;
+      }
+      if constexpr (TN * TM >= 2) promote2(TN * TM - 2, l2, h2);
+      promote2(TN * TM - 1, l1, h1);
+    } else if constexpr (kE8) {
 #pragma unroll
       for (int t = 0; t < TN * TM; ++t) {
         const int tn = t / TM, tm = t % TM;
@@ -489,6 +549,26 @@ hipError_t launch_fused_rows(const GemmArgs& args, hipStream_t stream) {
 hipError_t launch_gemm_ksplit_fused(const GemmArgs& args, int x_dtype, hipStream_t stream) {
   if (args.M < 1 || args.M > kFusedMaxM) return hipErrorInvalidValue;
   return x_dtype == kInF16 ? launch_fused_rows<kInF16>(args, stream) : launch_fused_rows<kInBf16>(args, stream);
+}
+
+namespace {
+template <int TN, int TM, int WAVES, int SLOTS>
+hipError_t launch_ksplit_g64(const GemmArgs& args, hipStream_t stream) {
+  const dim3 grid((unsigned)((args.N + 16 * TN - 1) / (16 * TN)), (unsigned)((args.M + 16 * TM - 1) / (16 * TM)));
+  hipLaunchKernelGGL((gemm_ksplit_kernel<TN, TM, WAVES, SLOTS, false, 0, 16, true>), grid, dim3(WAVES * 64), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_ksplit_1x64(const GemmArgs& args, hipStream_t stream) {
+  switch (choose_cfg(args.M, args.N, args.K)) {
+    case 0: return launch_ksplit_g64<1, 1, 8, 2>(args, stream);
+    case 1: return launch_ksplit_g64<1, 2, 8, 2>(args, stream);
+    case 2: return launch_ksplit_g64<2, 2, 8, 2>(args, stream);
+    case 3: return launch_ksplit_g64<4, 2, 8, 1>(args, stream);
+    default: return launch_ksplit_g64<4, 4, 8, 1>(args, stream);
+  }
 }
 
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream) {

@@ -50,6 +50,10 @@ hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, in
                             int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream,
                             const int32_t* src_rows = nullptr, int src_div = 1);
 
+// 1x64 groups: scales [ceil(K/64)][ld_as], float32.
+hipError_t launch_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                 int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
+
 // MoE chain (moe.hip). Dispatch: block_counts holds moe_dispatch_blocks(S) * E ints of scratch;
 // rows = length of layout and pair_of_row.
 int64_t moe_dispatch_blocks(int64_t S);
@@ -80,6 +84,9 @@ double ksplit_time_us(int64_t M, int64_t N, int64_t K);
 double tiled_time_us(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream);
+// 1x64 activation groups / 128x64 weight blocks (float scales): args.as is [ceil(K/64)][ld_as],
+// args.bs [ceil(N/128)][ld_bs >= ceil(K/64)]; the K-split kernel at every M.
+hipError_t launch_gemm_ksplit_1x64(const GemmArgs& args, hipStream_t stream);
 // The linear layer at small M: the K-split kernel's 16 x 16 tile quantizing the bf16/fp16
 // activations (args.a, args.lda in elements; args.as unused) itself, bit-identical to
 // launch_quant_act followed by launch_gemm_ksplit. Taken for the shapes ksplit_fused_shape

@@ -13,6 +13,9 @@
 // that power of two (exactly) and the scale is written as its UE8M0 code, the biased
 // exponent byte.
 //
+// 1x64 groups (kGroup = 64; the next block-scale layout named on the vLLM torch-backend page,
+// section "风险与影响"): the same arithmetic over groups of 64 columns, 8 lanes of 8 elements each.
+//
 // HBM-bound: per element it reads 4 (fp32) or 2 (bf16, fp16) bytes and writes 1, plus
 // 4 bytes of scale per 128 elements. Mapping: L lanes per group, 128 / L consecutive
 // elements per lane, 16-byte loads issued together and one store of the lane's codes.
@@ -39,16 +42,17 @@ constexpr int64_t kWideGroups = 32768;
 // Gather variant (kGather): output row m quantizes input row src_rows[m] / src_div, and rows
 // whose entry is negative are left unwritten (the MoE dispatch's padded buffer: entry = pair
 // index, src_div = top_k, so the input row is the pair's token).
-template <int kIn, bool kE8, bool kGather, int kLanesPerGroup>
+template <int kIn, bool kE8, bool kGather, int kLanesPerGroup, int kGroup = kBlock>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
                                                                   void* __restrict__ as, int64_t ld_as,
                                                                   int groups_per_row, int64_t total_groups,
                                                                   const int32_t* __restrict__ src_rows, int src_div,
                                                                   int64_t K) {
-  constexpr int kPerLane = kBlock / kLanesPerGroup;  // consecutive elements per lane
+  constexpr int kPerLane = kGroup / kLanesPerGroup;  // consecutive elements per lane
   constexpr int kGroupsPerBlock = kQuantThreads / kLanesPerGroup;
   static_assert(kLanesPerGroup == 8 || kLanesPerGroup == 16, "8 or 16 lanes per group");
+  static_assert(kPerLane == 8 || kPerLane == 16, "8 or 16 elements per lane");
   const int sub = threadIdx.x & (kLanesPerGroup - 1);  // which slice of the group
   const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x / kLanesPerGroup;
   const bool valid = gid < total_groups;
@@ -57,7 +61,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   const int64_t g_lin = valid ? gid : total_groups - 1;
   const int64_t m = g_lin / groups_per_row;
   const int g = (int)(g_lin - m * groups_per_row);
-  const int64_t col = (int64_t)g * kBlock + sub * kPerLane;
+  const int64_t col = (int64_t)g * kGroup + sub * kPerLane;
   // A partial last group (K % 128 != 0; K is a multiple of 16, so a lane's 8 or 16 elements
   // lie wholly before or wholly past K) has lanes past K: they load nothing, count as zeros
   // in the amax and store nothing.
@@ -174,6 +178,25 @@ void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void*
 }
 
 }  // namespace
+
+hipError_t launch_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                 int64_t ldq, float* as, int64_t ld_as, hipStream_t stream) {
+  const int groups_per_row = (int)((K + 63) / 64);
+  const int64_t total = M * groups_per_row;
+  constexpr int kGroupsPerBlock = kQuantThreads / 8;
+  const dim3 grid((unsigned)((total + kGroupsPerBlock - 1) / kGroupsPerBlock));
+  if (x_dtype == kInBf16) {
+    hipLaunchKernelGGL((quant_act_kernel<kInBf16, false, false, 8, 64>), grid, dim3(kQuantThreads), 0, stream, x, ldx,
+                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K);
+  } else if (x_dtype == kInF16) {
+    hipLaunchKernelGGL((quant_act_kernel<kInF16, false, false, 8, 64>), grid, dim3(kQuantThreads), 0, stream, x, ldx,
+                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K);
+  } else {
+    hipLaunchKernelGGL((quant_act_kernel<kInF32, false, false, 8, 64>), grid, dim3(kQuantThreads), 0, stream, x, ldx,
+                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream, const int32_t* src_rows,

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 11
+#define BFP8_ABI_VERSION 12
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -274,6 +274,28 @@ bfp8_status_t bfp8_gemm_f16(const uint8_t* a, int64_t lda, const float* as, int6
                             const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
                             uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * 1x64 activation groups with 128x64 weight blocks (the next block-scale layouts named on page
+ * "prhub.com.cn ... vllm/pull/49932", section "风险与影响"; the same definitions over K blocks
+ * of 64, weight blocks staying 128 rows tall):
+ *
+ * bfp8_quant_act_1x64: as bfp8_quant_act with groups of 64 columns: the scale of row m, group
+ * g = k / 64 is written to as[g * ld_as + m] (float32, ceil(K/64) groups; the last may be
+ * shorter). Same arguments, validation and errors.
+ *
+ * bfp8_gemm_1x64: C[m, n] = bf16(sum_g P_g * As[g][m] * Bs[n / 128][g]), P_g the e4m3 dot
+ * product over the 64 columns of group g. as is [ceil(K/64)][ld_as] (ld_as >= M), bs is
+ * [ceil(N/128)][ld_bs] with ld_bs >= ceil(K/64); a, b, c and every other rule as bfp8_gemm
+ * (operand rows of whole 128-byte blocks). Runs the K-split kernel at every M, with two matrix-
+ * core products and two promotions per 128-wide K block (no workspace). The float32
+ * accumulation error is bounded as for bfp8_gemm with K/64 promotions instead of K/128.
+ */
+bfp8_status_t bfp8_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* as, int64_t ld_as, void* stream);
+bfp8_status_t bfp8_gemm_1x64(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                             const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                             uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * UE8M0 (power-of-two) scale factors (page "transformers/integrations/deepgemm.py":

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 11
+    assert lib.bfp8_abi_version() == 12
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:
@@ -387,3 +387,21 @@ def test_linear_fusion_choice(lib):
         assert lib.bfp8_linear_fuses(1, 4096, 4096, 4096) == 1
     finally:
         lib.bfp8_set_schedule(0)
+
+
+def test_gemm_1x64_rejections(lib):
+    """The 1x64 GEMM validates as bfp8_gemm, plus ld_bs >= ceil(K/64) (weight scales of 64-wide
+    K blocks); M = 0 is a no-op."""
+    args = dict(a=A, lda=256, as_=AS, ld_as=8, b=B, ldb=256, bs=BS, ld_bs=4, c=C, ldc=64, M=8, N=64, K=208)
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.bfp8_gemm_1x64(a["a"], a["lda"], a["as_"], a["ld_as"], a["b"], a["ldb"], a["bs"], a["ld_bs"],
+                                  a["c"], a["ldc"], a["M"], a["N"], a["K"], None)
+    assert call(ld_bs=3) == _native.BFP8_ERR_INVALID_ARGUMENT  # ceil(208/64) = 4
+    assert call(ld_as=7) == _native.BFP8_ERR_INVALID_ARGUMENT
+    assert call(K=100) == _native.BFP8_ERR_UNSUPPORTED  # K % 16
+    assert call(lda=128) == _native.BFP8_ERR_INVALID_ARGUMENT  # rows of whole 128-byte blocks
+    assert call(M=0) == _native.BFP8_OK
+    assert lib.bfp8_quant_act_1x64(A, 1, 4, 208, 208, B, 256, AS, 3, None) == _native.BFP8_ERR_INVALID_ARGUMENT
+    assert lib.bfp8_quant_act_1x64(A, 1, 0, 208, 208, B, 256, AS, 3, None) == _native.BFP8_OK

@@ -69,16 +69,17 @@ class Mass:
         return self.absum.shape
 
 
-def abs_product_mass(a_q, a_s, b_q, b_s, rows, cols):
-    """mag[r, c] = sum_kb |As[r,kb] Bs[c//128,kb]| * sum_{k in kb} |a[r,k]| |b[c,k]| (float64)."""
+def abs_product_mass(a_q, a_s, b_q, b_s, rows, cols, k_block=128):
+    """mag[r, c] = sum_kb |As[r,kb] Bs[c//128,kb]| * sum_{k in kb} |a[r,k]| |b[c,k]| (float64),
+    kb running over K blocks of k_block (128, or 64 for the 1x64 layout)."""
     a_val = np.abs(e4m3.decode(np.asarray(a_q)[rows]))
     b_val = np.abs(e4m3.decode(np.asarray(b_q)[cols]))
     a_sc = np.abs(np.asarray(a_s, np.float64)[rows])
     b_sc = np.abs(np.asarray(b_s, np.float64)[np.asarray(cols) // 128])
     k = a_val.shape[1]
     mag = np.zeros((len(rows), len(cols)))
-    for kb in range(-(-k // 128)):  # the last block may be partial
-        ks = slice(kb * 128, min(k, kb * 128 + 128))
+    for kb in range(-(-k // k_block)):  # the last block may be partial
+        ks = slice(kb * k_block, min(k, kb * k_block + k_block))
         mag += (a_val[:, ks] @ b_val[:, ks].T) * (a_sc[:, kb][:, None] * b_sc[:, kb][None, :])
     return mag
 
@@ -102,19 +103,19 @@ def block_max_mass(a_q, a_s, b_q, b_s, rows, cols):
     return out
 
 
-def masses(a_q, a_s, b_q, b_s, rows, cols) -> Mass:
+def masses(a_q, a_s, b_q, b_s, rows, cols, k_block=128) -> Mass:
     """Mass of the outputs [rows x cols]: absum from the oracle, mag from abs_product_mass."""
-    _, absum = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, np.asarray(rows), np.asarray(cols))
-    return Mass(absum, abs_product_mass(a_q, a_s, b_q, b_s, rows, cols))
+    _, absum = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, np.asarray(rows), np.asarray(cols), k_block)
+    return Mass(absum, abs_product_mass(a_q, a_s, b_q, b_s, rows, cols, k_block))
 
 
-def reference(a_q, a_s, b_q, b_s, rows=None, cols=None):
+def reference(a_q, a_s, b_q, b_s, rows=None, cols=None, k_block=128):
     """(rows, cols, ref_bits, Mass) from the oracle."""
     m, n = np.asarray(a_q).shape[0], np.asarray(b_q).shape[0]
     rows = np.arange(m) if rows is None else np.asarray(rows)
     cols = np.arange(n) if cols is None else np.asarray(cols)
-    acc, absum = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, rows, cols)
-    mass = Mass(absum, abs_product_mass(a_q, a_s, b_q, b_s, rows, cols))
+    acc, absum = gemm.gemm_acc_ref(a_q, a_s, b_q, b_s, rows, cols, k_block)
+    mass = Mass(absum, abs_product_mass(a_q, a_s, b_q, b_s, rows, cols, k_block))
     return rows, cols, bf16.to_bits(acc), mass
 
 
@@ -130,9 +131,11 @@ def reference(a_q, a_s, b_q, b_s, rows=None, cols=None):
 FP32_FLOOR_ETA = 2.0**-24
 
 
-def fp32_floor(mass: Mass, k) -> np.ndarray:
-    """(K/128 + 130) 2**-24 mag: the worst case of float32 accumulation in any order."""
-    return (k / 128 + 130) * FP32_FLOOR_ETA * mass.mag
+def fp32_floor(mass: Mass, k, k_block=128) -> np.ndarray:
+    """(K/k_block + 130) 2**-24 mag: the worst case of float32 accumulation in any order (one
+    rounding per product-sum step inside a 128-wide matrix-core product, one for the scale
+    product, one per promotion: K/128 of them, or K/64 with 1x64 groups)."""
+    return (k / k_block + 130) * FP32_FLOOR_ETA * mass.mag
 
 
 def e8_floor(mass: Mass, k) -> np.ndarray:
@@ -186,7 +189,7 @@ def _rel_mean(d, ref):
     return d.mean() / max(np.abs(ref).mean(), 1e-300) if d.size else 0.0
 
 
-def compare(got_bits, ref_bits, mass: Mass, k, what="", hw_block=None):
+def compare(got_bits, ref_bits, mass: Mass, k, what="", hw_block=None, k_block=128):
     """Assert the bounds above; returns a dict of statistics. `hw_block` is mmax for tests
     whose codes span the whole e4m3 range (adds HW_BLOCK_ETA * mmax)."""
     got = bf16.from_bits(got_bits)
@@ -196,7 +199,7 @@ def compare(got_bits, ref_bits, mass: Mass, k, what="", hw_block=None):
     d = np.abs(got - ref)
     stated = 2 * bf16.ulp(ref) + 1e-3 * np.abs(ref)
     extra = HW_BLOCK_ETA * hw_block if hw_block is not None else None
-    floor = fp32_floor(mass, k) + (extra if extra is not None else 0.0)
+    floor = fp32_floor(mass, k, k_block) + (extra if extra is not None else 0.0)
     exact = np.mean(got_bits == ref_bits) if d.size else 1.0
     return _finish(what, got, ref, d, stated, floor, mass, _rel_mean(d, ref), exact, extra)
 

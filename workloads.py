@@ -85,6 +85,15 @@ def weight_ue8m0(n: int, k: int, seed: int) -> Weight:
     return Weight(q.contiguous(), e.contiguous())
 
 
+def weight_1x64(n: int, k: int, seed: int) -> Weight:
+    """The weight of weight(n, k, seed) (same codes) with 128x64 block scales U(0, 1e-2)
+    [ceil(n/128), ceil(k/64)], for the 1x64 / 128x64 layout."""
+    w = weight(n, k, seed)
+    g = torch.Generator().manual_seed(seed + 1_000_003)
+    s = torch.rand(_cdiv(n, BLOCK), _cdiv(k, 64), generator=g, dtype=torch.float32) * 1e-2
+    return Weight(w.q, s.contiguous())
+
+
 def act_uniform(m: int, k: int, seed: int) -> torch.Tensor:
     """fp32 activations ~ U(-448, 448)."""
     g = torch.Generator().manual_seed(seed)
