@@ -575,6 +575,30 @@ def swiglu_quant(proj: torch.Tensor, layout: torch.Tensor | None = None):
     return q, s
 
 
+def swiglu(proj: torch.Tensor, layout: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """h = bf16(bf16(silu(gate)) * up) of proj [M, 2I] (bf16, gate first) as bf16 [M, I], the values
+    swiglu_quant quantizes; rows with layout == -1 are left unwritten."""
+    _require(proj, "proj", torch.bfloat16, 2)
+    if proj.stride(1) != 1:
+        raise ValueError("proj must be contiguous along its columns")
+    m, two_i = proj.shape
+    i = two_i // 2
+    if layout is not None:
+        _require(layout, "layout", torch.int32, 1)
+        if layout.numel() != m or not layout.is_contiguous():
+            raise ValueError("layout must be a contiguous int32 vector of M entries")
+    if out is None:
+        out = torch.empty((m, i), dtype=torch.bfloat16, device=proj.device)
+    _require(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (m, i) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{m}, {i}] and contiguous along its columns")
+    st = _native.lib().bfp8_swiglu(proj.data_ptr(), m, i, proj.stride(0),
+                                   layout.data_ptr() if layout is not None else None, out.data_ptr(), out.stride(0),
+                                   _stream(proj.device))
+    _check(st, "bfp8_swiglu")
+    return out
+
+
 def moe_combine(out: torch.Tensor, row_of_pair: torch.Tensor, topk_weights: torch.Tensor) -> torch.Tensor:
     """y [T, H] = per token, sum_j bf16(out[row_of_pair[t, j]] * bf16(w[t, j])) (float32 sum, in order j)."""
     _require(out, "out", torch.bfloat16, 2)

@@ -48,6 +48,7 @@ SIGNATURES = [
     ("bfp8_quant_act_gather", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
     ("bfp8_swiglu_quant", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]),
+    ("bfp8_swiglu", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     ("bfp8_moe_combine", ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _i64, _vp]),
     ("bfp8_moe_forward_workspace_bytes", _sz, [_i64, _i32, _i32, _i64, _i64]),
     ("bfp8_moe_forward", ctypes.c_int,

@@ -626,6 +626,24 @@ bfp8_status_t bfp8_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int6
                   "swiglu_quant");
 }
 
+bfp8_status_t bfp8_swiglu(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout, uint16_t* h,
+                          int64_t ldh, void* stream) {
+  if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+  if (I < bfp8::kBlock || I % bfp8::kBlock != 0 || I > kMaxDim)
+    return fail(BFP8_ERR_UNSUPPORTED, "I = %lld must be a positive multiple of 128 (at most 2^30)", (long long)I);
+  if (M > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M must be at most 2^30");
+  if (M == 0) return BFP8_OK;
+  if (!proj || !h) return fail(BFP8_ERR_INVALID_ARGUMENT, "proj and h must not be NULL");
+  if (ldp < 2 * I) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldp = %lld < 2 I = %lld", (long long)ldp, (long long)(2 * I));
+  if (ldh < I) return fail(BFP8_ERR_INVALID_ARGUMENT, "ldh = %lld < I = %lld", (long long)ldh, (long long)I);
+  if ((ldp * 2) % 16 || (ldh * 2) % 16) return fail(BFP8_ERR_MISALIGNED, "row strides must be multiples of 16 bytes");
+  if (!aligned(proj, 16) || !aligned(h, 16) || !aligned(layout, 4))
+    return fail(BFP8_ERR_MISALIGNED, "proj and h must be 16-byte aligned, layout 4-byte aligned");
+  bfp8_status_t st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_swiglu(proj, M, I, ldp, layout, h, ldh, (hipStream_t)stream), "swiglu");
+}
+
 bfp8_status_t bfp8_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair,
                                const float* topk_weights, int64_t T, int32_t top_k, int64_t H, uint16_t* y,
                                int64_t ldy, void* stream) {

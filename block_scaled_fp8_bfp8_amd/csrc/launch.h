@@ -62,6 +62,8 @@ hipError_t launch_moe_dispatch(const int32_t* ids, int64_t S, int E, int align, 
                                int32_t* block_counts, hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout,
                                uint8_t* q, int64_t ldq, float* as, int64_t ld_as, hipStream_t stream);
+hipError_t launch_swiglu(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout, uint16_t* h,
+                         int64_t ldh, hipStream_t stream);
 // NN -> NT conversions (layout.hip): dst[e][n][k] = src[e][k][n] for bytes; dst[e][c][r] =
 // src[e][r][c] for float32 (contiguous).
 hipError_t launch_transpose_u8(const uint8_t* src, int64_t E, int64_t K, int64_t N, int64_t ld_src, uint8_t* dst,

@@ -148,39 +148,93 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
 
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-// bf16(silu(x)) for a bf16 input x, equal to rounding the exact silu once. Fast path in float32:
-// s = x / (1 + exp(-x)) is within a few float32 ulps of silu(x) (exp within 2 ulps, one rounding
-// for the sum and one for the IEEE divide), so its bf16 rounding is the exact one unless s lies
-// within 16 float32 ulps of a bf16 rounding midpoint (low 16 bits near 0x8000), or is tiny, where
-// float32 loses relative accuracy; those few elements are evaluated again in float64.
-__device__ __forceinline__ uint32_t silu_bf16(float x) {
-  const float s = x / (1.0f + expf(-x));
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t low = u & 0xffffu;
-  const bool clear = (low < 0x8000u - 16u || low > 0x8000u + 16u) && fabsf(s) >= 0x1p-100f && fabsf(s) < 0x1p100f;
-  if (clear) return f32_to_bf16_rne(s);
+// A finite normal float rounded to bf16 (nearest, ties to even) by the hardware conversion;
+// inf stays inf and a NaN stays a NaN.
+__device__ __forceinline__ float round_bf16(float f) { return (float)(__bf16)f; }
+
+// Float32 ulps of slack around a bf16 rounding midpoint inside which the float32 silu below does
+// not decide the rounding: twice its error bound.
+constexpr uint32_t kSiluSlackUlps = 16;
+
+// bf16 bits of silu(x) = x / (1 + exp(-x)) from float32 arithmetic, with `decided` false where
+// float32 cannot vouch for the rounding (the caller then takes the float64 path).
+//
+// The exponential: the argument a log2(e) (a = -x, or a = x for x < -20) is split into a float t
+// and the remainder tl that t misses (an fma and a product), t into an integer n and a fraction
+// f = t - n, and exp(a) = ldexp(2^f (1 + tl ln 2), n): the hardware exp2 (within 1 ulp) on
+// |f| <= 1/2, one rounding for the correction, one for the product, an exact ldexp.
+//  * x >= -20: silu = x * rcp(1 + exp(-x)) (the sum, the hardware reciprocal within 1 ulp and the
+//    product add one rounding each; errors of exp(-x) enter the sum damped by
+//    exp(-x) / (1 + exp(-x)) <= 1): at most 8 * 2^-24 relative error, 8 float32 ulps.
+//  * x < -20: silu = x e^x (1 - e^x + ...), and e^x < 2^-28, so x * exp(x) with the exponent
+//    raised by 64 (no underflow down to x = -131) is silu(x) 2^64 within 6 * 2^-24 relative.
+//    Where silu(x) >= 2^-126 the scaling back is exact; below, bf16 rounds on its subnormal grid
+//    2^-133, and k = |silu(x)| 2^133 < 128 is known to within 6 * 2^-24 * 128 < 2^-14.
+// The bf16 rounding is decided unless the result lies within the slack of a rounding midpoint
+// (k within 2^-13 of one on the subnormal grid), or is not a finite normal float32 value on
+// the main branch (zero gates excepted: silu(+-0) = +-0 exactly). All branches are selects.
+__device__ __forceinline__ uint32_t silu_bf16_f32(float x, bool& decided) {
+#pragma clang fp contract(off)  // every step rounds as written (explicit fmaf calls excepted)
+  constexpr float kLog2e = 0x1.715476p+0f;    // fl(log2 e)
+  constexpr float kLog2eLo = 0x1.4ae0c0p-26f; // fl(log2 e - kLog2e)
+  constexpr float kLn2 = 0x1.62e430p-1f;
+  const bool tail = x < -20.0f;
+  const float a = tail ? x : -x;
+  const float t = a * kLog2e;  // rounded (t - n fused with it would count tl twice); at most 29
+
+  const float tl = fmaf(a, kLog2e, -t) + a * kLog2eLo;
+  const float n = fminf(fmaxf(rintf(t), -200.0f), 200.0f);
+  const float p = __builtin_amdgcn_exp2f(t - n) * fmaf(tl, kLn2, 1.0f);
+  const float ex = __builtin_amdgcn_ldexpf(p, (int)n + (tail ? 64 : 0));
+  const float s1 = x * (tail ? ex : __builtin_amdgcn_rcpf(1.0f + ex));
+  const float s = tail ? s1 * 0x1p-64f : s1;
+  const float as = fabsf(s);
+  const uint32_t low = __float_as_uint(s) & 0xffffu;
+  const bool normal = (low + kSiluSlackUlps - 0x8000u > 2 * kSiluSlackUlps) & (as >= 0x1p-126f) &
+                      (as < __builtin_huge_valf());
+  const bool sub = tail & !(fabsf(s1) >= 0x1p-62f);
+  const float k = fabsf(s1) * 0x1p69f;  // exact scaling
+  const float kr = k <= 128.0f ? rintf(k) : 128.0f;
+  decided = sub ? (fabsf(k - truncf(k) - 0.5f) > 0x1p-13f) : (normal | (x == 0.0f));
+  return sub ? 0x8000u | (uint32_t)kr : (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s);
+}
+
+// bf16(silu(x)), silu evaluated in float64 (exp within an ulp of float64, one divide) and
+// rounded to bf16 through round-to-odd, for the elements float32 does not decide.
+__device__ __forceinline__ uint32_t silu_bf16_f64(float x) {
   const double xd = (double)x;
   return f64_to_bf16_rne(xd / (1.0 + exp(-xd)));
 }
 
-// bf16(a * b) for bf16 values a, b: the product has at most 16 significant bits, so float32 holds
-// it exactly unless it falls below the normal range; those are formed in float64.
+// bf16(a * b) for bf16 values a, b when the float32 product is not exact: below the normal range
+// (the product of two 8-bit significands always fits 24 bits otherwise), formed in float64.
+__device__ __forceinline__ uint32_t mul_bf16_f64(float a, float b) { return f64_to_bf16_rne((double)a * (double)b); }
+
+// The float32 product a * b of bf16 values is exact unless it left the normal range for a
+// nonzero result (underflow to a subnormal or to zero).
+__device__ __forceinline__ bool product_exact(float pr, float a, float b) {
+  return (fabsf(pr) >= 0x1p-126f) | ((pr == 0.0f) & ((a == 0.0f) | (b == 0.0f))) | (pr != pr);
+}
+
+// bf16(a * b) for bf16 values a, b.
 __device__ __forceinline__ uint32_t mul_bf16(float a, float b) {
   const float pr = a * b;
-  if (fabsf(pr) >= 0x1p-126f || pr == 0.0f && (a == 0.0f || b == 0.0f)) return f32_to_bf16_rne(pr);
-  return f64_to_bf16_rne((double)a * (double)b);
+  return product_exact(pr, a, b) ? f32_to_bf16_rne(pr) : mul_bf16_f64(a, b);
 }
 
 constexpr int kSwigluThreads = 256;
 constexpr int kSwigluGroupsPerBlock = kSwigluThreads / 16;
 
-// h = bf16(bf16(silu(gate)) * up) for one row's 1x128 group, then the activation quantizer's
-// steps on h: 16 lanes per group, 8 consecutive elements per lane.
-__global__ __launch_bounds__(kSwigluThreads) void swiglu_quant_kernel(const uint16_t* __restrict__ proj, int64_t ldp,
-                                                                      int I, const int32_t* __restrict__ layout,
-                                                                      uint8_t* __restrict__ q, int64_t ldq,
-                                                                      float* __restrict__ as, int64_t ld_as,
-                                                                      int groups_per_row, int64_t total_groups) {
+// h = bf16(bf16(silu(gate)) * up) for one row's 1x128 group, 16 lanes per group and 8
+// consecutive elements per lane; then either (kQuant) the activation quantizer's steps on h
+// into codes and the group scale, or h itself as bf16.
+template <bool kQuant>
+__global__ __launch_bounds__(kSwigluThreads) void swiglu_kernel(const uint16_t* __restrict__ proj, int64_t ldp, int I,
+                                                                const int32_t* __restrict__ layout,
+                                                                uint8_t* __restrict__ q, int64_t ldq,
+                                                                float* __restrict__ as, int64_t ld_as,
+                                                                uint16_t* __restrict__ h_out, int64_t ldh,
+                                                                int groups_per_row, int64_t total_groups) {
   const int sub = threadIdx.x & 15;
   const int64_t gid = (int64_t)blockIdx.x * kSwigluGroupsPerBlock + (threadIdx.x >> 4);
   bool valid = gid < total_groups;
@@ -195,30 +249,72 @@ __global__ __launch_bounds__(kSwigluThreads) void swiglu_quant_kernel(const uint
   const uint4 uraw = *reinterpret_cast<const uint4*>(proj + m * ldp + I + col);
   const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
   const uint32_t uw[4] = {uraw.x, uraw.y, uraw.z, uraw.w};
-  float h[8];
+  float gate[8], up[8], h[8];
+  uint32_t slow_silu = 0, slow_mul = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t gb = (gw[i / 2] >> (16 * (i & 1))) & 0xffffu;
-    const uint32_t ub = (uw[i / 2] >> (16 * (i & 1))) & 0xffffu;
-    const float sb = bf16_value(silu_bf16(bf16_value(gb)));
-    h[i] = bf16_value(mul_bf16(sb, bf16_value(ub)));
+    gate[i] = bf16_value((gw[i / 2] >> (16 * (i & 1))) & 0xffffu);
+    up[i] = bf16_value((uw[i / 2] >> (16 * (i & 1))) & 0xffffu);
+    bool decided;
+    const float sb = bf16_value(silu_bf16_f32(gate[i], decided));
+    slow_silu |= (decided ? 0u : 1u) << i;
+    const float pr = sb * up[i];
+    slow_mul |= (product_exact(pr, sb, up[i]) ? 0u : 1u) << i;
+    h[i] = round_bf16(pr);
   }
-  float amax = 0.f;
+  // Rare: elements whose silu is near a bf16 midpoint or tiny, or whose product underflows, are
+  // formed again in float64 (a wave enters only if one of its lanes has such an element).
+  if (slow_silu | slow_mul) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+    for (int i = 0; i < 8; ++i) {
+      if ((slow_silu | slow_mul) >> i & 1u) {
+        bool decided;
+        const uint32_t fast = silu_bf16_f32(gate[i], decided);
+        const float sb = bf16_value((slow_silu >> i & 1u) ? silu_bf16_f64(gate[i]) : fast);
+        const float pr = sb * up[i];
+        h[i] = product_exact(pr, sb, up[i]) ? round_bf16(pr) : bf16_value(mul_bf16_f64(sb, up[i]));
+      }
+    }
+  }
+  if constexpr (kQuant) {
+    float amax = 0.f;
 #pragma unroll
-  for (int mask = 1; mask < 16; mask <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mask));
-  const float s = fmaxf(amax, 1e-10f) / 448.0f;
-  float y[8];
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(h[i] / s, -448.0f), 448.0f);
-  uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-  uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-  if (valid) {
-    *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(w0, w1);
-    if (sub == 0) as[(int64_t)g * ld_as + m] = s;
+    for (int mask = 1; mask < 16; mask <<= 1) amax = fmaxf(amax, __shfl_xor(amax, mask));
+    const float s = fmaxf(amax, 1e-10f) / 448.0f;  // correctly rounded divide
+    float y[8];
+    if (s < __builtin_huge_valf()) {
+      // h / s without a divide per element: the correctly rounded reciprocal r, q0 = h r and one
+      // Newton correction with the exact residual h - q0 s. For every bf16 h and every finite
+      // scale of the quantizer this gives the correctly rounded quotient, or a quotient below
+      // 2^-10 in magnitude of the same sign (both encode as that signed zero).
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q0 = h[i] * r;
+        const float e = fmaf(-q0, s, h[i]);
+        y[i] = fminf(fmaxf(copysignf(fmaf(e, r, q0), h[i]), -448.0f), 448.0f);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(h[i] / s, -448.0f), 448.0f);
+    }
+    uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+    uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+    if (valid) {
+      *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(w0, w1);
+      if (sub == 0) as[(int64_t)g * ld_as + m] = s;
+    }
+  } else {
+    uint4 o;
+    o.x = (__float_as_uint(h[0]) >> 16) | (__float_as_uint(h[1]) & 0xffff0000u);
+    o.y = (__float_as_uint(h[2]) >> 16) | (__float_as_uint(h[3]) & 0xffff0000u);
+    o.z = (__float_as_uint(h[4]) >> 16) | (__float_as_uint(h[5]) & 0xffff0000u);
+    o.w = (__float_as_uint(h[6]) >> 16) | (__float_as_uint(h[7]) & 0xffff0000u);
+    if (valid) *reinterpret_cast<uint4*>(h_out + m * ldh + col) = o;
   }
 }
 
@@ -284,8 +380,18 @@ hipError_t launch_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64
   const int groups_per_row = (int)(I / kBlock);
   const int64_t total = M * groups_per_row;
   const int64_t blocks = (total + kSwigluGroupsPerBlock - 1) / kSwigluGroupsPerBlock;
-  hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(kSwigluThreads), 0, stream, proj, ldp, (int)I,
-                     layout, q, ldq, as, ld_as, groups_per_row, total);
+  hipLaunchKernelGGL(swiglu_kernel<true>, dim3((unsigned)blocks), dim3(kSwigluThreads), 0, stream, proj, ldp, (int)I,
+                     layout, q, ldq, as, ld_as, (uint16_t*)nullptr, (int64_t)0, groups_per_row, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout, uint16_t* h,
+                         int64_t ldh, hipStream_t stream) {
+  const int groups_per_row = (int)(I / kBlock);
+  const int64_t total = M * groups_per_row;
+  const int64_t blocks = (total + kSwigluGroupsPerBlock - 1) / kSwigluGroupsPerBlock;
+  hipLaunchKernelGGL(swiglu_kernel<false>, dim3((unsigned)blocks), dim3(kSwigluThreads), 0, stream, proj, ldp, (int)I,
+                     layout, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr, (int64_t)0, h, ldh, groups_per_row, total);
   return hipGetLastError();
 }
 

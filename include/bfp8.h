@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 12
+#define BFP8_ABI_VERSION 13
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -376,6 +376,16 @@ bfp8_status_t bfp8_quant_act_gather(const void* x, int x_dtype, int64_t src_rows
  */
 bfp8_status_t bfp8_swiglu_quant(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout,
                                 uint8_t* q, int64_t ldq, float* as, int64_t ld_as, void* stream);
+
+/*
+ * bfp8_swiglu: the gate activation of bfp8_swiglu_quant without the quantization:
+ * h[m][i] = bf16( bf16(silu(gate)) * up ) as bf16 into h [M][ldh], the same values the fused
+ * call quantizes (silu rounded once to bf16, the product rounded once). Rows whose layout entry
+ * is -1 are not written (layout may be NULL). I a multiple of 128; proj and h rows 16-byte
+ * aligned. For a consumer that takes h in bf16, and to inspect the activation.
+ */
+bfp8_status_t bfp8_swiglu(const uint16_t* proj, int64_t M, int64_t I, int64_t ldp, const int32_t* layout, uint16_t* h,
+                          int64_t ldh, void* stream);
 
 /*
  * bfp8_moe_combine: y[t, :] = bf16( sum_j bf16(out[row_of_pair[p], :] * bf16(topk_weights[p])) ),

@@ -75,6 +75,78 @@ def test_swiglu_quant(gpu):
     np.testing.assert_array_equal(s.cpu().numpy()[ok].view(np.uint32), s_ref[ok].view(np.uint32))
 
 
+def _bf16_equal_or_both_nan(got_bits, want_bits, what):
+    got, want = np.asarray(got_bits, np.uint16), np.asarray(want_bits, np.uint16)
+    nan_g = (got & 0x7FFF) > 0x7F80
+    nan_w = (want & 0x7FFF) > 0x7F80
+    np.testing.assert_array_equal(nan_g, nan_w, err_msg=f"{what}: NaN positions")
+    bad = np.nonzero((got != want) & ~nan_w)
+    assert bad[0].size == 0, f"{what}: {bad[0].size} differ, first at {tuple(b[0] for b in bad)}: " \
+                             f"{got[bad][0]:#06x} vs {want[bad][0]:#06x}"
+
+
+def test_swiglu_silu_every_bf16_gate(gpu):
+    """With up = 1, h = bf16(silu(gate)) exactly: all 65536 gate bit patterns (zeros, subnormals,
+    values that underflow silu to a subnormal or to zero, the largest finite values, infinities,
+    NaNs) against the oracle's float64 silu rounded once."""
+    gate = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(64, 1024)
+    up = np.full_like(gate, 0x3F80)  # 1.0
+    proj = np.concatenate([gate, up], axis=1)
+    announce("swiglu every bf16 gate")
+    h = bfp8.swiglu(torch.from_numpy(proj.view(np.int16)).view(torch.bfloat16).to(gpu))
+    torch.cuda.synchronize()
+    want = moe.swiglu_ref(proj)
+    _bf16_equal_or_both_nan(bits(h), want, "silu over every bf16")
+
+
+def test_swiglu_products(gpu):
+    """h = bf16(bf16(silu(gate)) * up) over gates and ups spread across the whole exponent range:
+    products that underflow to subnormals and to zero, that overflow, signed zeros; padding rows
+    untouched."""
+    rng = np.random.default_rng(17)
+    m, i = 257, 1024
+    mant = rng.integers(0, 128, (m, 2 * i)).astype(np.uint32)
+    expo = rng.integers(1, 255, (m, 2 * i)).astype(np.uint32)
+    sign = rng.integers(0, 2, (m, 2 * i)).astype(np.uint32)
+    proj = ((sign << 15) | (expo << 7) | mant).astype(np.uint16)
+    proj[3, :i] = 0x8000  # -0 gates
+    proj[4, i:] = 0x0000  # zero ups
+    proj[5] = rng.integers(0x0001, 0x0080, 2 * i)  # subnormal gates and ups
+    proj[6, :i] = 0x4080  # gate 4.0; ups of every exponent
+    proj[6, i:] = ((np.arange(i) % 255 + 1) << 7).astype(np.uint16)
+    layout = np.where(rng.random(m) < 0.1, -1, 0).astype(np.int32)
+    layout[:8] = 0
+    announce("swiglu products", m, i)
+    out = torch.full((m, i), 7.0, dtype=torch.bfloat16, device=gpu)
+    bfp8.swiglu(torch.from_numpy(proj.view(np.int16)).view(torch.bfloat16).to(gpu),
+                torch.from_numpy(layout).to(gpu), out=out)
+    torch.cuda.synchronize()
+    got = bits(out)
+    want = moe.swiglu_ref(proj)
+    ok = layout >= 0
+    _bf16_equal_or_both_nan(got[ok], want[ok], "swiglu products")
+    assert (got[~ok] == 0x40E0).all(), "padding rows written"
+
+
+def test_swiglu_quant_is_quant_of_swiglu(gpu):
+    """The fused call's codes and scales equal quantizing the unfused call's h, at the experts
+    chain's width (I = 2048) with wide-ranged rows, all-tiny rows and an infinite element."""
+    rng = np.random.default_rng(18)
+    m, i = 384, 2048
+    proj = torch.from_numpy((rng.standard_normal((m, 2 * i)) * np.exp2(rng.integers(-30, 30, (m, 1)))
+                             ).astype(np.float32)).to(torch.bfloat16)
+    proj[9] *= 2.0**-120
+    proj[10, 5] = float("inf")
+    pd = proj.to(gpu)
+    announce("swiglu_quant vs quant_act(swiglu)", m, i)
+    q, s = bfp8.swiglu_quant(pd)
+    h = bfp8.swiglu(pd)
+    q2, s2 = bfp8.quant_act(h)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2)
+    assert torch.equal(s.contiguous().view(torch.int32), s2.contiguous().view(torch.int32))
+
+
 def test_combine(gpu):
     t, k, h = 129, 4, 1024
     rng = np.random.default_rng(15)
