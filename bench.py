@@ -48,7 +48,7 @@ N = K = 4096
 SWEEP_M = (1, 8, 9, 16, 24, 32, 64, 128, 160, 192, 224, 256, 512, 1024, 2048, 4096, 8192)
 DOMINANT_M = 8192
 LLC_BYTES = 256 * 2**20
-KERNEL_SOURCES = ["api.hip", "gemm_tiled.hip", "device_common.h", "launch.h"]  # the dominant GEMM's code
+KERNEL_SOURCES = ["gemm_tiled.hip", "device_common.h"]  # the dominant GEMM's device code (kernel and helpers)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
