@@ -502,15 +502,16 @@ def main() -> int:
         us = graph_time_us(chain_calls, 3)
         # the steps one by one, for the breakdown
         rop, por, lay, _ = bfp8.moe_dispatch(ids_d, e_c)
-        q_c, s_c = bfp8.quant_act_gather(x_c, por, k_c)
-        proj_c = bfp8.grouped_gemm_contiguous(q_c, s_c, wts_c[0], wts_c[1], lay)
+        q_c, s_c = bfp8.quant_act_scatter(x_c, rop, k_c, lay.numel())  # each token once, scales at its rows
+        proj_c = bfp8.grouped_gemm_gathered(q_c, s_c, wts_c[0], wts_c[1], lay, por, k_c)
         q2_c, s2_c = bfp8.swiglu_quant(proj_c, lay)
         out_c = bfp8.grouped_gemm_contiguous(q2_c, s2_c, wts_c[2], wts_c[3], lay)
         steps = {
             "dispatch": graph_time_us(lambda n: [bfp8.moe_dispatch(ids_d, e_c) for _ in range(n)], 8),
-            "quant_gather": graph_time_us(lambda n: [bfp8.quant_act_gather(x_c, por, k_c) for _ in range(n)], 8),
-            "grouped_up": graph_time_us(lambda n: [bfp8.grouped_gemm_contiguous(q_c, s_c, wts_c[0], wts_c[1], lay,
-                                                                                out=proj_c) for _ in range(n)], 3),
+            "quant_tokens": graph_time_us(lambda n: [bfp8.quant_act_scatter(x_c, rop, k_c, lay.numel())
+                                                     for _ in range(n)], 8),
+            "grouped_up": graph_time_us(lambda n: [bfp8.grouped_gemm_gathered(q_c, s_c, wts_c[0], wts_c[1], lay, por,
+                                                                              k_c, out=proj_c) for _ in range(n)], 3),
             "swiglu_quant": graph_time_us(lambda n: [bfp8.swiglu_quant(proj_c, lay) for _ in range(n)], 8),
             "grouped_down": graph_time_us(lambda n: [bfp8.grouped_gemm_contiguous(q2_c, s2_c, wts_c[2], wts_c[3], lay,
                                                                                   out=out_c) for _ in range(n)], 3),

@@ -23,10 +23,10 @@ from . import _native
 from ._native import SCHEDULES, LibraryMissing  # noqa: F401
 
 __all__ = [
-    "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "linear", "linear_workspace_bytes", "linear_fuses",
+    "quant_act", "gemm", "gemm_f16", "grouped_gemm_contiguous", "grouped_gemm_gathered", "linear", "linear_workspace_bytes", "linear_fuses",
     "quant_act_1x64", "gemm_1x64",
     "quant_act_ue8m0", "gemm_ue8m0", "grouped_gemm_contiguous_ue8m0", "ue8m0_scales",
-    "moe_padded_rows", "moe_dispatch", "quant_act_gather", "swiglu_quant", "moe_combine", "moe_forward",
+    "moe_padded_rows", "moe_dispatch", "quant_act_gather", "quant_act_scatter", "swiglu_quant", "swiglu", "moe_combine", "moe_forward",
     "moe_forward_workspace_bytes", "nn_to_nt_weights", "pad_k", "expand_act_scales", "expand_weight_scale", "set_schedule", "get_schedule", "schedule_for",
     "abi_version", "BfpError", "LibraryMissing",
 ]
@@ -292,6 +292,42 @@ def grouped_gemm_contiguous(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Ten
     return out
 
 
+def grouped_gemm_gathered(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+                          layout: torch.Tensor, row_src: torch.Tensor, src_div: int = 1,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """grouped_gemm_contiguous with gathered activation codes: row m of the [M, N] product uses
+    expert layout[m], reads its codes from row row_src[m] // src_div of a_q [rows, K] and its
+    scales from row m of a_s [M, ceil(K/128)] (group-major, as quant_act_scatter writes them);
+    rows with row_src < 0 are padding (layout -1, not written). With moe_dispatch: row_src =
+    pair_of_row, src_div = top_k."""
+    a_q, b_q = _as_u8(a_q, "a_q"), _as_u8(b_q, "b_q")
+    _require(a_q, "a_q", torch.uint8, 2)
+    _require(b_q, "b_q", torch.uint8, 3)
+    _require(a_s, "a_s", torch.float32, 2)
+    _require(b_s, "b_s", torch.float32, 3)
+    _require(layout, "layout", torch.int32, 1)
+    _require(row_src, "row_src", torch.int32, 1)
+    rows, k = a_q.shape
+    g, n, k2 = b_q.shape
+    m = layout.shape[0]
+    if k2 != k or row_src.shape[0] != m:
+        raise ValueError("shape mismatch between a_q, b_q, layout and row_src")
+    _check_expert_codes(b_q)
+    if not (b_s.is_contiguous() and layout.is_contiguous() and row_src.is_contiguous()):
+        raise ValueError("b_s, layout and row_src must be contiguous")
+    if tuple(b_s.shape) != (g, -(-n // 128), -(-k // 128)) or tuple(a_s.shape) != (m, -(-k // 128)):
+        raise ValueError("scale shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    _require(out, "out", torch.bfloat16, 2)
+    st = _native.lib().bfp8_grouped_gemm_gathered(
+        a_q.data_ptr(), a_q.stride(0), a_s.data_ptr(), _scale_ld_as(a_s, m), rows, row_src.data_ptr(), src_div,
+        b_q.data_ptr(), b_q.stride(1), b_s.data_ptr(), b_s.stride(1), layout.data_ptr(), g, out.data_ptr(),
+        out.stride(0), m, n, k, _stream(a_q.device))
+    _check(st, "bfp8_grouped_gemm_gathered")
+    return out
+
+
 def linear(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, bias: torch.Tensor | None = None,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """FP8 linear layer, bf16 (or fp16) in and out: per-1x128-group quantization of x [M, K], the
@@ -551,6 +587,27 @@ def quant_act_gather(x: torch.Tensor, row_src: torch.Tensor, src_div: int = 1):
                                              src_div, m, q.data_ptr(), q.stride(0), s.data_ptr(), max(m, 1),
                                              _stream(x.device))
     _check(st, "bfp8_quant_act_gather")
+    return q, s
+
+
+def quant_act_scatter(x: torch.Tensor, scale_dst: torch.Tensor, scale_fan: int, rows: int):
+    """quant_act of x [M, K] with each row's scales written to rows scale_dst[m * scale_fan + j] of
+    a [rows, ceil(K/128)] group-major scale matrix (entries < 0 skipped; rows no entry names are
+    left unwritten). Returns (q [M, K], s [rows, ceil(K/128)]). With moe_dispatch: scale_dst =
+    row_of_pair, scale_fan = top_k, rows = len(layout)."""
+    _require(x, "x", x.dtype, 2)
+    _require(scale_dst, "scale_dst", torch.int32, 1)
+    m, k = x.shape
+    if scale_dst.numel() != m * scale_fan or not scale_dst.is_contiguous():
+        raise ValueError("scale_dst must be a contiguous int32 vector of M * scale_fan entries")
+    if x.stride(1) != 1:
+        raise ValueError("x must be contiguous along K")
+    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    s = torch.empty((-(-k // 128), max(rows, 1)), dtype=torch.float32, device=x.device).t()[:rows]
+    st = _native.lib().bfp8_quant_act_scatter(x.data_ptr(), _in_dtype(x, "x"), m, k, x.stride(0), q.data_ptr(),
+                                              q.stride(0), s.data_ptr(), max(rows, 1), scale_dst.data_ptr(), scale_fan,
+                                              _stream(x.device))
+    _check(st, "bfp8_quant_act_scatter")
     return q, s
 
 

@@ -33,6 +33,8 @@ SIGNATURES = [
     ("bfp8_gemm", ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_grouped_gemm_contiguous", ctypes.c_int,
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    ("bfp8_grouped_gemm_gathered", ctypes.c_int,
+     [_vp, _i64, _vp, _i64, _i64, _vp, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i64, _i64, _vp]),
     ("bfp8_gemm_f16", ctypes.c_int,
      [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     ("bfp8_quant_act_1x64", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
@@ -47,6 +49,7 @@ SIGNATURES = [
     ("bfp8_moe_dispatch", ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     ("bfp8_quant_act_gather", ctypes.c_int,
      [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
+    ("bfp8_quant_act_scatter", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp]),
     ("bfp8_swiglu_quant", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]),
     ("bfp8_swiglu", ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     ("bfp8_moe_combine", ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _i64, _vp]),

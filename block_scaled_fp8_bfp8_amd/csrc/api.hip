@@ -391,12 +391,32 @@ bfp8_status_t bfp8_gemm_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, 
 
 namespace {
 
+// gathered: A has a_rows rows and row r of the GEMM reads its codes from A row
+// row_src[r] / src_div; its scales stay at column r of as (float scales only).
 bfp8_status_t grouped_gemm(const uint8_t* a, int64_t lda, const void* as, int64_t ld_as, const uint8_t* b,
                            int64_t ldb, const void* bs, int64_t ld_bs, const int32_t* grouped_layout, int32_t G,
                            uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
-                           size_t workspace_bytes, void* stream, bool e8) {
-  bfp8_status_t st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace,
-                                     workspace_bytes, true, e8);
+                           size_t workspace_bytes, void* stream, bool e8, bool gathered = false,
+                           const int32_t* row_src = nullptr, int32_t src_div = 1, int64_t a_rows = 0) {
+  bfp8_status_t st;
+  if (!gathered) {
+    st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M, N, K, workspace, workspace_bytes, true, e8);
+  } else {
+    if (M < 0) return fail(BFP8_ERR_INVALID_ARGUMENT, "M = %lld is negative", (long long)M);
+    if (M > kMaxDim) return fail(BFP8_ERR_UNSUPPORTED, "M must be at most 2^30");
+    if (M > 0 && a_rows < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "a_rows = %lld must be >= 1", (long long)a_rows);
+    if (src_div < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "src_div = %d must be >= 1", (int)src_div);
+    if (M > 0 && !row_src) return fail(BFP8_ERR_INVALID_ARGUMENT, "row_src must not be NULL");
+    if (!aligned(row_src, 4)) return fail(BFP8_ERR_MISALIGNED, "row_src must be 4-byte aligned");
+    // A and its scales as a GEMM of a_rows rows; C as one of M rows (c, ldc and N checked here too)
+    st = check_gemm_args(a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, M > 0 ? a_rows : 0, N, K, workspace,
+                         workspace_bytes, true, false);
+    if (st == BFP8_OK && ld_as < M)
+      st = fail(BFP8_ERR_INVALID_ARGUMENT, "ld_as = %lld < M = %lld (one scale column per row of the product)",
+                (long long)ld_as, (long long)M);
+    if (st == BFP8_OK && M > 0 && ((M + 63) / 64) * ((N + 127) / 128) > (int64_t)INT32_MAX)
+      st = fail(BFP8_ERR_UNSUPPORTED, "M x N has more output tiles than one launch grid holds");
+  }
   if (st != BFP8_OK) return st;
   if (G < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "G = %d must be >= 1", (int)G);
   if (M % bfp8::kBlock != 0)
@@ -408,8 +428,10 @@ bfp8_status_t grouped_gemm(const uint8_t* a, int64_t lda, const void* as, int64_
   if (M == 0) return ok();
   st = check_device();
   if (st != BFP8_OK) return st;
-  const bfp8::GemmArgs args{a,   lda,    as,     ld_as,  b,              ldb,    bs,      ld_bs, c,
-                            ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G, nullptr, e8};
+  bfp8::GemmArgs args{a,   lda,    as,     ld_as,  b,              ldb,    bs,      ld_bs, c,
+                      ldc, (int)M, (int)N, (int)K, grouped_layout, (int)G, nullptr, e8};
+  args.a_row_src = row_src;
+  args.a_row_div = src_div;
   return launched(bfp8::launch_grouped_tiled(args, (hipStream_t)stream), "grouped_gemm_tiled");
 }
 
@@ -424,6 +446,14 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
                                            void* stream) {
   return grouped_gemm(a, lda, as, ld_as, b, ldb, bs, ld_bs, grouped_layout, G, c, ldc, M, N, K, workspace,
                       workspace_bytes, stream, false);
+}
+
+bfp8_status_t bfp8_grouped_gemm_gathered(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as, int64_t a_rows,
+                                         const int32_t* row_src, int32_t src_div, const uint8_t* b, int64_t ldb,
+                                         const float* bs, int64_t ld_bs, const int32_t* grouped_layout, int32_t G,
+                                         uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  return grouped_gemm(a, lda, as, ld_as, b, ldb, bs, ld_bs, grouped_layout, G, c, ldc, M, N, K, nullptr, 0, stream,
+                      false, true, row_src, src_div, a_rows);
 }
 
 bfp8_status_t bfp8_grouped_gemm_contiguous_ue8m0(const uint8_t* a, int64_t lda, const uint8_t* as, int64_t ld_as,
@@ -571,8 +601,8 @@ MoeLayout moe_layout(int64_t T, int32_t top_k, int32_t E, int64_t H, int64_t I) 
   L.layout = off; off += up(4 * R);
   L.expert_start = off; off += up(4 * ((size_t)E + 1));
   L.scratch = off; off += up(bfp8_moe_dispatch_workspace_bytes(S, E));
-  L.q = off; off += up(R * (size_t)H);
-  L.as = off; off += up(4 * (size_t)(H / bfp8::kBlock) * R);
+  L.q = off; off += up((size_t)T * (size_t)H);  // the tokens quantized once, [T][H]
+  L.as = off; off += up(4 * (size_t)(H / bfp8::kBlock) * R);  // their scales at the padded rows
   L.proj = off; off += up(2 * R * 2 * (size_t)I);
   L.q2 = off; off += up(R * (size_t)I);
   L.as2 = off; off += up(4 * (size_t)(I / bfp8::kBlock) * R);
@@ -644,6 +674,22 @@ bfp8_status_t bfp8_swiglu(const uint16_t* proj, int64_t M, int64_t I, int64_t ld
   return launched(bfp8::launch_swiglu(proj, M, I, ldp, layout, h, ldh, (hipStream_t)stream), "swiglu");
 }
 
+bfp8_status_t bfp8_quant_act_scatter(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                     int64_t ldq, float* as, int64_t ld_as, const int32_t* scale_dst,
+                                     int32_t scale_fan, void* stream) {
+  bfp8_status_t st = check_quant_args(x, x_dtype, M, K, ldx, q, ldq, as, ld_as);
+  if (st != BFP8_OK || M == 0) return st;
+  if (scale_fan < 1) return fail(BFP8_ERR_INVALID_ARGUMENT, "scale_fan = %d must be >= 1", (int)scale_fan);
+  if (M * scale_fan > (int64_t)INT32_MAX) return fail(BFP8_ERR_UNSUPPORTED, "M * scale_fan must be below 2^31");
+  if (!scale_dst) return fail(BFP8_ERR_INVALID_ARGUMENT, "scale_dst must not be NULL");
+  if (!aligned(scale_dst, 4)) return fail(BFP8_ERR_MISALIGNED, "scale_dst must be 4-byte aligned");
+  st = check_device();
+  if (st != BFP8_OK) return st;
+  return launched(bfp8::launch_quant_act(x, x_dtype, M, K, ldx, q, ldq, as, ld_as, false, (hipStream_t)stream,
+                                         nullptr, 1, scale_dst, scale_fan),
+                  "quant_act_scatter");
+}
+
 bfp8_status_t bfp8_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* row_of_pair,
                                const float* topk_weights, int64_t T, int32_t top_k, int64_t H, uint16_t* y,
                                int64_t ldy, void* stream) {
@@ -697,9 +743,11 @@ bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int
   uint16_t* out = reinterpret_cast<uint16_t*>(ws + L.out);
   // Every argument of every step, validated before the first launch.
   bfp8_status_t st = check_dispatch_args(topk_ids, S, E, bfp8::kBlock, row_of_pair, pair_of_row, layout, expert_start);
-  if (st == BFP8_OK) st = check_quant_args(hidden, BFP8_IN_BF16, R, H, ldh, q, H, as, R);
+  if (st == BFP8_OK) st = check_quant_args(hidden, BFP8_IN_BF16, T, H, ldh, q, H, as, R);
+  // The up projection reads its codes (T token rows) through the row map and its scales at the
+  // R padded rows; its R output rows are the workspace's proj, checked with the SwiGLU step.
   if (st == BFP8_OK)
-    st = check_gemm_args(q, H, as, R, w_up, H, s_up, H / bfp8::kBlock, proj, 2 * I, R, 2 * I, H, nullptr, 0, true);
+    st = check_gemm_args(q, H, as, R, w_up, H, s_up, H / bfp8::kBlock, proj, 2 * I, T, 2 * I, H, nullptr, 0, true);
   if (st == BFP8_OK) st = check_swiglu_args(proj, R, I, 2 * I, layout, q2, I, as2, R);
   if (st == BFP8_OK)
     st = check_gemm_args(q2, I, as2, R, w_down, I, s_down, I / bfp8::kBlock, out, H, R, H, I, nullptr, 0, true);
@@ -712,12 +760,17 @@ bfp8_status_t bfp8_moe_forward(const uint16_t* hidden, int64_t T, int64_t H, int
   st = dispatch(topk_ids, S, E, bfp8::kBlock, row_of_pair, pair_of_row, layout, expert_start,
                 reinterpret_cast<int32_t*>(ws + L.scratch), stream);
   if (st != BFP8_OK) return st;
-  st = launched(bfp8::launch_quant_act(hidden, BFP8_IN_BF16, R, H, ldh, q, H, as, R, false, (hipStream_t)stream,
-                                       pair_of_row, top_k),
-                "quant_act_gather");
+  // Each token is quantized once, its scales written at its padded rows (row_of_pair); the up
+  // projection reads padded row r's codes from token pair_of_row[r] / top_k. Codes and scales
+  // are the gathered quantizer's, so the product is that of the quantized padded rows.
+  st = launched(bfp8::launch_quant_act(hidden, BFP8_IN_BF16, T, H, ldh, q, H, as, R, false, (hipStream_t)stream,
+                                       nullptr, 1, row_of_pair, top_k),
+                "quant_act_scatter");
   if (st != BFP8_OK) return st;
-  const bfp8::GemmArgs up_args{q, H, as, R, w_up, H, s_up, H / bfp8::kBlock, proj, 2 * I, (int)R, (int)(2 * I),
-                               (int)H, layout, E, nullptr, false};
+  bfp8::GemmArgs up_args{q, H, as, R, w_up, H, s_up, H / bfp8::kBlock, proj, 2 * I, (int)R, (int)(2 * I),
+                         (int)H, layout, E, nullptr, false};
+  up_args.a_row_src = pair_of_row;
+  up_args.a_row_div = top_k;
   st = launched(bfp8::launch_grouped_tiled(up_args, (hipStream_t)stream), "grouped_gemm_up");
   if (st != BFP8_OK) return st;
   st = launched(bfp8::launch_swiglu_quant(proj, R, I, 2 * I, layout, q2, I, as2, R, (hipStream_t)stream),

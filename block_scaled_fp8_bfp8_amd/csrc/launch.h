@@ -33,6 +33,11 @@ struct GemmArgs {
   // inside the scaled MFMA and accumulate in its FP32 accumulator (no separate promotion).
   bool e8;
   bool out_f16;  // C (and bias) are fp16 instead of bf16
+  // Tiled schedule with float scales only: a gathered A. When set, GEMM row r reads its codes
+  // from activation row a_row_src[r] / a_row_div of a (row 0 where the entry is negative:
+  // padding, whose results are never stored); its scales stay at column r of as.
+  const int32_t* a_row_src = nullptr;
+  int a_row_div = 1;
 };
 
 // Tiled-schedule plan for a dense GEMM: tile shape, and the workspace it needs (none so far).
@@ -48,7 +53,8 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K);
 // not written.
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream,
-                            const int32_t* src_rows = nullptr, int src_div = 1);
+                            const int32_t* src_rows = nullptr, int src_div = 1, const int32_t* scale_dst = nullptr,
+                            int scale_fan = 1);
 
 // 1x64 groups: scales [ceil(K/64)][ld_as], float32.
 hipError_t launch_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,

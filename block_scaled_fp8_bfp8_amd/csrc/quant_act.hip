@@ -42,13 +42,17 @@ constexpr int64_t kWideGroups = 32768;
 // Gather variant (kGather): output row m quantizes input row src_rows[m] / src_div, and rows
 // whose entry is negative are left unwritten (the MoE dispatch's padded buffer: entry = pair
 // index, src_div = top_k, so the input row is the pair's token).
+// Scattered scales (scale_dst != nullptr): row m's group scale is written to the columns
+// scale_dst[m * scale_fan + j], j < scale_fan, that are not negative, instead of column m (the
+// codes stay in row m): each token quantized once, its scales placed at its padded rows.
 template <int kIn, bool kE8, bool kGather, int kLanesPerGroup, int kGroup = kBlock>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int64_t ldx,
                                                                   uint8_t* __restrict__ q, int64_t ldq,
                                                                   void* __restrict__ as, int64_t ld_as,
                                                                   int groups_per_row, int64_t total_groups,
                                                                   const int32_t* __restrict__ src_rows, int src_div,
-                                                                  int64_t K) {
+                                                                  int64_t K, const int32_t* __restrict__ scale_dst,
+                                                                  int scale_fan) {
   constexpr int kPerLane = kGroup / kLanesPerGroup;  // consecutive elements per lane
   constexpr int kGroupsPerBlock = kQuantThreads / kLanesPerGroup;
   static_assert(kLanesPerGroup == 8 || kLanesPerGroup == 16, "8 or 16 lanes per group");
@@ -138,7 +142,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
     } else {
       *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(wq[0], wq[1]);
     }
-    if (sub == 0) {
+    if (!kE8 && scale_dst != nullptr) {
+      // the group's lanes share the destinations
+      for (int j = sub; j < scale_fan; j += kLanesPerGroup) {
+        const int32_t r = scale_dst[m * scale_fan + j];
+        if (r >= 0) static_cast<float*>(as)[(int64_t)g * ld_as + r] = s;
+      }
+    } else if (sub == 0) {
       if constexpr (kE8) {
         static_cast<uint8_t*>(as)[(int64_t)g * ld_as + m] = (uint8_t)(__float_as_uint(s) >> 23);
       } else {
@@ -155,25 +165,28 @@ namespace {
 template <int kIn, bool kE8, int L>
 void launch_quant_lanes(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as,
                         int groups_per_row, int64_t total, const int32_t* src_rows, int src_div, int64_t K,
-                        hipStream_t stream) {
+                        const int32_t* scale_dst, int scale_fan, hipStream_t stream) {
   constexpr int kGroupsPerBlock = kQuantThreads / L;
   const int64_t blocks = (total + kGroupsPerBlock - 1) / kGroupsPerBlock;
   if (src_rows) {
     hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, true, L>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, scale_dst, scale_fan);
   } else {
     hipLaunchKernelGGL((quant_act_kernel<kIn, kE8, false, L>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K);
+                       x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, scale_dst, scale_fan);
   }
 }
 
 template <int kIn, bool kE8>
 void launch_quant_cfg(const void* x, int64_t ldx, uint8_t* q, int64_t ldq, void* as, int64_t ld_as, int groups_per_row,
-                      int64_t total, const int32_t* src_rows, int src_div, int64_t K, hipStream_t stream) {
+                      int64_t total, const int32_t* src_rows, int src_div, int64_t K, const int32_t* scale_dst,
+                      int scale_fan, hipStream_t stream) {
   if (total < kWideGroups) {
-    launch_quant_lanes<kIn, kE8, 16>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    launch_quant_lanes<kIn, kE8, 16>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, scale_dst,
+                                     scale_fan, stream);
   } else {
-    launch_quant_lanes<kIn, kE8, 8>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    launch_quant_lanes<kIn, kE8, 8>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, scale_dst,
+                                    scale_fan, stream);
   }
 }
 
@@ -187,32 +200,36 @@ hipError_t launch_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t 
   const dim3 grid((unsigned)((total + kGroupsPerBlock - 1) / kGroupsPerBlock));
   if (x_dtype == kInBf16) {
     hipLaunchKernelGGL((quant_act_kernel<kInBf16, false, false, 8, 64>), grid, dim3(kQuantThreads), 0, stream, x, ldx,
-                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K);
+                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K, nullptr, 1);
   } else if (x_dtype == kInF16) {
     hipLaunchKernelGGL((quant_act_kernel<kInF16, false, false, 8, 64>), grid, dim3(kQuantThreads), 0, stream, x, ldx,
-                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K);
+                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K, nullptr, 1);
   } else {
     hipLaunchKernelGGL((quant_act_kernel<kInF32, false, false, 8, 64>), grid, dim3(kQuantThreads), 0, stream, x, ldx,
-                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K);
+                       q, ldq, as, ld_as, groups_per_row, total, nullptr, 1, K, nullptr, 1);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, void* as, int64_t ld_as, bool e8, hipStream_t stream, const int32_t* src_rows,
-                            int src_div) {
+                            int src_div, const int32_t* scale_dst, int scale_fan) {
   const int groups_per_row = (int)((K + kBlock - 1) / kBlock);
   const int64_t total = M * groups_per_row;
+#define BFP8_QUANT_CFG(IN, E8)                                                                                    \
+  launch_quant_cfg<IN, E8>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, scale_dst, scale_fan, \
+                           stream)
   if (x_dtype == kInBf16) {
-    if (e8) launch_quant_cfg<kInBf16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
-    else launch_quant_cfg<kInBf16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    if (e8) BFP8_QUANT_CFG(kInBf16, true);
+    else BFP8_QUANT_CFG(kInBf16, false);
   } else if (x_dtype == kInF16) {
-    if (e8) launch_quant_cfg<kInF16, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
-    else launch_quant_cfg<kInF16, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    if (e8) BFP8_QUANT_CFG(kInF16, true);
+    else BFP8_QUANT_CFG(kInF16, false);
   } else {
-    if (e8) launch_quant_cfg<kInF32, true>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
-    else launch_quant_cfg<kInF32, false>(x, ldx, q, ldq, as, ld_as, groups_per_row, total, src_rows, src_div, K, stream);
+    if (e8) BFP8_QUANT_CFG(kInF32, true);
+    else BFP8_QUANT_CFG(kInF32, false);
   }
+#undef BFP8_QUANT_CFG
   return hipGetLastError();
 }
 

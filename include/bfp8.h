@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BFP8_ABI_VERSION 13
+#define BFP8_ABI_VERSION 15
 
 typedef enum bfp8_status {
   BFP8_OK = 0,
@@ -200,6 +200,29 @@ bfp8_status_t bfp8_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const 
                                            const int32_t* grouped_layout, int32_t G,
                                            uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bfp8_grouped_gemm_gathered: bfp8_grouped_gemm_contiguous with the activation codes gathered
+ * through an index instead of laid out in the padded order (the experts forward quantizes each
+ * token once and reads it for each of its experts). Row m of the M-row product reads its codes
+ * from row row_src[m] / src_div of a [a_rows][lda]; rows with row_src[m] < 0 read row 0
+ * (padding rows: the layout marks them -1, they are not written). Its scales are column m of
+ * as, as in bfp8_grouped_gemm_contiguous (bfp8_quant_act_scatter puts them there). With the
+ * dispatch, row_src = pair_of_row and src_div = top_k.
+ *   a, lda   as in bfp8_gemm for a GEMM of a_rows rows
+ *   as, ld_as  device, [ceil(K/128)][ld_as] float32, ld_as >= M: scales of the product's rows
+ *   row_src  device, int32 [M], 4-byte aligned; entries -1 or in [0, a_rows * src_div)
+ *            (device data, not checked)
+ *   src_div  >= 1
+ *   b, ldb, bs, ld_bs, grouped_layout, G, c, ldc, M, N, K  as in bfp8_grouped_gemm_contiguous
+ * The product equals bfp8_grouped_gemm_contiguous on the gathered codes, bit for bit. Float
+ * scales only; no workspace.
+ */
+bfp8_status_t bfp8_grouped_gemm_gathered(const uint8_t* a, int64_t lda, const float* as, int64_t ld_as,
+                                         int64_t a_rows, const int32_t* row_src, int32_t src_div,
+                                         const uint8_t* b, int64_t ldb, const float* bs, int64_t ld_bs,
+                                         const int32_t* grouped_layout, int32_t G, uint16_t* c, int64_t ldc,
+                                         int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Bytes of device workspace bfp8_linear needs (0 when M == 0): the quantized activations
  * (M * K bytes), their scales (4 * M * K / 128 bytes) and the GEMM's workspace, each part
@@ -365,6 +388,19 @@ bfp8_status_t bfp8_moe_dispatch(const int32_t* topk_ids, int64_t S, int32_t E, i
 bfp8_status_t bfp8_quant_act_gather(const void* x, int x_dtype, int64_t src_rows, int64_t K, int64_t ldx,
                                     const int32_t* row_src, int32_t src_div, int64_t M, uint8_t* q,
                                     int64_t ldq, float* as, int64_t ld_as, void* stream);
+
+/*
+ * bfp8_quant_act_scatter: bfp8_quant_act of x [M][ldx] (codes into q row m), with each group's
+ * scale written to the columns scale_dst[m * scale_fan + j] (j < scale_fan) that are not
+ * negative, instead of column m: as[g * ld_as + scale_dst[m * scale_fan + j]]. With the
+ * dispatch (scale_dst = row_of_pair, scale_fan = top_k) each token is quantized once and its
+ * scales land at its padded rows, ready for bfp8_grouped_gemm_gathered. Entries of scale_dst
+ * must be -1 or below ld_as (device data, not checked); x_dtype BFP8_IN_F32, BFP8_IN_BF16 or
+ * BFP8_IN_F16; other arguments and checks as in bfp8_quant_act (ld_as >= M).
+ */
+bfp8_status_t bfp8_quant_act_scatter(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                     int64_t ldq, float* as, int64_t ld_as, const int32_t* scale_dst,
+                                     int32_t scale_fan, void* stream);
 
 /*
  * bfp8_swiglu_quant: the gate activation fused with the second quantization. Row m of

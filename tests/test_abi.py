@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bfp8_abi_version() == 13
+    assert lib.bfp8_abi_version() == 15
     for code, name in [(0, b"BFP8_OK"), (1, b"BFP8_ERR_INVALID_ARGUMENT"), (2, b"BFP8_ERR_UNSUPPORTED"),
                        (3, b"BFP8_ERR_MISALIGNED"), (4, b"BFP8_ERR_WORKSPACE"), (5, b"BFP8_ERR_DEVICE"),
                        (6, b"BFP8_ERR_LAUNCH")]:

@@ -48,8 +48,8 @@ def test_workspace_sizes(lib):
     assert lib.bfp8_moe_dispatch_workspace_bytes(-1, 4) == 0
     small = lib.bfp8_moe_forward_workspace_bytes(512, 8, 16, 7168, 2048)
     rows = lib.bfp8_moe_padded_rows(512 * 8, 16, 128)
-    # at least the two quantized activations, the up-projection output and the down output
-    assert small >= rows * 7168 + rows * 2048 * 2 * 2 + rows * 2048 + rows * 7168 * 2
+    # at least the tokens' codes, the up-projection output, the second codes and the down output
+    assert small >= 512 * 7168 + rows * 2048 * 2 * 2 + rows * 2048 + rows * 7168 * 2
     assert small % 256 == 0
     for args in [(0, 8, 16, 7168, 2048), (512, 0, 16, 7168, 2048), (512, 8, 0, 7168, 2048), (1 << 29, 8, 16, 128, 128)]:
         assert lib.bfp8_moe_forward_workspace_bytes(*args) == 0
@@ -160,3 +160,41 @@ def test_forward_rejections(lib, kw, status):
 
 def test_forward_t_zero_is_a_no_op(lib):
     assert _forward(lib, T=0, hidden=None, ids=None, w=None, y=None, ws=None) == _native.BFP8_OK
+
+
+def _gathered(lib, a=P1, lda=256, as_=P2, ld_as=128, rows=16, src=P3, div=2, b=P4, ldb=256, bs=P5, ld_bs=2, lay=P6,
+              G=4, c=P7, ldc=64, M=128, N=64, K=256):
+    return lib.bfp8_grouped_gemm_gathered(a, lda, as_, ld_as, rows, src, div, b, ldb, bs, ld_bs, lay, G, c, ldc, M, N,
+                                          K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), E_INV), (dict(M=100), E_INV), (dict(M=1 << 31), E_UNS), (dict(rows=0), E_INV), (dict(div=0), E_INV),
+    (dict(src=None), E_INV), (dict(src=P3 + 2), E_MIS), (dict(ld_as=15), E_INV), (dict(ld_as=100), E_INV),
+    (dict(lda=128), E_INV),
+    (dict(a=None), E_INV), (dict(as_=None), E_INV), (dict(c=None), E_INV), (dict(lay=None), E_INV),
+    (dict(lay=P6 + 2), E_MIS), (dict(G=0), E_INV), (dict(ldc=32), E_INV), (dict(K=200), E_UNS), (dict(b=None), E_INV),
+])
+def test_grouped_gathered_rejections(lib, kw, status):
+    assert _gathered(lib, **kw) == status, lib.bfp8_last_error_message()
+
+
+def test_grouped_gathered_m_zero_is_a_no_op(lib):
+    assert _gathered(lib, M=0, src=None, lay=None, rows=0) == _native.BFP8_OK
+
+
+def _scatter(lib, x=P1, dt=_native.BFP8_IN_BF16, M=16, K=256, ldx=256, q=P2, ldq=256, as_=P3, ld_as=64, dst=P4, fan=4):
+    return lib.bfp8_quant_act_scatter(x, dt, M, K, ldx, q, ldq, as_, ld_as, dst, fan, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), E_INV), (dict(dt=9), E_UNS), (dict(K=200), E_UNS), (dict(fan=0), E_INV), (dict(dst=None), E_INV),
+    (dict(dst=P4 + 2), E_MIS), (dict(ld_as=8), E_INV), (dict(q=None), E_INV), (dict(as_=None), E_INV),
+    (dict(M=1 << 29, fan=8, ld_as=1 << 30), E_UNS),
+])
+def test_quant_scatter_rejections(lib, kw, status):
+    assert _scatter(lib, **kw) == status, lib.bfp8_last_error_message()
+
+
+def test_quant_scatter_m_zero_is_a_no_op(lib):
+    assert _scatter(lib, M=0, x=None, q=None, as_=None, dst=None) == _native.BFP8_OK

@@ -176,21 +176,58 @@ def _chain_inputs(dev, t=192, k=4, e=8, h=256, i=256, sent=0.05):
     return _chain[key]
 
 
-def test_forward_equals_its_steps(gpu):
-    """bfp8_moe_forward, bit for bit, equals dispatch -> gathered quantization -> grouped GEMM ->
-    SwiGLU + quantization -> grouped GEMM -> combine called one by one."""
+@pytest.mark.parametrize("gathered", [True, False])
+def test_forward_equals_its_steps(gpu, gathered):
+    """bfp8_moe_forward, bit for bit, equals its steps called one by one: dispatch -> the tokens
+    quantized once, scales placed at their padded rows -> grouped GEMM reading the codes through
+    pair_of_row (the fused forward's own steps), or dispatch -> gathered quantization of the
+    padded rows -> contiguous grouped GEMM (the page's order); then SwiGLU + quantization ->
+    grouped GEMM -> combine."""
     x, ids, w, wts, (xd, idsd, wd, wu, su, wdn, sdn) = _chain_inputs(gpu)
     e = wu.shape[0]
-    announce("moe_forward fused vs steps")
+    announce("moe_forward fused vs steps", "gathered" if gathered else "padded rows")
     y = bfp8.moe_forward(xd, idsd, wd, wu, su, wdn, sdn)
     row_of_pair, pair_of_row, layout, _ = bfp8.moe_dispatch(idsd, e)
-    q, s = bfp8.quant_act_gather(xd, pair_of_row, ids.shape[1])
-    proj = bfp8.grouped_gemm_contiguous(q, s, wu, su, layout)
+    if gathered:
+        q, s = bfp8.quant_act_scatter(xd, row_of_pair, ids.shape[1], layout.numel())
+        proj = bfp8.grouped_gemm_gathered(q, s, wu, su, layout, pair_of_row, ids.shape[1])
+    else:
+        q, s = bfp8.quant_act_gather(xd, pair_of_row, ids.shape[1])
+        proj = bfp8.grouped_gemm_contiguous(q, s, wu, su, layout)
     q2, s2 = bfp8.swiglu_quant(proj, layout)
     out = bfp8.grouped_gemm_contiguous(q2, s2, wdn, sdn, layout)
     y2 = bfp8.moe_combine(out, row_of_pair, wd)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("t,k,e,h,n,sent", [(512, 8, 16, 7168, 4096, 0.0), (300, 6, 32, 1024, 640, 0.1),
+                                            (97, 2, 5, 400, 300, 0.2), (1, 1, 1, 256, 128, 0.0)])
+def test_gathered_grouped_equals_contiguous(gpu, t, k, e, h, n, sent):
+    """Tokens quantized once with their scales scattered to their padded rows, and the grouped
+    GEMM reading the token codes through pair_of_row, equal the gathered quantizer and the
+    contiguous grouped GEMM on the padded rows, bit for bit, on every non-padding row: the
+    benchmark's up projection, ragged N and K (K = 400: a partial last block), sentinel pairs
+    and a single token."""
+    x = workloads.act_normal_bf16(t, h, seed=40 + t).to(gpu)
+    ids, _ = workloads.moe_routing(t, k, e, seed=41 + t, sentinel_frac=sent)
+    ws = [workloads.weight(n, h, seed=42 + g) for g in range(e)]
+    wq = bfp8.pad_k(torch.stack([w_.q for w_ in ws]).to(gpu))
+    wsc = torch.stack([w_.s for w_ in ws]).to(gpu)
+    announce("gathered grouped GEMM vs contiguous", t, k, e, h, n, sent)
+    row_of_pair, pair_of_row, layout, _ = bfp8.moe_dispatch(ids.to(gpu), e)
+    q_tok, s_rows = bfp8.quant_act_scatter(x, row_of_pair, k, layout.numel())
+    q_one, s_one = bfp8.quant_act(x)
+    q_pad, s_pad = bfp8.quant_act_gather(x, pair_of_row, k)
+    a = bfp8.grouped_gemm_gathered(bfp8.pad_k(q_tok), s_rows, wq, wsc, layout, pair_of_row, k)
+    b = bfp8.grouped_gemm_contiguous(bfp8.pad_k(q_pad), s_pad, wq, wsc, layout)
+    torch.cuda.synchronize()
+    ok = (layout >= 0).cpu().numpy()
+    assert ok.any()
+    # the scattered quantizer: the plain quantizer's codes, the gathered quantizer's scales
+    assert torch.equal(q_tok, q_one)
+    np.testing.assert_array_equal(s_rows.cpu().numpy()[ok].view(np.uint32), s_pad.cpu().numpy()[ok].view(np.uint32))
+    np.testing.assert_array_equal(bits(a)[ok], bits(b)[ok])
 
 
 def _down_mass(x, ids, w, wts):
