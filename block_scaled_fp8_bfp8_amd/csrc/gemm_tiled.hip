@@ -138,13 +138,14 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   const uint8_t* asmat = static_cast<const uint8_t*>(args.as);
   const int prow_base = w * 8 * kCopies;
   const int lrow = lane >> 3;
-  // A gathered A: the row-map entries of the activation rows this lane copies, loaded first so
-  // that their round trip overlaps the layout read below.
+  // Grouped, with a gathered A: the row-map entries of the activation rows this lane copies,
+  // loaded first so that their round trip overlaps the layout read below.
   int a_map[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
     const int prow = prow_base + j * 8;  // uniform
-    a_map[j] = args.a_row_src != nullptr && prow >= BN ? args.a_row_src[min(m0 + prow - BN + lrow, M - 1)] : 0;
+    a_map[j] = kGrouped && args.a_row_src != nullptr && prow >= BN ? args.a_row_src[min(m0 + prow - BN + lrow, M - 1)]
+                                                                    : 0;
   }
   if constexpr (kGrouped) {
     int gid = -1;
@@ -171,8 +172,8 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     const int lcol = (lane & 7) ^ lds_swizzle(prow + lrow);
     // activation rows: the row itself, or with a gathered A the row its map entry names (the
     // codes only: the scales of row r stay at column r); padding entries (< 0) read row 0
-    const int arow = args.a_row_src == nullptr ? min(m0 + prow - BN + lrow, M - 1)
-                                               : (a_map[j] < 0 ? 0 : a_map[j] / args.a_row_div);
+    const int arow = !kGrouped || args.a_row_src == nullptr ? min(m0 + prow - BN + lrow, M - 1)
+                                                            : (a_map[j] < 0 ? 0 : a_map[j] / args.a_row_div);
     const int row = prow < BN ? min(n0 + prow + lrow, N - 1) : arow;
     const int64_t ld = prow < BN ? args.ldb : args.lda;
     coff[j] = (uint32_t)((int64_t)row * ld + lcol * 16);

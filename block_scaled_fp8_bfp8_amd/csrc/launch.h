@@ -33,7 +33,7 @@ struct GemmArgs {
   // inside the scaled MFMA and accumulate in its FP32 accumulator (no separate promotion).
   bool e8;
   bool out_f16;  // C (and bias) are fp16 instead of bf16
-  // Tiled schedule with float scales only: a gathered A. When set, GEMM row r reads its codes
+  // Grouped launches only (ignored elsewhere): a gathered A. When set, GEMM row r reads its codes
   // from activation row a_row_src[r] / a_row_div of a (row 0 where the entry is negative:
   // padding, whose results are never stored); its scales stay at column r of as.
   const int32_t* a_row_src = nullptr;
