@@ -360,6 +360,13 @@ bfp8_status_t bfp8_gemm_1x64(const uint8_t* a, int64_t lda, const float* as, int
   if (st != BFP8_OK) return st;
   const bfp8::GemmArgs args{a, lda, as, ld_as, b, ldb, bs, ld_bs, c, ldc, (int)M, (int)N, (int)K, nullptr, 1, nullptr,
                             false, false};
+  // The schedule override picks the kernel family; by default the tiled kernel takes the GEMMs
+  // with enough 256 x 128 tiles to fill the chip.
+  const int sched = g_schedule.load(std::memory_order_relaxed);
+  const int64_t tiles = ((N + 255) / 256) * ((M + 127) / 128);
+  const bool tiled = sched == BFP8_SCHED_TILED || sched == BFP8_SCHED_PERSISTENT ||
+                     (sched == BFP8_SCHED_AUTO && tiles >= bfp8::kTiled1x64MinTiles);
+  if (tiled) return launched(bfp8::launch_gemm_tiled_1x64(args, (hipStream_t)stream), "gemm_tiled_1x64");
   return launched(bfp8::launch_gemm_ksplit_1x64(args, (hipStream_t)stream), "gemm_ksplit_1x64");
 }
 

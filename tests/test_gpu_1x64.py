@@ -98,3 +98,49 @@ def test_gemm_1x64_deterministic_and_equal_half_scales(gpu):
     _, _, ref_bits, mass = tolerance.reference(q128_ref, s128_ref, wq.numpy(), ws128.numpy(), rows=rows)
     tolerance.compare(bits(c64)[rows], ref_bits, mass, k, "gemm_1x64 equal halves vs 1x128 oracle", k_block=64)
     tolerance.compare(bits(c128)[rows], ref_bits, mass, k, "gemm 1x128 (same inputs)")
+
+
+# The tiled schedule (256 x 128 tiles, two MFMAs and promotions per sub-tile and K block), forced
+# on shapes the automatic choice gives the K-split kernel and taken by default at large M: ragged
+# M and N, one and several tiles per XCD, K tails where the last 128-wide block has a partial or
+# absent second group, and a K of one block.
+@pytest.mark.parametrize("m,n,k", [(128, 256, 1024), (300, 520, 1040), (1000, 4096, 4160), (700, 1000, 4176),
+                                   (2048, 4096, 4096), (513, 384, 128), (96, 300, 208)])
+def test_gemm_1x64_tiled_against_oracle(gpu, m, n, k):
+    x = workloads.act_uniform(m, k, seed=940 + m)
+    q, s, q_ref, s_ref = _quant_checked(x, gpu, f"tiled {m}x{n}x{k}")
+    wq, ws = _weight(n, k, 941 + n % 89)
+    announce("gemm_1x64 tiled", m, n, k)
+    bfp8.set_schedule("tiled")
+    try:
+        c = bfp8.gemm_1x64(q, s, bfp8.pad_k(wq.to(gpu)), ws.to(gpu))
+        c2 = bfp8.gemm_1x64(q, s, bfp8.pad_k(wq.to(gpu)), ws.to(gpu))
+        torch.cuda.synchronize()
+    finally:
+        bfp8.set_schedule("auto")
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16)), "run to run"
+    rows = np.arange(m) if m <= 128 else np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).choice(m, 64, replace=False)]))
+    _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, wq.numpy(), ws.numpy(), rows=rows, k_block=64)
+    tolerance.compare(bits(c)[rows], ref_bits, mass, k, f"gemm_1x64 tiled {m}x{n}x{k}", k_block=64)
+
+
+def test_gemm_1x64_schedule_choice(gpu):
+    """Large M takes the tiled kernel by default; a forced K-split gives results of the same
+    oracle at that size (sampled rows)."""
+    m, n, k = 4096, 4096, 2048
+    x = workloads.act_uniform(m, k, seed=950)
+    q, s, q_ref, s_ref = _quant_checked(x, gpu, "schedule choice")
+    wq, ws = _weight(n, k, 951)
+    wq_d, ws_d = wq.to(gpu), ws.to(gpu)
+    announce("gemm_1x64 auto vs forced K-split", m, n, k)
+    c_auto = bfp8.gemm_1x64(q, s, wq_d, ws_d)
+    bfp8.set_schedule("small_m")
+    try:
+        c_ks = bfp8.gemm_1x64(q, s, wq_d, ws_d)
+        torch.cuda.synchronize()
+    finally:
+        bfp8.set_schedule("auto")
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(952).choice(m, 40, replace=False)]))
+    _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, wq.numpy(), ws.numpy(), rows=rows, k_block=64)
+    tolerance.compare(bits(c_auto)[rows], ref_bits, mass, k, "gemm_1x64 auto (tiled)", k_block=64)
+    tolerance.compare(bits(c_ks)[rows], ref_bits, mass, k, "gemm_1x64 forced K-split", k_block=64)
