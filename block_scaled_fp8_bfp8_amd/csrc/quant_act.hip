@@ -136,19 +136,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
     wq[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i + 2], y[4 * i + 3], wq[i], true);
   }
 
+  if (!kE8 && valid && scale_dst != nullptr) {
+    // the group's lanes share the destinations (also those past K in a partial last group)
+    for (int j = sub; j < scale_fan; j += kLanesPerGroup) {
+      const int32_t r = scale_dst[m * scale_fan + j];
+      if (r >= 0) static_cast<float*>(as)[(int64_t)g * ld_as + r] = s;
+    }
+  }
   if (store) {
     if constexpr (kPerLane == 16) {
       *reinterpret_cast<uint4*>(q + m * ldq + col) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
     } else {
       *reinterpret_cast<uint2*>(q + m * ldq + col) = make_uint2(wq[0], wq[1]);
     }
-    if (!kE8 && scale_dst != nullptr) {
-      // the group's lanes share the destinations
-      for (int j = sub; j < scale_fan; j += kLanesPerGroup) {
-        const int32_t r = scale_dst[m * scale_fan + j];
-        if (r >= 0) static_cast<float*>(as)[(int64_t)g * ld_as + r] = s;
-      }
-    } else if (sub == 0) {
+    if (sub == 0 && (kE8 || scale_dst == nullptr)) {  // scattered scales are written above
       if constexpr (kE8) {
         static_cast<uint8_t*>(as)[(int64_t)g * ld_as + m] = (uint8_t)(__float_as_uint(s) >> 23);
       } else {

@@ -202,13 +202,15 @@ def test_forward_equals_its_steps(gpu, gathered):
 
 
 @pytest.mark.parametrize("t,k,e,h,n,sent", [(512, 8, 16, 7168, 4096, 0.0), (300, 6, 32, 1024, 640, 0.1),
-                                            (97, 2, 5, 400, 300, 0.2), (1, 1, 1, 256, 128, 0.0)])
+                                            (97, 2, 5, 400, 300, 0.2), (1, 1, 1, 256, 128, 0.0),
+                                            (130, 8, 12, 272, 256, 0.1), (40, 20, 24, 528, 136, 0.0)])
 def test_gathered_grouped_equals_contiguous(gpu, t, k, e, h, n, sent):
     """Tokens quantized once with their scales scattered to their padded rows, and the grouped
     GEMM reading the token codes through pair_of_row, equal the gathered quantizer and the
     contiguous grouped GEMM on the padded rows, bit for bit, on every non-padding row: the
-    benchmark's up projection, ragged N and K (K = 400: a partial last block), sentinel pairs
-    and a single token."""
+    benchmark's up projection, ragged N and K (K = 400, 272, 528: a partial last block, whose
+    group has fewer lanes inside K than a token has pairs), sentinel pairs, top-20 and a single
+    token."""
     x = workloads.act_normal_bf16(t, h, seed=40 + t).to(gpu)
     ids, _ = workloads.moe_routing(t, k, e, seed=41 + t, sentinel_frac=sent)
     ws = [workloads.weight(n, h, seed=42 + g) for g in range(e)]
