@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libbfp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "quant_act.hip", "gemm_ksplit.hip", "gemm_tiled.hip", "gemm_persistent.hip", "moe.hip", "layout.hip"]
+SOURCES = ["api.hip", "quant_act.hip", "gemm_ksplit.hip", "gemm_tiled.hip", "gemm_g64.hip", "gemm_persistent.hip", "moe.hip",
+           "layout.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -366,7 +366,7 @@ bfp8_status_t bfp8_gemm_1x64(const uint8_t* a, int64_t lda, const float* as, int
   const int64_t tiles = ((N + 255) / 256) * ((M + 127) / 128);
   const bool tiled = sched == BFP8_SCHED_TILED || sched == BFP8_SCHED_PERSISTENT ||
                      (sched == BFP8_SCHED_AUTO && tiles >= bfp8::kTiled1x64MinTiles);
-  if (tiled) return launched(bfp8::launch_gemm_tiled_1x64(args, (hipStream_t)stream), "gemm_tiled_1x64");
+  if (tiled) return launched(bfp8::launch_gemm_g64(args, (hipStream_t)stream), "gemm_g64");
   return launched(bfp8::launch_gemm_ksplit_1x64(args, (hipStream_t)stream), "gemm_ksplit_1x64");
 }
 

@@ -193,6 +193,20 @@ __device__ __forceinline__ void wait_copies_upto() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Tile of workgroup `bid`: each XCD (bid % 8) owns a contiguous run of the tiles,
+// ordered in groups of `group_m` M-tiles with the M-tile index fastest.
+__device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int group_m, int& tn, int& tm) {
+  const int total = n_tiles * m_tiles;
+  int t = bid;
+  if (total % 8 == 0) t = (bid % 8) * (total / 8) + bid / 8;
+  const int band = group_m * n_tiles;
+  const int first_m = (t / band) * group_m;
+  const int gm = min(m_tiles - first_m, group_m);
+  const int r = t - (t / band) * band;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // XOR swizzle of the 16-byte columns of a 128-byte LDS row. A fragment read has 16 lanes

@@ -1,0 +1,405 @@
+// Blockwise FP8 GEMM with 1x64 activation groups and 128x64 weight blocks on gfx950's
+// 32x32x64 matrix-core product (mid and large M).
+//
+// Role: the 1x64 / 128x64 block-scale layouts that page "prhub.com.cn ... vllm/pull/49932",
+// section "风险与影响", names as the next ones: C[m, n] = bf16(sum_g P_g[m, n] As[g][m] Bs[n/128][g]),
+// g over the 64-wide K groups and P_g the FP32 dot product of the e4m3 codes over group g.
+//   * one v_mfma_scale_f32_32x32x64_f8f6f4 covers exactly one group of a 32x32 sub-tile, so each
+//     group's sum is one product's result with nothing masked (the 16x16x128 product spans two
+//     groups: it takes one product per group with the other half of the operand zeroed, half of
+//     the matrix-core work wasted);
+//   * tiles, copies and pipeline follow the 1x128 tiled kernel: a 256 x 128 tile of C^T
+//     (weight rows on the product's first operand, activation rows on its second) with 8 waves
+//     of 64 x 64, three LDS stages of (256 + 128) rows of 128 bytes filled by the direct-to-LDS
+//     copies with the conflict-free XOR swizzle, plus the block's two groups of activation
+//     scales; the workgroup barrier of iteration kb sits just before the first LDS read of
+//     block kb + 1 and the stage of block kb is refilled with block kb + 3 right after it;
+//   * promotion: acc += P_g * (As[g][m] * Bs[n/128][g]); lane l holds activation row l % 32 of a
+//     sub-tile and 16 of its weight rows, all inside one 128-row scale strip, so a sub-tile and
+//     group take one scale product and 16 FMAs, lagging their product by two steps.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bfp8 {
+
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// One 32x32x64 FP8 (e4m3 x e4m3) product with a zero accumulator input. Lane l supplies 32 K
+// bytes of row l % 32 of each operand, the lanes l < 32 one half of the 64-wide slice and the
+// others the other half; both operands are laid out alike, so which K index sits where does not
+// change the sum. Result register v of lane l is D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32], the
+// row index running over src0's rows and the column index over src1's. Zero scale operands
+// select the unscaled instruction.
+__device__ __forceinline__ v16f mfma_group(const v8i& src0, const v8i& src1) {
+  const v16f zero = {};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(src0, src1, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Zeroes the bytes of a group fragment that lie at or past K in a partial last K block: lane
+// (r, kc) holds bytes [64 h + 32 kc, 64 h + 32 kc + 32) of the block, of which the first `valid`
+// exist (K a multiple of 16, so whole dwords are kept or cleared).
+__device__ __forceinline__ v8i mask_group_tail(v8i f, int valid, int h, int kc) {
+  const int v = valid - 64 * h - 32 * kc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v >= 4 * (i + 1) ? f[i] : 0;
+  return f;
+}
+
+template <int BN, int BM, int WGN, int WGM, int STAGES, bool kTail>
+__global__ __launch_bounds__(WGN * WGM * 64) void gemm_g64_kernel(GemmArgs args) {
+  constexpr int kWaves = WGN * WGM;
+  constexpr int WN = BN / WGN, WM = BM / WGM;  // the wave tile
+  constexpr int TN = WN / 32, TM = WM / 32;    // 32 x 32 sub-tiles
+  constexpr int kRows = BN + BM;               // 128-byte LDS rows per stage: weights, then activations
+  constexpr int kStage = kRows * kBlock;
+  constexpr int kCopies = kRows / 8 / kWaves;  // 1 KB (8-row) copies per wave per K block
+  constexpr int kSteps = TM * TN * 2;          // (tm, tn, group half) per K block
+  static_assert(kRows % (8 * kWaves) == 0 && BN % 8 == 0, "each wave copies whole 8-row groups");
+  static_assert(kBlock % WN == 0, "a wave's weight rows lie in one scale strip");
+  static_assert(WN % 32 == 0 && WM % 32 == 0 && TM >= 2, "32 x 32 sub-tiles, two rows of them or more");
+  static_assert(BM % 64 == 0 && 2 * BM / 64 <= kWaves, "activation scales: one 64-lane copy per 64 rows and group");
+  static_assert(STAGES >= 3 && STAGES <= 8, "the refill of a stage follows the barrier of the block before");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES][kStage];
+  __shared__ __attribute__((aligned(16))) float as_lds[STAGES][2 * BM];  // [group half][activation row]
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = w % WGN, wm = w / WGN;
+  const int M = args.M, N = args.N;
+  const int n_tiles = (N + BN - 1) / BN, m_tiles = (M + BM - 1) / BM;
+  const int KB = (args.K + kBlock - 1) / kBlock;
+  const int G = (args.K + 63) / 64;  // 64-wide groups along K
+  const int k_tail = kTail ? args.K - (KB - 1) * kBlock : kBlock;
+  int tile_n, tile_m;
+  map_tile(blockIdx.x, n_tiles, m_tiles, 8, tile_n, tile_m);
+  const int n0 = tile_n * BN, m0 = tile_m * BM;
+
+  // Copy plan: wave w copies stage rows [8 kCopies w, 8 kCopies (w + 1)) in 8-row pieces; lane l of a piece
+  // lands at row prow + l / 8, physical 16-byte column l % 8, so it loads the logical column
+  // (l % 8) ^ swizzle(row). Rows past M or N are clamped to the last row (never stored).
+  const int prow_base = w * 8 * kCopies;
+  const int lrow = lane >> 3;
+  uint32_t coff[kCopies];
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    const int prow = prow_base + j * 8;  // uniform
+    const int lcol = (lane & 7) ^ lds_swizzle(prow + lrow);
+    const int row = prow < BN ? min(n0 + prow + lrow, N - 1) : min(m0 + prow - BN + lrow, M - 1);
+    const int64_t ld = prow < BN ? args.ldb : args.lda;
+    coff[j] = (uint32_t)((int64_t)row * ld + lcol * 16);
+  }
+  // Activation scales of K block kb: groups 2 kb and 2 kb + 1 (the latter clamped to the last
+  // group: a clamped group only meets K bytes past K, which the tail mask zeroes), BM rows
+  // each; waves 0 .. 2 BM / 64 - 1 copy 64 of them each, wave w the group half w / (BM / 64) and
+  // the rows (w % (BM / 64)) 64 + lane.
+  const bool copies_as = w < 2 * BM / 64;
+  const int as_h = w / (BM / 64);
+  const uint32_t as_voff = (uint32_t)min(m0 + (w % (BM / 64)) * 64 + lane, M - 1) * 4u;
+  const uint32_t as_dst_off = (uint32_t)(w * 64 * 4);
+  const uint8_t* asmat = static_cast<const uint8_t*>(args.as);
+
+  uint32_t stage_lds[STAGES], as_lds_addr[STAGES];
+#pragma unroll
+  for (int i = 0; i < STAGES; ++i) {
+    stage_lds[i] = lds_addr(&smem[i][0]);
+    as_lds_addr[i] = lds_addr(&as_lds[i][0]);
+  }
+  auto issue_piece = [&](int buf, int kb, int j) __attribute__((always_inline)) {
+    const uint8_t* src = prow_base + j * 8 < BN ? args.b + (int64_t)kb * kBlock : args.a + (int64_t)kb * kBlock;
+    copy16_to_lds(src, coff[j], stage_lds[buf] + (uint32_t)((prow_base + j * 8) * kBlock));
+  };
+  auto issue_scales = [&](int buf, int kb) __attribute__((always_inline)) {
+    if (copies_as)
+      copy4_to_lds(asmat + (int64_t)min(2 * kb + as_h, G - 1) * args.ld_as * 4, as_voff, as_lds_addr[buf] + as_dst_off);
+  };
+
+  // Weight scales of the wave's strip through the scalar cache: groups 2 kb and 2 kb + 1 (a
+  // second group past K gets 0, so its zeroed fragment adds nothing).
+  const __attribute__((address_space(4))) float* bs_row =
+      (const __attribute__((address_space(4))) float*)(static_cast<const uint8_t*>(args.bs) +
+                                                       (int64_t)(min(n0 + wn * WN, N - 1) / kBlock) * args.ld_bs * 4);
+  auto weight_scales = [&](int kb, float (&out)[2]) __attribute__((always_inline)) {
+    out[0] = bs_row[2 * kb];
+    out[1] = 2 * kb + 1 < G ? bs_row[2 * kb + 1] : 0.f;
+  };
+
+  // Group fragments: lane (r, kc) reads row row0 + r, bytes [64 h + 32 kc, +32), i.e. the logical
+  // 16-byte columns 4 h + 2 kc and 4 h + 2 kc + 1. Every fragment starts at a multiple of 32 rows,
+  // so row % 16 == r % 16 and the swizzle, hence the per-lane offsets, are shared by all of them.
+  const int r = lane & 31, kc = lane >> 5;
+  const int fsw = lds_swizzle(r);
+  uint32_t foff[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) foff[h][c] = (uint32_t)(r * kBlock + (((4 * h + 2 * kc + c) ^ fsw) << 4));
+  auto frag_at = [&](const uint8_t* stage, int row0, int h) __attribute__((always_inline)) -> v8i {
+    const v4i lo = *reinterpret_cast<const v4i*>(stage + foff[h][0] + row0 * kBlock);
+    const v4i hi = *reinterpret_cast<const v4i*>(stage + foff[h][1] + row0 * kBlock);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto frag_b = [&](const uint8_t* stage, int tn, int h) __attribute__((always_inline)) {
+    return frag_at(stage, wn * WN + tn * 32, h);
+  };
+  auto frag_a = [&](const uint8_t* stage, int tm, int h) __attribute__((always_inline)) {
+    return frag_at(stage, BN + wm * WM + tm * 32, h);
+  };
+  auto act_scale = [&](int slot, int tm, int h) __attribute__((always_inline)) -> float {
+    return as_lds[slot][h * BM + wm * WM + tm * 32 + r];
+  };
+
+  float acc[TN][TM][16];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tn][tm][e] = 0.f;
+
+  // Software pipeline. Step t = (tm TN + tn) 2 + h multiplies weight fragment (tn, h) by
+  // activation fragment (tm, h). Block kb is multiplied out of registers while block kb + 1 is
+  // read from LDS into the same registers, each fragment right after its last use (activation
+  // fragments at the end of their row tm, weight fragments in the last row). The barrier of
+  // iteration kb sits at step kBarStep, just before the first read of block kb + 1: past it,
+  // block kb + 1 has landed (every wave waited for its own copies of it) and every wave has
+  // finished reading block kb (read during iteration kb - 1), so stage kb % STAGES is refilled
+  // with block kb + STAGES from there on. The promotion of a step lags its product by two
+  // steps, across blocks too: the first two steps of block kb promote the last two of block
+  // kb - 1 with that block's scale products.
+  v8i fa[TM][2], fb[TN][2];
+  float sa[TM][2], bsv[2], sc[TM][2];
+  constexpr int kBarStep = 2 * TN - 1;
+  constexpr int kCopySpan = kSteps - kBarStep;
+  auto copy_step = [](int j) constexpr { return kBarStep + j * kCopySpan / kCopies; };
+  static_assert(copy_step(kCopies - 1) < kSteps, "every copy of a refill is issued inside the block");
+  auto wait_next_block = [&](bool steady) __attribute__((always_inline)) {
+    if (!steady) {
+      wait_copies();
+    } else if (copies_as) {
+      wait_copies_upto<(STAGES - 2) * (kCopies + 1)>();
+    } else {
+      wait_copies_upto<(STAGES - 2) * kCopies>();
+    }
+  };
+  auto promote = [&](int u, const v16f& pu, float s) __attribute__((always_inline)) {
+    const int um = u / (2 * TN), un = (u / 2) % TN;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[un][um][e] = fmaf(pu[e], s, acc[un][um][e]);
+    // Pin the promotion here: otherwise the FMAs are sunk past the loop's branch, since their
+    // results are only read in the next K block.
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      asm volatile("" : "+v"(acc[un][um][e]), "+v"(acc[un][um][e + 1]), "+v"(acc[un][um][e + 2]),
+                   "+v"(acc[un][um][e + 3]));
+  };
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) sc[tm][0] = sc[tm][1] = 0.f;
+  // The last two products of the previous block (zero before the first block: promoting them
+  // adds 0 * 0 to a zero accumulator).
+  v16f p1c = {}, p2c = {};
+
+  auto iter = [&](int kb, auto steady_c) __attribute__((always_inline)) {
+    constexpr bool kSteady = decltype(steady_c)::value;  // kb + STAGES < KB: refill a stage
+    const int cslot = kb % STAGES;
+    // The last iteration also reads a (stale, in-bounds) stage, which keeps the steps free of
+    // branches; those registers are never used.
+    const int nslot = (kb + 1) % STAGES;
+    const uint8_t* nstage = &smem[nslot][0];
+    const bool mask_next = kTail && kb + 1 == KB - 1;  // uniform
+    float bs_next[2];
+    weight_scales(min(kb + 1, KB - 1), bs_next);
+    v16f p1 = p1c, p2 = p2c;
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      const int tm = t / (2 * TN), tn = (t / 2) % TN, h = t % 2;
+      // The scale products of row tm are formed at the row's first step, while sa[tm] still
+      // holds this block's activation scales (the row's last step reloads them). Until then
+      // sc[TM - 1] keeps the previous block's, which its two lagging promotions use.
+      if (tn == 0 && h == 0) {
+        sc[tm][0] = sa[tm][0] * bsv[0];
+        sc[tm][1] = sa[tm][1] * bsv[1];
+      }
+      const v16f p = mfma_group(fb[tn][h], fa[tm][h]);
+      if (t >= 2) {
+        promote(t - 2, p2, sc[(t - 2) / (2 * TN)][t % 2]);
+      } else {
+        promote(kSteps - 2 + t, p2, sc[TM - 1][t % 2]);
+      }
+      if (t == kBarStep) {
+        wait_next_block(kSteady);
+        lds_barrier();
+        if constexpr (kSteady) issue_scales(cslot, kb + STAGES);
+      }
+      if constexpr (kSteady) {
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j)
+          if (t == copy_step(j)) issue_piece(cslot, kb + STAGES, j);
+      }
+      if (tn == TN - 1 && h == 1) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          fa[tm][hh] = frag_a(nstage, tm, hh);
+          if (mask_next) fa[tm][hh] = mask_group_tail(fa[tm][hh], k_tail, hh, kc);
+          sa[tm][hh] = act_scale(nslot, tm, hh);
+        }
+      }
+      if (tm == TM - 1) {
+        fb[tn][h] = frag_b(nstage, tn, h);
+        if (mask_next) fb[tn][h] = mask_group_tail(fb[tn][h], k_tail, h, kc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      p2 = p1;
+      p1 = p;
+    }
+    p1c = p1;
+    p2c = p2;
+    bsv[0] = bs_next[0];
+    bsv[1] = bs_next[1];
+  };
+
+#pragma unroll
+  for (int i = 0; i < STAGES; ++i) {
+    const int kb = min(i, KB - 1);
+    issue_scales(i, kb);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) issue_piece(i, kb, j);
+  }
+  // block 0 has landed once the copies of blocks 1 .. STAGES-1 are the only ones left
+  if (copies_as) {
+    wait_copies_upto<(STAGES - 1) * (kCopies + 1)>();
+  } else {
+    wait_copies_upto<(STAGES - 1) * kCopies>();
+  }
+  lds_barrier();
+  const bool mask_first = kTail && KB == 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      fa[tm][h] = frag_a(&smem[0][0], tm, h);
+      if (mask_first) fa[tm][h] = mask_group_tail(fa[tm][h], k_tail, h, kc);
+      sa[tm][h] = act_scale(0, tm, h);
+    }
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      fb[tn][h] = frag_b(&smem[0][0], tn, h);
+      if (mask_first) fb[tn][h] = mask_group_tail(fb[tn][h], k_tail, h, kc);
+    }
+  }
+  weight_scales(0, bsv);
+  int kb = 0;
+  for (; kb + STAGES < KB; ++kb) iter(kb, std::true_type{});
+  for (; kb < KB; ++kb) iter(kb, std::false_type{});
+  promote(kSteps - 2, p2c, sc[TM - 1][0]);
+  promote(kSteps - 1, p1c, sc[TM - 1][1]);
+  // Every wave's LDS reads (the last iteration's stale ones included) are done before the
+  // stages are reused below. No copy is in flight: the last iteration waited for all of them.
+  lds_barrier();
+
+  // Output. Register v of sub-tile (tn, tm) holds activation row tm 32 + r and weight row
+  // tn 32 + 8 (v / 4) + 4 kc + v % 4, so each quad of registers is 4 consecutive outputs of one
+  // row. With 16-byte stores allowed, each wave stages its tile in LDS as bf16 rows (padded by
+  // 16 bytes) and stores whole row segments of WN * 2 bytes.
+  const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
+  if (vec16) {
+    constexpr int kRowBytes = WN * 2 + 16;
+    static_assert(kWaves * WM * kRowBytes <= STAGES * kStage, "output staging fits the stages");
+    uint8_t* out_lds = &smem[0][0] + w * (WM * kRowBytes);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = f32_to_bf16_rne(acc[tn][tm][4 * q]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 1]) << 16);
+          pk.y = f32_to_bf16_rne(acc[tn][tm][4 * q + 2]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(out_lds + (tm * 32 + r) * kRowBytes + (tn * 32 + 8 * q + 4 * kc) * 2) = pk;
+        }
+    // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
+    // wave's accesses in order, and this keeps the compiler from reordering them.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    constexpr int kLanesPerRow = WN / 8;  // 16 bytes (8 outputs) per lane
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
+#pragma unroll
+    for (int pass = 0; pass < WM / kRowsPerPass; ++pass) {
+      const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+      const int seg = lane % kLanesPerRow;
+      const v4i v = *reinterpret_cast<const v4i*>(out_lds + row * kRowBytes + seg * 16);
+      const int m = m0 + wm * WM + row;
+      const int n = n0 + wn * WN + seg * 8;
+      if (m < M && n < N) {
+        uint16_t* cp = args.c + (int64_t)m * args.ldc + n;
+        if (n + 8 <= N) {
+          *reinterpret_cast<v4i*>(cp) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) cp[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
+        }
+      }
+    }
+    return;
+  }
+  const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = m0 + wm * WM + tm * 32 + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WN + tn * 32 + 8 * q + 4 * kc;
+        if (n < N)
+          store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1],
+                        acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3], nullptr, false);
+      }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+template <int BN, int BM, int WGN, int WGM, int STAGES>
+hipError_t launch_g64_cfg(const GemmArgs& args, hipStream_t stream) {
+  const dim3 grid((unsigned)(((args.N + BN - 1) / BN) * ((args.M + BM - 1) / BM)));
+  if (args.K % kBlock) {
+    hipLaunchKernelGGL((gemm_g64_kernel<BN, BM, WGN, WGM, STAGES, true>), grid, dim3(WGN * WGM * 64), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((gemm_g64_kernel<BN, BM, WGN, WGM, STAGES, false>), grid, dim3(WGN * WGM * 64), 0, stream,
+                       args);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The tile shape whose rounds of 256 workgroups (one per CU) take less time at the per-K-block
+// round times measured at N = K = 4096: 1.25 us for 256 x 128 tiles, 0.86 us for 128 x 128 (K
+// scales both alike). E.g. M = 1024: one round of 128 x 128 tiles (32.9 us) instead of one of
+// 256 x 128 (44.7 us); M = 1536: one round of 256 x 128 (45.1 us) instead of two of 128 x 128
+// (56.7 us).
+int g64_tile_n(int64_t M, int64_t N) {
+  const int64_t m_tiles = (M + 127) / 128;
+  const int64_t rounds256 = ((N + 255) / 256 * m_tiles + 255) / 256;
+  const int64_t rounds128 = ((N + 127) / 128 * m_tiles + 255) / 256;
+  return 1.25 * (double)rounds256 <= 0.86 * (double)rounds128 ? 256 : 128;
+}
+
+// bf16 output without bias (the 1x64 entry point has neither): 256 x 128 tiles (8 waves of
+// 64 x 64, three stages) or 128 x 128 (8 waves of 32 x 64, four stages), as g64_tile_n picks.
+hipError_t launch_gemm_g64(const GemmArgs& args, hipStream_t stream) {
+  if (args.bias != nullptr || args.out_f16 || args.e8) return hipErrorInvalidValue;
+  if (g64_tile_n(args.M, args.N) == 256) return launch_g64_cfg<256, 128, 4, 2, 3>(args, stream);
+  return launch_g64_cfg<128, 128, 4, 2, 4>(args, stream);
+}
+
+}  // namespace bfp8

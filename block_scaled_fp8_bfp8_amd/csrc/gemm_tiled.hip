@@ -50,20 +50,6 @@ constexpr int largest_divisor_upto(int n, int cap) {
   return 0;
 }
 
-// Tile of workgroup `bid`: each XCD (bid % 8) owns a contiguous run of the tiles,
-// ordered in groups of `group_m` M-tiles with the M-tile index fastest.
-__device__ __forceinline__ void map_tile(int bid, int n_tiles, int m_tiles, int group_m, int& tn, int& tm) {
-  const int total = n_tiles * m_tiles;
-  int t = bid;
-  if (total % 8 == 0) t = (bid % 8) * (total / 8) + bid / 8;
-  const int band = group_m * n_tiles;
-  const int first_m = (t / band) * group_m;
-  const int gm = min(m_tiles - first_m, group_m);
-  const int r = t - (t / band) * band;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
-
 // The same order for a grid padded to a multiple of 8 workgroups (the grouped launches): each XCD
 // gets a run of ceil(total / 8) tiles whatever the tile count; returns false for the padding.
 // Without the padding a tile count that is not a multiple of 8 deals consecutive tiles to
@@ -82,7 +68,7 @@ __device__ __forceinline__ bool map_tile_padded(int bid, int n_tiles, int m_tile
   return true;
 }
 
-template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped, bool kE8, bool kTail, bool kG64 = false>
+template <int BN, int BM, int WGN, int WGM, int STAGES, int KG, bool kGrouped, bool kE8, bool kTail>
 __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArgs args) {
   constexpr int kWaves = WGN * WGM;  // waves per K group
   constexpr int WN = BN / WGN, WM = BM / WGM;
@@ -95,13 +81,6 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   static_assert(WN % 16 == 0 && WM % 16 == 0, "wave tiles are made of 16x16 MFMA tiles");
   static_assert(kBlock % WN == 0 && BN % WN == 0, "a wave's N range must lie inside one weight-scale strip");
   static_assert(!kGrouped || kBlock % BM == 0, "grouped: a workgroup's rows must lie in one 128-row block");
-  // kG64: 1x64 activation groups and 128x64 weight blocks. Each 128-wide K block holds two
-  // scale groups; the lanes with kc < 2 hold its K bytes 0-63, the others 64-127, so a sub-tile
-  // takes two MFMAs, one on each half of the activation fragment (the other half zeroed), each
-  // promoted with its own scale product.
-  static_assert(!kG64 || (!kE8 && !kGrouped && KG == 1 && BN * BM < 256 * 256), "1x64: float scales, dense, mid tile");
-  constexpr int kScaleGroups = kG64 ? 2 : 1;
-  static_assert(BM / 64 * kScaleGroups <= WGN * WGM, "activation scales: one 64-lane copy per 64 rows and group");
 
   static_assert(STAGES >= 2 && STAGES <= 8, "2 to 8 pipeline stages");
   static_assert(KG == 1 || KG == 2, "one or two K groups");
@@ -110,7 +89,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   // through its own LDS ring, and the groups' tiles are summed in group order at the end.
   // Activation scales of a stage: BM floats, or with kE8 BM code bytes (one 64-lane dword copy
   // fills 256 bytes).
-  constexpr int kAsWords = kE8 ? 64 : BM * kScaleGroups;
+  constexpr int kAsWords = kE8 ? 64 : BM;
   constexpr int kScaleBytes = kE8 ? 1 : 4;
   static_assert(!kE8 || BM <= 256, "one copy holds the codes of 256 activation rows");
   using ScaleT = std::conditional_t<kE8, int, float>;
@@ -188,18 +167,10 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   // Activation scales of a K block: waves 0 .. BM/64-1 copy 64 of them each (clamped rows);
   // UE8M0 codes: wave 0 copies 4 codes per lane (dwords clamped to the one holding row M-1,
   // which lies inside the row of codes: its length is a multiple of 4).
-  const bool copies_as = kE8 ? w == 0 : w < BM / 64 * kScaleGroups;
-  // kG64: waves 0 .. BM/64-1 copy the block's first scale group, the next BM/64 its second
-  const int as_half = kG64 && copies_as ? w / (BM / 64) : 0;
+  const bool copies_as = kE8 ? w == 0 : w < BM / 64;
   const uint32_t as_voff = kE8 ? (uint32_t)min(m0 + 4 * lane, (M - 1) & ~3)
-                               : (uint32_t)min(m0 + (copies_as ? w % (BM / 64) : 0) * 64 + lane, M - 1) * 4u;
+                               : (uint32_t)min(m0 + (copies_as ? w : 0) * 64 + lane, M - 1) * 4u;
   const uint32_t as_dst_off = kE8 ? 0u : (uint32_t)(w * 64 * 4);
-  const int G64 = (args.K + 63) / 64;  // kG64: scale groups along K
-  // Scale column of this wave's copy for K block kb (kG64: group 2 kb + half, clamped to the last
-  // group; a clamped group only meets K bytes past K, which the tail mask zeroes).
-  auto as_col = [&](int kb) __attribute__((always_inline)) -> int64_t {
-    return kG64 ? (int64_t)min(2 * kb + as_half, G64 - 1) : (int64_t)kb;
-  };
 
   uint32_t stage_lds[STAGES], as_lds_addr[STAGES];
 #pragma unroll
@@ -217,7 +188,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 #pragma unroll
     for (int j = 0; j < kCopies; ++j)
       copy16_to_lds(prow_base + j * 8 < BN ? bsrc : asrc, coff[j], dst + (uint32_t)(j * 8 * kBlock));
-    if (copies_as) copy4_to_lds(asmat + as_col(kb) * args.ld_as * kScaleBytes, as_voff, as_lds_addr[buf] + as_dst_off);
+    if (copies_as) copy4_to_lds(asmat + (int64_t)kb * args.ld_as * kScaleBytes, as_voff, as_lds_addr[buf] + as_dst_off);
   };
   // One piece of a block's copy (for spreading a block's copies over the multiply steps).
   auto issue_piece = [&](int buf, int kb_local, int j) __attribute__((always_inline)) {
@@ -227,7 +198,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   };
   auto issue_scales = [&](int buf, int kb_local) __attribute__((always_inline)) {
     if (copies_as)
-      copy4_to_lds(asmat + as_col(gkb(kb_local)) * args.ld_as * kScaleBytes, as_voff, as_lds_addr[buf] + as_dst_off);
+      copy4_to_lds(asmat + (int64_t)gkb(kb_local) * args.ld_as * kScaleBytes, as_voff, as_lds_addr[buf] + as_dst_off);
   };
 
   const int r = lane & 15, kc = lane >> 4;
@@ -238,17 +209,6 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
       return e8_code_scalar((const __attribute__((address_space(4))) uint32_t*)bs_row, kb_global);
     } else {
       return ((const __attribute__((address_space(4))) float*)bs_row)[kb_global];
-    }
-  };
-  // The weight scales of K block kb, one per scale group (kG64: groups 2 kb and 2 kb + 1 of the
-  // strip's row; a second group past K gets 0, so its zeroed half adds nothing).
-  auto weight_scales = [&](int kb_global, ScaleT (&out)[kScaleGroups]) __attribute__((always_inline)) {
-    if constexpr (kG64) {
-      const __attribute__((address_space(4))) float* row = (const __attribute__((address_space(4))) float*)bs_row;
-      out[0] = row[2 * kb_global];
-      out[1] = 2 * kb_global + 1 < G64 ? row[2 * kb_global + 1] : 0.f;
-    } else {
-      out[0] = weight_scale(kb_global);
     }
   };
 
@@ -277,20 +237,12 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   auto frag_a = [&](const uint8_t* stage, int tm) __attribute__((always_inline)) {
     return frag_at(stage, BN + wm * WM + tm * 16);
   };
-  auto act_scale = [&](int slot, int tm, int h) __attribute__((always_inline)) -> ScaleT {
+  auto act_scale = [&](int slot, int tm) __attribute__((always_inline)) -> ScaleT {
     if constexpr (kE8) {
       return reinterpret_cast<const uint8_t*>(&as_lds[g][slot][0])[wm * WM + tm * 16 + r];
     } else {
-      return as_lds[g][slot][h * BM + wm * WM + tm * 16 + r];
+      return as_lds[g][slot][wm * WM + tm * 16 + r];
     }
-  };
-  // kG64: the halves of an activation fragment (K bytes 0-63 on lanes kc < 2, 64-127 on the rest)
-  const bool lo_lane = kc < 2;
-  auto half_frag = [&](const v8i& f, bool keep) __attribute__((always_inline)) -> v8i {
-    v8i o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = keep ? f[i] : 0;
-    return o;
   };
 
   // Software pipeline. Sub-tiles are visited activation-row by activation-row: step
@@ -314,8 +266,8 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   //     iteration kb + 1 reads, and ends with the barrier.
   v8i fa[TM];
   v8i fb[TN];
-  ScaleT sa[TM][kScaleGroups];
-  ScaleT bsv[kScaleGroups];
+  ScaleT sa[TM];
+  ScaleT bsv;
   constexpr int kSteps = TN * TM;
   constexpr bool kMid = BN * BM < 256 * 256;
   constexpr int kBarStep = kMid ? TN - 1 : -1;
@@ -345,18 +297,14 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     }
   };
 
-  float sc[TM][kScaleGroups];  // scale products As * Bs of the block's activation rows
+  float sc[TM];  // scale products As * Bs of the block's activation rows
   if constexpr (kMid) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int h = 0; h < kScaleGroups; ++h) sc[tm][h] = 0.f;
+    for (int tm = 0; tm < TM; ++tm) sc[tm] = 0.f;
   }
   // kMid: the last two MFMA results of the previous block (zero before the first block:
   // promoting them then adds 0 * 0 to a zero accumulator).
-  v4f p1c[kScaleGroups], p2c[kScaleGroups];
-#pragma unroll
-  for (int h = 0; h < kScaleGroups; ++h) p1c[h] = p2c[h] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4f p1c = {0.f, 0.f, 0.f, 0.f}, p2c = p1c;
   auto promote = [&](int u, const v4f& pu, float s) __attribute__((always_inline)) {
     const int um = u / TN, un = u % TN;
 #pragma unroll
@@ -364,12 +312,6 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     // Pin the promotion here: otherwise the FMAs are sunk past the loop's branch,
     // since their results are only read in the next K block.
     asm volatile("" : "+v"(acc[un][um][0]), "+v"(acc[un][um][1]), "+v"(acc[un][um][2]), "+v"(acc[un][um][3]));
-  };
-  // A sub-tile's promotions, one per scale group in group order.
-  auto promote_all = [&](int u, const v4f (&pu)[kScaleGroups], const float (&su)[kScaleGroups])
-                         __attribute__((always_inline)) {
-#pragma unroll
-    for (int h = 0; h < kScaleGroups; ++h) promote(u, pu[h], su[h]);
   };
 
   auto iter = [&](int kb, auto steady_c) __attribute__((always_inline)) {
@@ -380,23 +322,19 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
     const int nslot = (kb + 1) % STAGES;
     const uint8_t* nstage = &smem[g][nslot][0];
     const bool mask_next = kTail && kb + 1 < KB && gkb(kb + 1) == KB_all - 1;  // uniform
-    ScaleT bs_next[kScaleGroups];
-    weight_scales(gkb(min(kb + 1, KB - 1)), bs_next);
+    const ScaleT bs_next = weight_scale(gkb(min(kb + 1, KB - 1)));
     // With kMid the scale products live across blocks; otherwise they are this block's alone.
-    float sc_block[TM][kScaleGroups];
-    float (*const scp)[kScaleGroups] = kMid ? sc : sc_block;
+    float sc_block[TM];
+    float* const scp = kMid ? sc : sc_block;
     if constexpr (!kE8 && !kMid) {
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int h = 0; h < kScaleGroups; ++h) scp[tm][h] = sa[tm][h] * bsv[h];
+      for (int tm = 0; tm < TM; ++tm) scp[tm] = sa[tm] * bsv;
     }
     if constexpr (kSteady && !kMid) issue_scales(cslot, kb + STAGES);
-    v4f p1[kScaleGroups], p2[kScaleGroups];  // MFMA results of the previous two steps
-#pragma unroll
-    for (int h = 0; h < kScaleGroups; ++h) {
-      p1[h] = kMid ? p1c[h] : v4f{0.f, 0.f, 0.f, 0.f};
-      p2[h] = kMid ? p2c[h] : v4f{0.f, 0.f, 0.f, 0.f};
+    v4f p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1;  // MFMA results of the previous two steps
+    if constexpr (kMid) {
+      p1 = p1c;
+      p2 = p2c;
     }
     // Step t issues the MFMA of sub-tile t, the promotion FMAs of the sub-tile two steps back
     // (its result is then at least one MFMA old), its share of the copies and of the next
@@ -404,11 +342,11 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
       const int tm = t / TN, tn = t % TN;
-      v4f p[kScaleGroups];
+      v4f p;
       if constexpr (kE8) {
         // The scaled product is added to the tile by the MFMA itself.
         const v4f cur = {acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
-        const v4f nxt = mfma_block_e8(fb[tn], fa[tm], cur, bsv[0], sa[tm][0]);
+        const v4f nxt = mfma_block_e8(fb[tn], fa[tm], cur, bsv, sa[tm]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[tn][tm][e] = nxt[e];
       } else {
@@ -416,20 +354,12 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
         // holds this block's activation scale (the row's last step reloads it). Until then
         // sc[TM - 1] keeps the previous block's, which its two lagging promotions use (the
         // last two steps of a block lie in its last row, since TN >= 2).
-        if (kMid && tn == 0) {
-#pragma unroll
-          for (int h = 0; h < kScaleGroups; ++h) scp[tm][h] = sa[tm][h] * bsv[h];
-        }
-        if constexpr (kG64) {
-          p[0] = mfma_block(fb[tn], half_frag(fa[tm], lo_lane));
-          p[1] = mfma_block(fb[tn], half_frag(fa[tm], !lo_lane));
-        } else {
-          p[0] = mfma_block(fb[tn], fa[tm]);
-        }
+        if (kMid && tn == 0) scp[tm] = sa[tm] * bsv;
+        p = mfma_block(fb[tn], fa[tm]);
         if (t >= 2) {
-          promote_all(t - 2, p2, scp[(t - 2) / TN]);
+          promote(t - 2, p2, scp[(t - 2) / TN]);
         } else if constexpr (kMid) {
-          promote_all(kSteps - 2 + t, p2, scp[TM - 1]);
+          promote(kSteps - 2 + t, p2, scp[TM - 1]);
         }
       }
       if (kMid && t == kBarStep) {
@@ -445,8 +375,7 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
       if (tn == TN - 1) {
         fa[tm] = frag_a(nstage, tm);
         if (mask_next) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
-#pragma unroll
-        for (int h = 0; h < kScaleGroups; ++h) sa[tm][h] = act_scale(nslot, tm, h);
+        sa[tm] = act_scale(nslot, tm);
       }
       if (tm == TM - 1) {
         fb[tn] = frag_b(nstage, tn);
@@ -454,26 +383,19 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!kE8) {
-#pragma unroll
-        for (int h = 0; h < kScaleGroups; ++h) {
-          p2[h] = p1[h];
-          p1[h] = p[h];
-        }
+        p2 = p1;
+        p1 = p;
       }
     }
     if constexpr (!kE8 && !kMid) {
-      promote_all(kSteps - 2, p2, scp[TM - 1]);
-      promote_all(kSteps - 1, p1, scp[TM - 1]);
+      promote(kSteps - 2, p2, scp[TM - 1]);
+      promote(kSteps - 1, p1, scp[TM - 1]);
     }
     if constexpr (kMid) {
-#pragma unroll
-      for (int h = 0; h < kScaleGroups; ++h) {
-        p1c[h] = p1[h];
-        p2c[h] = p2[h];
-      }
+      p1c = p1;
+      p2c = p2;
     }
-#pragma unroll
-    for (int h = 0; h < kScaleGroups; ++h) bsv[h] = bs_next[h];
+    bsv = bs_next;
     if constexpr (!kMid) {
       wait_next_block(kSteady);
       lds_barrier();
@@ -499,15 +421,14 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   for (int tm = 0; tm < TM; ++tm) {
     fa[tm] = frag_a(&smem[g][0][0], tm);
     if (mask_first) fa[tm] = mask_k_tail(fa[tm], k_tail, kc);
-#pragma unroll
-    for (int h = 0; h < kScaleGroups; ++h) sa[tm][h] = act_scale(0, tm, h);
+    sa[tm] = act_scale(0, tm);
   }
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
     fb[tn] = frag_b(&smem[g][0][0], tn);
     if (mask_first) fb[tn] = mask_k_tail(fb[tn], k_tail, kc);
   }
-  weight_scales(g, bsv);
+  bsv = weight_scale(g);
   // every wave has read stage 0 before iteration 0 refills it (with kMid, the refill follows
   // the barrier of iteration 0 instead)
   if constexpr (!kMid) lds_barrier();
@@ -516,8 +437,8 @@ __global__ __launch_bounds__(KG * WGN * WGM * 64) void gemm_tiled_kernel(GemmArg
   for (; kb < KB; ++kb) iter(kb, std::false_type{});
   if constexpr (kMid) {
     if constexpr (!kE8 && kMid) {
-      promote_all(kSteps - 2, p2c, sc[TM - 1]);
-      promote_all(kSteps - 1, p1c, sc[TM - 1]);
+      promote(kSteps - 2, p2c, sc[TM - 1]);
+      promote(kSteps - 1, p1c, sc[TM - 1]);
     }
     // Every wave's LDS reads (the last iteration's stale ones included) are done before the
     // stages are reused below (the end-of-block barrier already covers them).
@@ -796,20 +717,6 @@ hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t 
 }
 
 // Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
-// 1x64 activation groups and 128x64 weight blocks on the 256 x 128 tile (two MFMAs and two
-// promotions per sub-tile and K block).
-hipError_t launch_gemm_tiled_1x64(const GemmArgs& args, hipStream_t stream) {
-  const dim3 grid((unsigned)(((args.N + 255) / 256) * ((args.M + 127) / 128)));
-  if (args.K % kBlock) {
-    hipLaunchKernelGGL((gemm_tiled_kernel<256, 128, 4, 2, 3, 1, false, false, true, true>), grid, dim3(512), 0, stream,
-                       args);
-  } else {
-    hipLaunchKernelGGL((gemm_tiled_kernel<256, 128, 4, 2, 3, 1, false, false, false, true>), grid, dim3(512), 0, stream,
-                       args);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream) {
   if (args.K % kBlock) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true, true>(args, stream);
   return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true, false>(args, stream);

@@ -95,10 +95,14 @@ hipError_t launch_gemm_ksplit(const GemmArgs& args, hipStream_t stream);
 // 1x64 activation groups / 128x64 weight blocks (float scales): args.as is [ceil(K/64)][ld_as],
 // args.bs [ceil(N/128)][ld_bs >= ceil(K/64)]; the K-split kernel at every M.
 hipError_t launch_gemm_ksplit_1x64(const GemmArgs& args, hipStream_t stream);
-// The same on the tiled schedule (256 x 128 tiles).
-hipError_t launch_gemm_tiled_1x64(const GemmArgs& args, hipStream_t stream);
-// 1x64 GEMMs with at least this many 256 x 128 output tiles take the tiled schedule.
-constexpr int64_t kTiled1x64MinTiles = 256;
+// The same on 256 x 128 tiles with the 32x32x64 matrix-core product, one product per 64-wide
+// group (bf16 output, no bias).
+hipError_t launch_gemm_g64(const GemmArgs& args, hipStream_t stream);
+// Weight rows per tile of that launch (256 or 128).
+int g64_tile_n(int64_t M, int64_t N);
+// 1x64 GEMMs with at least this many 256 x 128 output tiles take the tiled schedule (N = K = 4096:
+// M >= 385; measured at M = 384 K-split 26.1 us, tiled 27.2; M = 512 28.9 and 27.7 us).
+constexpr int64_t kTiled1x64MinTiles = 64;
 // The linear layer at small M: the K-split kernel's 16 x 16 tile quantizing the bf16/fp16
 // activations (args.a, args.lda in elements; args.as unused) itself, bit-identical to
 // launch_quant_act followed by launch_gemm_ksplit. Taken for the shapes ksplit_fused_shape

@@ -310,8 +310,10 @@ bfp8_status_t bfp8_gemm_f16(const uint8_t* a, int64_t lda, const float* as, int6
  * bfp8_gemm_1x64: C[m, n] = bf16(sum_g P_g * As[g][m] * Bs[n / 128][g]), P_g the e4m3 dot
  * product over the 64 columns of group g. as is [ceil(K/64)][ld_as] (ld_as >= M), bs is
  * [ceil(N/128)][ld_bs] with ld_bs >= ceil(K/64); a, b, c and every other rule as bfp8_gemm
- * (operand rows of whole 128-byte blocks). Runs the K-split kernel at every M, with two matrix-
- * core products and two promotions per 128-wide K block (no workspace). The float32
+ * (operand rows of whole 128-byte blocks). No workspace. Small M runs the K-split kernel (two
+ * 16x16x128 matrix-core products per 128-wide K block, each on one group with the other half
+ * zeroed); from 64 output tiles of 256 x 128 on, a tiled kernel with one 32x32x64 product per
+ * 64-wide group (bfp8_set_schedule forces either). Both round each group's sum once; the float32
  * accumulation error is bounded as for bfp8_gemm with K/64 promotions instead of K/128.
  */
 bfp8_status_t bfp8_quant_act_1x64(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,

@@ -100,12 +100,13 @@ def test_gemm_1x64_deterministic_and_equal_half_scales(gpu):
     tolerance.compare(bits(c128)[rows], ref_bits, mass, k, "gemm 1x128 (same inputs)")
 
 
-# The tiled schedule (256 x 128 tiles, two MFMAs and promotions per sub-tile and K block), forced
-# on shapes the automatic choice gives the K-split kernel and taken by default at large M: ragged
-# M and N, one and several tiles per XCD, K tails where the last 128-wide block has a partial or
-# absent second group, and a K of one block.
+# The tiled schedule (one 32x32x64 matrix-core product and one promotion per sub-tile and 64-wide
+# group; 128 x 128 tiles, or 256 x 128 where those fill every CU), forced on shapes the automatic
+# choice gives the K-split kernel and taken by default from mid M: ragged M and N, one and several
+# tiles per XCD, K tails where the last 128-wide block has a partial or absent second group (on
+# both tile shapes), and a K of one block.
 @pytest.mark.parametrize("m,n,k", [(128, 256, 1024), (300, 520, 1040), (1000, 4096, 4160), (700, 1000, 4176),
-                                   (2048, 4096, 4096), (513, 384, 128), (96, 300, 208)])
+                                   (2048, 4096, 4096), (2100, 4096, 1040), (513, 384, 128), (96, 300, 208)])
 def test_gemm_1x64_tiled_against_oracle(gpu, m, n, k):
     x = workloads.act_uniform(m, k, seed=940 + m)
     q, s, q_ref, s_ref = _quant_checked(x, gpu, f"tiled {m}x{n}x{k}")
