@@ -8,12 +8,12 @@
 //     group's sum is one product's result with nothing masked (the 16x16x128 product spans two
 //     groups: it takes one product per group with the other half of the operand zeroed, half of
 //     the matrix-core work wasted);
-//   * tiles, copies and pipeline follow the 1x128 tiled kernel: a 256 x 128 tile of C^T
-//     (weight rows on the product's first operand, activation rows on its second) with 8 waves
-//     of 64 x 64, three LDS stages of (256 + 128) rows of 128 bytes filled by the direct-to-LDS
-//     copies with the conflict-free XOR swizzle, plus the block's two groups of activation
-//     scales; the workgroup barrier of iteration kb sits just before the first LDS read of
-//     block kb + 1 and the stage of block kb is refilled with block kb + 3 right after it;
+//   * tiles, copies and pipeline follow the 1x128 tiled kernel: a tile of C^T (weight rows on
+//     the product's first operand, activation rows on its second) computed by 8 waves, LDS
+//     stages of (BN + BM) rows of 128 bytes filled by the direct-to-LDS copies with the
+//     conflict-free XOR swizzle, plus the block's two groups of activation scales; 128 x 128 and
+//     256 x 128 tiles hold a block's fragments of both groups, 256 x 256 tiles (whose
+//     accumulators take half the registers) one group's at a time;
 //   * promotion: acc += P_g * (As[g][m] * Bs[n/128][g]); lane l holds activation row l % 32 of a
 //     sub-tile and 16 of its weight rows, all inside one 128-row scale strip, so a sub-tile and
 //     group take one scale product and 16 FMAs, lagging their product by two steps.
@@ -364,6 +364,262 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_g64_kernel(GemmArgs args)
   }
 }
 
+
+// The 256 x 256 tile for large M: 8 waves of 128 x 64 (4 x 2 sub-tiles), two LDS stages. Its
+// accumulators (128 registers per lane) leave no room for all fragments of a block, so the steps
+// run group by group and weight fragment by weight fragment: step t = (h TN + tn) TM + tm
+// multiplies group h of weight fragment tn by group h of activation fragment tm. The wave holds
+// the TM activation fragments of the current group and two weight fragments (the current one and
+// the next, read at the first step of the current one). Each activation fragment is refilled
+// after its last use in a group with the next group: group 1 of the same block (same stage) or
+// group 0 of the next block. The barrier of iteration kb sits at the first read of block kb + 1;
+// past it every wave has read block kb's group 1 as well, so its stage takes block kb + 2. One
+// iteration covers the copies' latency, as in the 1x128 kernel's 256 x 256 tile.
+template <bool kTail>
+__global__ __launch_bounds__(512) void gemm_g64_wide_kernel(GemmArgs args) {
+  constexpr int BN = 256, BM = 256, WGN = 2, WGM = 4, STAGES = 2;
+  constexpr int kWaves = WGN * WGM;
+  constexpr int WN = BN / WGN, WM = BM / WGM;  // 128 x 64 per wave
+  constexpr int TN = WN / 32, TM = WM / 32;    // 4 x 2 sub-tiles of 32 x 32
+  constexpr int kRows = BN + BM;
+  constexpr int kStage = kRows * kBlock;
+  constexpr int kCopies = kRows / 8 / kWaves;  // 8
+  constexpr int kSteps = 2 * TN * TM;          // (group half, tn, tm) per K block
+  constexpr int kBarStep = (2 * TN - 1) * TM;  // group 1, last weight fragment, first row: the first read of the next block
+  static_assert(kRows % (8 * kWaves) == 0 && BN % 8 == 0 && kBlock % WN == 0 && TM >= 2 && TN % 2 == 0, "tile");
+  static_assert(2 * BM / 64 == kWaves, "activation scales: every wave copies 64 of them");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES][kStage];
+  __shared__ __attribute__((aligned(16))) float as_lds[STAGES][2 * BM];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = w % WGN, wm = w / WGN;
+  const int M = args.M, N = args.N;
+  const int n_tiles = (N + BN - 1) / BN, m_tiles = (M + BM - 1) / BM;
+  const int KB = (args.K + kBlock - 1) / kBlock;
+  const int G = (args.K + 63) / 64;
+  const int k_tail = kTail ? args.K - (KB - 1) * kBlock : kBlock;
+  int tile_n, tile_m;
+  map_tile(blockIdx.x, n_tiles, m_tiles, 8, tile_n, tile_m);
+  const int n0 = tile_n * BN, m0 = tile_m * BM;
+
+  // Copy plan and scale copies as in the 256 x 128 kernel; here all 8 waves copy scales (wave w:
+  // group half w / 4, rows (w % 4) 64 + lane).
+  const int prow_base = w * 8 * kCopies;
+  const int lrow = lane >> 3;
+  uint32_t coff[kCopies];
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    const int prow = prow_base + j * 8;  // uniform
+    const int lcol = (lane & 7) ^ lds_swizzle(prow + lrow);
+    const int row = prow < BN ? min(n0 + prow + lrow, N - 1) : min(m0 + prow - BN + lrow, M - 1);
+    const int64_t ld = prow < BN ? args.ldb : args.lda;
+    coff[j] = (uint32_t)((int64_t)row * ld + lcol * 16);
+  }
+  const int as_h = w / (BM / 64);
+  const uint32_t as_voff = (uint32_t)min(m0 + (w % (BM / 64)) * 64 + lane, M - 1) * 4u;
+  const uint32_t as_dst_off = (uint32_t)(w * 64 * 4);
+  const uint8_t* asmat = static_cast<const uint8_t*>(args.as);
+  auto issue_piece = [&](int buf, int kb, int j) __attribute__((always_inline)) {
+    const uint8_t* src = prow_base + j * 8 < BN ? args.b + (int64_t)kb * kBlock : args.a + (int64_t)kb * kBlock;
+    copy16_to_lds(src, coff[j], lds_addr(&smem[buf][0]) + (uint32_t)((prow_base + j * 8) * kBlock));
+  };
+  auto issue_scales = [&](int buf, int kb) __attribute__((always_inline)) {
+    copy4_to_lds(asmat + (int64_t)min(2 * kb + as_h, G - 1) * args.ld_as * 4, as_voff,
+                 lds_addr(&as_lds[buf][0]) + as_dst_off);
+  };
+  const __attribute__((address_space(4))) float* bs_row =
+      (const __attribute__((address_space(4))) float*)(static_cast<const uint8_t*>(args.bs) +
+                                                       (int64_t)(min(n0 + wn * WN, N - 1) / kBlock) * args.ld_bs * 4);
+  auto weight_scales = [&](int kb, float (&out)[2]) __attribute__((always_inline)) {
+    out[0] = bs_row[2 * kb];
+    out[1] = 2 * kb + 1 < G ? bs_row[2 * kb + 1] : 0.f;
+  };
+
+  // Group fragments (see the 256 x 128 kernel); the four per-lane offsets differ only in the
+  // group and chunk bits of the 16-byte column, which the XOR swizzle leaves in place.
+  const int r = lane & 31, kc = lane >> 5;
+  const uint32_t foff0 = (uint32_t)(r * kBlock + (((2 * kc) ^ lds_swizzle(r)) << 4));
+  auto frag_at = [&](int slot, int row0, int h) __attribute__((always_inline)) -> v8i {
+    const uint8_t* stage = &smem[slot][0] + row0 * kBlock;
+    const v4i lo = *reinterpret_cast<const v4i*>(stage + (foff0 ^ (uint32_t)(h << 6)));
+    const v4i hi = *reinterpret_cast<const v4i*>(stage + (foff0 ^ (uint32_t)((h << 6) | 16)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  float acc[TN][TM][16];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tn][tm][e] = 0.f;
+
+  v8i fa[TM], fb[2];
+  float sa[TM][2], bsv[2], sc[TM][2];
+  auto promote = [&](int u, const v16f& pu) __attribute__((always_inline)) {
+    const int uh = u / (TN * TM), un = (u / TM) % TN, um = u % TM;
+    const float s = sc[um][uh];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[un][um][e] = fmaf(pu[e], s, acc[un][um][e]);
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      asm volatile("" : "+v"(acc[un][um][e]), "+v"(acc[un][um][e + 1]), "+v"(acc[un][um][e + 2]),
+                   "+v"(acc[un][um][e + 3]));
+  };
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) sc[tm][0] = sc[tm][1] = 0.f;
+  v16f p1c = {}, p2c = {};
+
+  auto iter = [&](int kb, auto steady_c) __attribute__((always_inline)) {
+    constexpr bool kSteady = decltype(steady_c)::value;  // kb + 2 < KB: refill the stage
+    const int cslot = kb % STAGES, nslot = (kb + 1) % STAGES;
+    const bool mask_cur = kTail && kb == KB - 1;       // uniform
+    const bool mask_next = kTail && kb + 1 == KB - 1;  // uniform
+    float bs_next[2];
+    weight_scales(min(kb + 1, KB - 1), bs_next);
+    v16f p1 = p1c, p2 = p2c;
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      const int h = t / (TN * TM), tn = (t / TM) % TN, tm = t % TM;
+      // The scale products of (tm, h) are formed at their first step, while sa[tm] still holds
+      // this block's activation scales (the last step of tm in group 1 reloads them); the
+      // previous block's sc[.][1] serve its two lagging promotions first.
+      if (tn == 0) sc[tm][h] = sa[tm][h] * bsv[h];
+      const v16f p = mfma_group(fb[tn % 2], fa[tm]);
+      promote(t >= 2 ? t - 2 : kSteps - 2 + t, p2);
+      if (t == kBarStep) {
+        wait_copies();  // block kb + 1 has landed (the only copies in flight)
+        lds_barrier();
+        if constexpr (kSteady) {
+          issue_scales(cslot, kb + STAGES);
+#pragma unroll
+          for (int j = 0; j < kCopies; ++j) issue_piece(cslot, kb + STAGES, j);
+        }
+      }
+      // The next weight fragment, at the first step of the current one: (h, tn + 1), or group 1
+      // of this block's first one, or group 0 of the next block's.
+      if (tm == 0) {
+        const int nh = tn + 1 < TN ? h : 1 - h;
+        const int slot = tn + 1 < TN || h == 0 ? cslot : nslot;
+        const bool msk = slot == cslot ? mask_cur : mask_next;
+        fb[(tn + 1) % 2] = frag_at(slot, wn * WN + ((tn + 1) % TN) * 32, nh);
+        if (msk) fb[(tn + 1) % 2] = mask_group_tail(fb[(tn + 1) % 2], k_tail, nh, kc);
+      }
+      // Activation fragment tm after its last use in the group, with the next group; at the end
+      // of group 1 also block kb + 1's activation scales.
+      if (tn == TN - 1) {
+        const int slot = h == 0 ? cslot : nslot;
+        fa[tm] = frag_at(slot, BN + wm * WM + tm * 32, 1 - h);
+        if (h == 0 ? mask_cur : mask_next) fa[tm] = mask_group_tail(fa[tm], k_tail, 1 - h, kc);
+        if (h == 1) {
+          sa[tm][0] = as_lds[nslot][wm * WM + tm * 32 + r];
+          sa[tm][1] = as_lds[nslot][BM + wm * WM + tm * 32 + r];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      p2 = p1;
+      p1 = p;
+    }
+    p1c = p1;
+    p2c = p2;
+    bsv[0] = bs_next[0];
+    bsv[1] = bs_next[1];
+  };
+
+#pragma unroll
+  for (int i = 0; i < STAGES; ++i) {
+    const int kb = min(i, KB - 1);
+    issue_scales(i, kb);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) issue_piece(i, kb, j);
+  }
+  wait_copies_upto<kCopies + 1>();  // block 0 has landed
+  lds_barrier();
+  const bool mask_first = kTail && KB == 1;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    fa[tm] = frag_at(0, BN + wm * WM + tm * 32, 0);
+    if (mask_first) fa[tm] = mask_group_tail(fa[tm], k_tail, 0, kc);
+    sa[tm][0] = as_lds[0][wm * WM + tm * 32 + r];
+    sa[tm][1] = as_lds[0][BM + wm * WM + tm * 32 + r];
+  }
+  fb[0] = frag_at(0, wn * WN, 0);
+  if (mask_first) fb[0] = mask_group_tail(fb[0], k_tail, 0, kc);
+  weight_scales(0, bsv);
+  int kb = 0;
+  for (; kb + STAGES < KB; ++kb) iter(kb, std::true_type{});
+  for (; kb < KB; ++kb) iter(kb, std::false_type{});
+  promote(kSteps - 2, p2c);
+  promote(kSteps - 1, p1c);
+  lds_barrier();
+
+  // Output: each wave stages its 128 x 64 tile in LDS, 32 activation rows (one sub-tile row) at
+  // a time as rows of 256 bytes + 16 of padding, and stores whole row segments.
+  const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
+  if (vec16) {
+    constexpr int kRowBytes = WN * 2 + 16;
+    static_assert(kWaves * 32 * kRowBytes <= STAGES * kStage, "output staging fits the stages");
+    uint8_t* out_lds = &smem[0][0] + w * (32 * kRowBytes);
+    constexpr int kLanesPerRow = WN / 8;
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = f32_to_bf16_rne(acc[tn][tm][4 * q]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 1]) << 16);
+          pk.y = f32_to_bf16_rne(acc[tn][tm][4 * q + 2]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(out_lds + r * kRowBytes + (tn * 32 + 8 * q + 4 * kc) * 2) = pk;
+        }
+      // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
+      // wave's accesses in order, and this keeps the compiler from reordering them.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+        const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+        const int seg = lane % kLanesPerRow;
+        const v4i v = *reinterpret_cast<const v4i*>(out_lds + row * kRowBytes + seg * 16);
+        const int m = m0 + wm * WM + tm * 32 + row;
+        const int n = n0 + wn * WN + seg * 8;
+        if (m < M && n < N) {
+          uint16_t* cp = args.c + (int64_t)m * args.ldc + n;
+          if (n + 8 <= N) {
+            *reinterpret_cast<v4i*>(cp) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) cp[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+    return;
+  }
+  const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = m0 + wm * WM + tm * 32 + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WN + tn * 32 + 8 * q + 4 * kc;
+        if (n < N)
+          store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1],
+                        acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3], nullptr, false);
+      }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -382,24 +638,42 @@ hipError_t launch_g64_cfg(const GemmArgs& args, hipStream_t stream) {
 
 }  // namespace
 
-// The tile shape whose rounds of 256 workgroups (one per CU) take less time at the per-K-block
-// round times measured at N = K = 4096: 1.25 us for 256 x 128 tiles, 0.86 us for 128 x 128 (K
-// scales both alike). E.g. M = 1024: one round of 128 x 128 tiles (32.9 us) instead of one of
-// 256 x 128 (44.7 us); M = 1536: one round of 256 x 128 (45.1 us) instead of two of 128 x 128
-// (56.7 us).
-int g64_tile_n(int64_t M, int64_t N) {
-  const int64_t m_tiles = (M + 127) / 128;
-  const int64_t rounds256 = ((N + 255) / 256 * m_tiles + 255) / 256;
-  const int64_t rounds128 = ((N + 127) / 128 * m_tiles + 255) / 256;
-  return 1.25 * (double)rounds256 <= 0.86 * (double)rounds128 ? 256 : 128;
+// The tile shape whose rounds of 256 workgroups (one per CU) take the least time at the time per
+// K block of a full round measured at N = K = 4096 (K scales every shape alike): 2.75 us for
+// 256 x 256 tiles, 1.55 us for 256 x 128, 1.0 us for 128 x 128; the larger tile on a tie. E.g.
+// M = 1024: one round of 128 x 128 tiles (32.9 us) rather than one of 256 x 128 (44.7 us);
+// M = 1536: one round of 256 x 128 (45.1 us) rather than two of 128 x 128 (56.7 us); M = 6144:
+// three rounds of 256 x 128 (138.6 us) rather than one and a half of 256 x 256 (153.7 us);
+// M = 8192: two rounds of 256 x 256 (171.6 us) rather than four of 256 x 128 (198.9 us).
+G64Tile g64_tile(int64_t M, int64_t N) {
+  auto rounds = [&](int64_t bn, int64_t bm) { return (((N + bn - 1) / bn) * ((M + bm - 1) / bm) + 255) / 256; };
+  const double t256x256 = 2.75 * (double)rounds(256, 256);
+  const double t256x128 = 1.55 * (double)rounds(256, 128);
+  const double t128x128 = 1.0 * (double)rounds(128, 128);
+  if (t256x256 <= t256x128 && t256x256 <= t128x128) return G64Tile::k256x256;
+  return t256x128 <= t128x128 ? G64Tile::k256x128 : G64Tile::k128x128;
 }
 
-// bf16 output without bias (the 1x64 entry point has neither): 256 x 128 tiles (8 waves of
-// 64 x 64, three stages) or 128 x 128 (8 waves of 32 x 64, four stages), as g64_tile_n picks.
+// bf16 output without bias (the 1x64 entry point has neither): 256 x 256 tiles (8 waves of
+// 128 x 64, two stages, one group's fragments at a time), 256 x 128 (8 waves of 64 x 64, three
+// stages) or 128 x 128 (8 waves of 32 x 64, four stages), as g64_tile picks.
 hipError_t launch_gemm_g64(const GemmArgs& args, hipStream_t stream) {
   if (args.bias != nullptr || args.out_f16 || args.e8) return hipErrorInvalidValue;
-  if (g64_tile_n(args.M, args.N) == 256) return launch_g64_cfg<256, 128, 4, 2, 3>(args, stream);
-  return launch_g64_cfg<128, 128, 4, 2, 4>(args, stream);
+  switch (g64_tile(args.M, args.N)) {
+    case G64Tile::k256x256: {
+      const dim3 grid((unsigned)(((args.N + 255) / 256) * ((args.M + 255) / 256)));
+      if (args.K % kBlock) {
+        hipLaunchKernelGGL(gemm_g64_wide_kernel<true>, grid, dim3(512), 0, stream, args);
+      } else {
+        hipLaunchKernelGGL(gemm_g64_wide_kernel<false>, grid, dim3(512), 0, stream, args);
+      }
+      return hipGetLastError();
+    }
+    case G64Tile::k256x128:
+      return launch_g64_cfg<256, 128, 4, 2, 3>(args, stream);
+    default:
+      return launch_g64_cfg<128, 128, 4, 2, 4>(args, stream);
+  }
 }
 
 }  // namespace bfp8

@@ -98,8 +98,9 @@ hipError_t launch_gemm_ksplit_1x64(const GemmArgs& args, hipStream_t stream);
 // The same on 256 x 128 tiles with the 32x32x64 matrix-core product, one product per 64-wide
 // group (bf16 output, no bias).
 hipError_t launch_gemm_g64(const GemmArgs& args, hipStream_t stream);
-// Weight rows per tile of that launch (256 or 128).
-int g64_tile_n(int64_t M, int64_t N);
+// The tile shape of that launch.
+enum class G64Tile { k128x128, k256x128, k256x256 };
+G64Tile g64_tile(int64_t M, int64_t N);
 // 1x64 GEMMs with at least this many 256 x 128 output tiles take the tiled schedule (N = K = 4096:
 // M >= 385; measured at M = 384 K-split 26.1 us, tiled 27.2; M = 512 28.9 and 27.7 us).
 constexpr int64_t kTiled1x64MinTiles = 64;

@@ -101,12 +101,13 @@ def test_gemm_1x64_deterministic_and_equal_half_scales(gpu):
 
 
 # The tiled schedule (one 32x32x64 matrix-core product and one promotion per sub-tile and 64-wide
-# group; 128 x 128 tiles, or 256 x 128 where those fill every CU), forced on shapes the automatic
-# choice gives the K-split kernel and taken by default from mid M: ragged M and N, one and several
-# tiles per XCD, K tails where the last 128-wide block has a partial or absent second group (on
-# both tile shapes), and a K of one block.
+# group; 128 x 128, 256 x 128 or 256 x 256 tiles), forced on shapes the automatic choice gives the
+# K-split kernel and taken by default from mid M: ragged M and N, one and several tiles per XCD,
+# K tails where the last 128-wide block has a partial or absent second group (on every tile
+# shape), a K of one block, and output rows that allow only 8-byte stores.
 @pytest.mark.parametrize("m,n,k", [(128, 256, 1024), (300, 520, 1040), (1000, 4096, 4160), (700, 1000, 4176),
-                                   (2048, 4096, 4096), (2100, 4096, 1040), (513, 384, 128), (96, 300, 208)])
+                                   (2048, 4096, 4096), (2100, 4096, 1040), (513, 384, 128), (96, 300, 208),
+                                   (4100, 4096, 1040), (4096, 4004, 208), (4096, 4096, 128)])
 def test_gemm_1x64_tiled_against_oracle(gpu, m, n, k):
     x = workloads.act_uniform(m, k, seed=940 + m)
     q, s, q_ref, s_ref = _quant_checked(x, gpu, f"tiled {m}x{n}x{k}")
