@@ -129,7 +129,9 @@ def measure_ceilings(torch, np, dev, stream, graph_time_us) -> dict:
     """Ceilings measured on this device in this run (libbfp8_probes.so):
       * fp8_mfma_loop_tflops: 256 workgroups of 8 waves (the GEMMs' occupancy, 2 waves per SIMD)
         issuing independent 16x16x128 FP8 MFMAs from registers; fp8_mfma_promote_tflops: the same
-        with the four promotion FMAs per MFMA of the float-scale method;
+        with the four promotion FMAs per MFMA of the float-scale method; fp8_mfma32_loop_tflops and
+        fp8_mfma32_promote_tflops: the 32x32x64 MFMA (one 1x64 group) accumulating, or promoted
+        with sixteen FMAs per MFMA as the 1x64 method does;
       * hbm_read_1gib_gbs: one launch streaming 1 GiB (4x the last-level cache);
       * hbm_read_16mib_cold_us: one launch streaming 16 MiB (the N = K = 4096 weight) that is not in
         the last-level cache (40 buffers read in turn), the floor of a small-M GEMM launch;
@@ -154,6 +156,18 @@ def measure_ceilings(torch, np, dev, stream, graph_time_us) -> dict:
             times.append(e0.elapsed_time(e1) * 1e3)
         us = float(np.median(times[1:]))
         res[key] = round(pr.bfp8_probe_mfma_loop_flops(wgs, iters) / (us * 1e-6) / 1e12, 1)
+    for mode, key in ((0, "fp8_mfma32_loop_tflops"), (1, "fp8_mfma32_promote_tflops")):
+        times = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if pr.bfp8_probe_mfma32_loop(out.data_ptr(), wgs, iters // 2, mode, stream.cuda_stream):
+                raise RuntimeError("mfma32 probe launch failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(times[1:]))
+        res[key] = round(pr.bfp8_probe_mfma32_loop_flops(wgs, iters // 2) / (us * 1e-6) / 1e12, 1)
     sink = torch.empty(2048 * 512, dtype=torch.int32, device=dev)
     big = torch.zeros(2**30 // 4, dtype=torch.int32, device=dev)
 
@@ -542,6 +556,12 @@ def main() -> int:
                 e_["frac_measured"] = round(ceilings["hbm_read_16mib_cold_us"] / e_["gemm_us"], 4)
             else:
                 e_["frac_measured"] = round(e_["tflops"] / ceilings["fp8_mfma_loop_tflops"], 4)
+        if "gemm_1x64" in configs:
+            # against the 32x32x64 products alone, and with the 16 promotion FMAs each takes
+            for e_ in configs["gemm_1x64"]["per_m"].values():
+                if e_["bound"] == "mfma":
+                    e_["frac_measured"] = round(e_["tflops"] / ceilings["fp8_mfma32_loop_tflops"], 4)
+                    e_["frac_promote_ceiling"] = round(e_["tflops"] / ceilings["fp8_mfma32_promote_tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline and not args.only_m and not args.only_config and not args.ceilings_only:

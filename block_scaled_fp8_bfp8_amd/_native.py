@@ -100,6 +100,8 @@ PROBES_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libb
 PROBE_SIGNATURES = [
     ("bfp8_probe_mfma_loop", ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     ("bfp8_probe_mfma_loop_flops", ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
+    ("bfp8_probe_mfma32_loop", ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    ("bfp8_probe_mfma32_loop_flops", ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
     ("bfp8_probe_stream_read", ctypes.c_int, [_vp, _sz, _vp, ctypes.c_int, _vp]),
     ("bfp8_probe_copy_lds", ctypes.c_int,
      [_vp, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_int, _vp]),

@@ -5,6 +5,8 @@
 //     on operands held in registers (no memory traffic), either accumulating in the MFMA or,
 //     as the float-scale GEMM does, each from a zero accumulator with its product scaled into
 //     a float32 sum by four FMAs (the per-128-block promotion of the blockwise method).
+//   * the same with the 32x32x64 FP8 MFMA, whose K of 64 is one 1x64 group: accumulating in the
+//     MFMA, or each product from a zero accumulator promoted with sixteen FMAs (one per result).
 //   * Streaming read: a grid of 256-thread workgroups reads a buffer once with 16-byte loads,
 //     eight in flight per thread (HBM bandwidth for a buffer larger than the last-level cache).
 #include <hip/hip_runtime.h>
@@ -152,6 +154,47 @@ __global__ __launch_bounds__(512) void copy_lds_kernel(const uint8_t* __restrict
   out[blockIdx.x * 512 + threadIdx.x] = x;
 }
 
+// 32x32x64 products, kChains32 independent ones per wave per step. kPromote false: each adds
+// into its chain's accumulator; true: each starts from zero and its 16 results are scaled into a
+// float32 sum by 16 FMAs (the promotion of the 1x64 method).
+constexpr int kChains32 = 4;
+typedef float v16f __attribute__((ext_vector_type(16)));
+template <bool kPromote>
+__global__ __launch_bounds__(512) void mfma32_loop_kernel(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  v8i a, b[kChains32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0x38383838 ^ ((lane + i) & 1);
+#pragma unroll
+    for (int j = 0; j < kChains32; ++j) b[j][i] = 0x30303030 ^ (j << 8) ^ ((lane + 2 * i) & 1);
+  }
+  v16f acc[kChains32];
+#pragma unroll
+  for (int j = 0; j < kChains32; ++j) acc[j] = v16f{};
+  float s = 1.0f + lane * 1e-7f;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(a));
+#pragma unroll
+    for (int j = 0; j < kChains32; ++j) {
+      if constexpr (kPromote) {
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], v16f{}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] = fmaf(p[e], s, acc[j][e]);
+      } else {
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], acc[j], 0, 0, 0, 0, 0, 0);
+      }
+    }
+    s = s * 0.999999f;
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int j = 0; j < kChains32; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r += acc[j][e];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,6 +214,20 @@ int bfp8_probe_mfma_loop(float* out, int workgroups, int iters, int mode, void* 
 double bfp8_probe_mfma_loop_flops(int workgroups, int iters) {
   // 8 waves per workgroup, kChains MFMAs per step, 2 * 16 * 16 * 128 flops each
   return (double)workgroups * 8.0 * (double)iters * kChains * 2.0 * 16 * 16 * 128;
+}
+
+int bfp8_probe_mfma32_loop(float* out, int workgroups, int iters, int mode, void* stream) {
+  if (!out || workgroups < 1 || iters < 1 || mode < 0 || mode > 1) return 1;
+  if (mode == 0) {
+    hipLaunchKernelGGL(mfma32_loop_kernel<false>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, out, iters);
+  } else {
+    hipLaunchKernelGGL(mfma32_loop_kernel<true>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, out, iters);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+double bfp8_probe_mfma32_loop_flops(int workgroups, int iters) {
+  return (double)workgroups * 8.0 * (double)iters * kChains32 * 2.0 * 32 * 32 * 64;
 }
 
 int bfp8_probe_stream_read(const void* src, size_t bytes, uint32_t* out, int workgroups, void* stream) {

@@ -32,6 +32,17 @@ int bfp8_probe_mfma_loop(float* out, int workgroups, int iters, int mode, void* 
 double bfp8_probe_mfma_loop_flops(int workgroups, int iters);
 
 /*
+ * The same loop with 4 independent 32x32x64 e4m3 MFMAs per step (gfx950
+ * v_mfma_f32_32x32x64_f8f6f4, whose K of 64 is one group of the 1x64 layout). mode 0: each MFMA
+ * accumulates into its chain; mode 1: each starts from a zero accumulator and its 16 results are
+ * scaled into float32 sums with 16 FMAs (the promotion of the 1x64 method). Other modes return 1.
+ */
+int bfp8_probe_mfma32_loop(float* out, int workgroups, int iters, int mode, void* stream);
+
+/* FLOPs of one bfp8_probe_mfma32_loop launch (2 * 32 * 32 * 64 per MFMA). */
+double bfp8_probe_mfma32_loop_flops(int workgroups, int iters);
+
+/*
  * Streaming read of `bytes` bytes (a multiple of 16) at src (16-byte aligned) by `workgroups`
  * workgroups of 256 threads, 16-byte loads, eight in flight per thread, each byte read once.
  * out: workgroups * 256 words (one per thread, so the loads are not dead).

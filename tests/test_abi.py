@@ -353,6 +353,9 @@ def test_probe_library_exports_its_header():
     fake = 1 << 40
     assert pr.bfp8_probe_mfma_loop(fake, 256, 10, 3, None) == 1  # unknown mode
     assert pr.bfp8_probe_mfma_loop(None, 256, 10, 0, None) == 1
+    assert pr.bfp8_probe_mfma32_loop_flops(256, 2000) == 256 * 8 * 2000 * 4 * 2.0 * 32 * 32 * 64
+    assert pr.bfp8_probe_mfma32_loop(fake, 256, 10, 2, None) == 1  # unknown mode
+    assert pr.bfp8_probe_mfma32_loop(None, 256, 10, 0, None) == 1
     assert pr.bfp8_probe_stream_read(fake + 8, 1 << 20, fake, 64, None) == 1  # misaligned source
     assert pr.bfp8_probe_stream_read(fake, 1000, fake, 64, None) == 1  # not whole 16-byte words
     assert pr.bfp8_probe_copy_lds(fake, 3, 64, 8, 1, fake, 1, None) == 1  # groups not a power of two
