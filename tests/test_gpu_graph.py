@@ -109,9 +109,11 @@ def test_graph_linear_noalloc(gpu, m):
     _replays_match_eager(gpu, lambda: bfp8.linear_noalloc(x, wq, ws, out), [out], f"linear_noalloc M={m}")
 
 
-@pytest.mark.parametrize("m", [16, 1000])
-def test_graph_1x64(gpu, m):
-    n, k = 1024, 4160
+# K-split (M = 16, and M = 1000 on 1024 columns), then the tiled kernel on 128 x 128 tiles
+# (M = 1000, 4096 columns) and on 256 x 256 tiles (M = 4096), all with a K tail.
+@pytest.mark.parametrize("m,n", [(16, 1024), (1000, 1024), (1000, 4096), (4096, 4096)])
+def test_graph_1x64(gpu, m, n):
+    k = 4160
     w = workloads.weight_1x64(n, k, seed=48)
     x = workloads.act_uniform(m, k, seed=49).to(gpu)
     wq, ws = bfp8.pad_k(w.q.to(gpu)), w.s.to(gpu)
