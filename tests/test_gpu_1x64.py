@@ -150,3 +150,22 @@ def test_gemm_1x64_schedule_choice(gpu):
     _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, wq.numpy(), ws.numpy(), rows=rows, k_block=64)
     tolerance.compare(bits(c_auto)[rows], ref_bits, mass, k, "gemm_1x64 auto (tiled)", k_block=64)
     tolerance.compare(bits(c_ks)[rows], ref_bits, mass, k, "gemm_1x64 forced K-split", k_block=64)
+
+
+# Output rows that allow only 2-byte (ldc odd) or 8-byte (ldc % 8 == 4) stores, on each tiled
+# shape (128 x 128, 256 x 128, 256 x 256); the columns past N must stay untouched.
+@pytest.mark.parametrize("m", [1000, 2048, 4096])
+@pytest.mark.parametrize("pad", [3, 4])
+def test_gemm_1x64_tiled_padded_output(gpu, m, pad):
+    n, k = 4096, 1040
+    x = workloads.act_uniform(m, k, seed=960 + m)
+    q, s, q_ref, s_ref = _quant_checked(x, gpu, f"padded out {m}x{n}x{k}")
+    wq, ws = _weight(n, k, 961)
+    buf = torch.full((m, n + pad), -7.0, dtype=torch.bfloat16, device=gpu)
+    announce("gemm_1x64 padded output", m, n, k, "ldc", n + pad)
+    bfp8.gemm_1x64(q, s, bfp8.pad_k(wq.to(gpu)), ws.to(gpu), out=buf[:, :n])
+    torch.cuda.synchronize()
+    assert (buf[:, n:] == -7.0).all(), "columns past N were written"
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m + pad).choice(m, 40, replace=False)]))
+    _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, wq.numpy(), ws.numpy(), rows=rows, k_block=64)
+    tolerance.compare(bits(buf[:, :n])[rows], ref_bits, mass, k, f"gemm_1x64 {m}x{n}x{k} ldc {n + pad}", k_block=64)
