@@ -49,6 +49,80 @@ __device__ __forceinline__ v8i mask_group_tail(v8i f, int valid, int h, int kc) 
   return f;
 }
 
+// Output of a wave's WN x WM tile (TN x TM sub-tiles of 32 x 32 in acc). Register v of sub-tile
+// (tn, tm) holds activation row tm 32 + r and weight row tn 32 + 8 (v / 4) + 4 kc + v % 4, so each
+// quad of registers is 4 consecutive outputs of one row. When C's rows allow 16-byte stores, the
+// wave stages 32 activation rows (one sub-tile row) at a time in LDS at `out_lds` as bf16 rows
+// padded by 16 bytes and stores whole row segments of WN * 2 bytes; otherwise it stores 4 outputs
+// per lane straight from the registers.
+template <int WN, int WM>
+__device__ __forceinline__ void store_tile(const GemmArgs& args, const float (&acc)[WN / 32][WM / 32][16],
+                                           uint8_t* out_lds, int m_base, int n_base, int lane) {
+  constexpr int TN = WN / 32, TM = WM / 32;
+  constexpr int kRowBytes = WN * 2 + 16;
+  const int r = lane & 31, kc = lane >> 5;
+  const int M = args.M, N = args.N;
+  const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
+  if (vec16) {
+    constexpr int kLanesPerRow = WN / 8;  // 16 bytes (8 outputs) per lane
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = f32_to_bf16_rne(acc[tn][tm][4 * q]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 1]) << 16);
+          pk.y = f32_to_bf16_rne(acc[tn][tm][4 * q + 2]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(out_lds + r * kRowBytes + (tn * 32 + 8 * q + 4 * kc) * 2) = pk;
+        }
+      // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
+      // wave's accesses in order, and this keeps the compiler from reordering them.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+        const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+        const int seg = lane % kLanesPerRow;
+        const v4i v = *reinterpret_cast<const v4i*>(out_lds + row * kRowBytes + seg * 16);
+        const int m = m_base + tm * 32 + row;
+        const int n = n_base + seg * 8;
+        if (m < M && n < N) {
+          uint16_t* cp = args.c + (int64_t)m * args.ldc + n;
+          if (n + 8 <= N) {
+            *reinterpret_cast<v4i*>(cp) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) cp[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+    return;
+  }
+  const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = m_base + tm * 32 + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n_base + tn * 32 + 8 * q + 4 * kc;
+        if (n < N)
+          store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1],
+                        acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3], nullptr, false);
+      }
+  }
+}
+
 template <int BN, int BM, int WGN, int WGM, int STAGES, bool kTail>
 __global__ __launch_bounds__(WGN * WGM * 64) void gemm_g64_kernel(GemmArgs args) {
   constexpr int kWaves = WGN * WGM;
@@ -300,68 +374,9 @@ __global__ __launch_bounds__(WGN * WGM * 64) void gemm_g64_kernel(GemmArgs args)
   // stages are reused below. No copy is in flight: the last iteration waited for all of them.
   lds_barrier();
 
-  // Output. Register v of sub-tile (tn, tm) holds activation row tm 32 + r and weight row
-  // tn 32 + 8 (v / 4) + 4 kc + v % 4, so each quad of registers is 4 consecutive outputs of one
-  // row. With 16-byte stores allowed, each wave stages its tile in LDS as bf16 rows (padded by
-  // 16 bytes) and stores whole row segments of WN * 2 bytes.
-  const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
-  if (vec16) {
-    constexpr int kRowBytes = WN * 2 + 16;
-    static_assert(kWaves * WM * kRowBytes <= STAGES * kStage, "output staging fits the stages");
-    uint8_t* out_lds = &smem[0][0] + w * (WM * kRowBytes);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 pk;
-          pk.x = f32_to_bf16_rne(acc[tn][tm][4 * q]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 1]) << 16);
-          pk.y = f32_to_bf16_rne(acc[tn][tm][4 * q + 2]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(out_lds + (tm * 32 + r) * kRowBytes + (tn * 32 + 8 * q + 4 * kc) * 2) = pk;
-        }
-    // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
-    // wave's accesses in order, and this keeps the compiler from reordering them.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    constexpr int kLanesPerRow = WN / 8;  // 16 bytes (8 outputs) per lane
-    constexpr int kRowsPerPass = 64 / kLanesPerRow;
-#pragma unroll
-    for (int pass = 0; pass < WM / kRowsPerPass; ++pass) {
-      const int row = pass * kRowsPerPass + lane / kLanesPerRow;
-      const int seg = lane % kLanesPerRow;
-      const v4i v = *reinterpret_cast<const v4i*>(out_lds + row * kRowBytes + seg * 16);
-      const int m = m0 + wm * WM + row;
-      const int n = n0 + wn * WN + seg * 8;
-      if (m < M && n < N) {
-        uint16_t* cp = args.c + (int64_t)m * args.ldc + n;
-        if (n + 8 <= N) {
-          *reinterpret_cast<v4i*>(cp) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n + e < N) cp[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
-        }
-      }
-    }
-    return;
-  }
-  const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int m = m0 + wm * WM + tm * 32 + r;
-    if (m >= M) continue;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + tn * 32 + 8 * q + 4 * kc;
-        if (n < N)
-          store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1],
-                        acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3], nullptr, false);
-      }
-  }
+  // Output, staged in this wave's part of the stages (every wave has finished with them).
+  static_assert(kWaves * 32 * (WN * 2 + 16) <= STAGES * kStage, "output staging fits the stages");
+  store_tile<WN, WM>(args, acc, &smem[0][0] + w * 32 * (WN * 2 + 16), m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 
@@ -554,70 +569,9 @@ __global__ __launch_bounds__(512) void gemm_g64_wide_kernel(GemmArgs args) {
   promote(kSteps - 1, p1c);
   lds_barrier();
 
-  // Output: each wave stages its 128 x 64 tile in LDS, 32 activation rows (one sub-tile row) at
-  // a time as rows of 256 bytes + 16 of padding, and stores whole row segments.
-  const bool vec16 = ((args.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 15) == 0);
-  if (vec16) {
-    constexpr int kRowBytes = WN * 2 + 16;
-    static_assert(kWaves * 32 * kRowBytes <= STAGES * kStage, "output staging fits the stages");
-    uint8_t* out_lds = &smem[0][0] + w * (32 * kRowBytes);
-    constexpr int kLanesPerRow = WN / 8;
-    constexpr int kRowsPerPass = 64 / kLanesPerRow;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 pk;
-          pk.x = f32_to_bf16_rne(acc[tn][tm][4 * q]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 1]) << 16);
-          pk.y = f32_to_bf16_rne(acc[tn][tm][4 * q + 2]) | (f32_to_bf16_rne(acc[tn][tm][4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(out_lds + r * kRowBytes + (tn * 32 + 8 * q + 4 * kc) * 2) = pk;
-        }
-      // The wave's LDS writes are read back by other lanes of the same wave; LDS executes one
-      // wave's accesses in order, and this keeps the compiler from reordering them.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-      for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
-        const int row = pass * kRowsPerPass + lane / kLanesPerRow;
-        const int seg = lane % kLanesPerRow;
-        const v4i v = *reinterpret_cast<const v4i*>(out_lds + row * kRowBytes + seg * 16);
-        const int m = m0 + wm * WM + tm * 32 + row;
-        const int n = n0 + wn * WN + seg * 8;
-        if (m < M && n < N) {
-          uint16_t* cp = args.c + (int64_t)m * args.ldc + n;
-          if (n + 8 <= N) {
-            *reinterpret_cast<v4i*>(cp) = v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n + e < N) cp[e] = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    }
-    return;
-  }
-  const bool vec_ok = ((args.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(args.c) & 7) == 0);
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int m = m0 + wm * WM + tm * 32 + r;
-    if (m >= M) continue;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + tn * 32 + 8 * q + 4 * kc;
-        if (n < N)
-          store_out16x4(args.c + (int64_t)m * args.ldc + n, n, N, vec_ok, acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1],
-                        acc[tn][tm][4 * q + 2], acc[tn][tm][4 * q + 3], nullptr, false);
-      }
-  }
+  // Output, staged in this wave's part of the stages (every wave has finished with them).
+  static_assert(kWaves * 32 * (WN * 2 + 16) <= STAGES * kStage, "output staging fits the stages");
+  store_tile<WN, WM>(args, acc, &smem[0][0] + w * 32 * (WN * 2 + 16), m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 }  // namespace
