@@ -1,7 +1,8 @@
 """GPU parity over seeded random shapes: the automatic schedule and tile choices (K-split or tiled;
 the tiled plans with their column splits and fewest-round shapes; the 1x64 kernel's three tile
-shapes) on ragged M, N and K, each against the oracle on sampled rows, with output rows padded
-so that columns past N can be checked untouched."""
+shapes; the linear layer's one-launch or two-launch path; the grouped GEMM over random expert
+counts) on ragged M, N and K, each against the oracle on sampled rows, with output rows padded
+(or padding rows preset) so that what must stay untouched can be checked."""
 
 import numpy as np
 import pytest
@@ -9,9 +10,9 @@ import torch
 
 import block_scaled_fp8_bfp8_amd as bfp8
 import workloads
-from oracle import quant
+from oracle import linear, quant
 from tests import tolerance
-from tests.gpu_util import announce, bits
+from tests.gpu_util import announce, bits, quant_gpu_checked
 
 pytestmark = pytest.mark.gpu
 
@@ -75,3 +76,65 @@ def test_gemm_1x64_random_shape(gpu, m, n, k):
     _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows=rows, k_block=64)
     hw = tolerance.block_max_mass(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, np.arange(n), 64) if k < 128 else None
     tolerance.compare(bits(out)[rows], ref_bits, mass, k, f"gemm_1x64 random {m}x{n}x{k}", hw_block=hw, k_block=64)
+
+
+def _linear_shapes(count):
+    out = []
+    for _ in range(count):
+        m = int(_RNG.choice([_RNG.integers(1, 9), _RNG.integers(9, 300), _RNG.integers(300, 2500)]))
+        out.append((m, int(_RNG.integers(1, 3000)), int(_RNG.integers(8, 262)) * 16))
+    return out
+
+
+def _grouped_shapes(count):
+    return [(int(_RNG.integers(1, 13)), int(_RNG.integers(1, 2500)), int(_RNG.integers(1, 2049)),
+             int(_RNG.integers(8, 129)) * 16) for _ in range(count)]
+
+
+SHAPES_LINEAR = _linear_shapes(9)
+SHAPES_GROUPED = _grouped_shapes(6)
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES_LINEAR)
+def test_linear_random_shape(gpu, m, n, k):
+    """bf16 activations and a bias: the one-launch path at small M where it pays, else the
+    quantizer and the GEMM."""
+    w = workloads.weight(n, k, seed=n * 13 + k)
+    x = workloads.act_normal_bf16(m, k, seed=m * 17 + k)
+    rng = np.random.default_rng(m + n + k)
+    bias = torch.from_numpy((rng.choice([-1.0, 1.0], n) * np.exp2(rng.uniform(-6, 3, n))).astype(np.float32))
+    bias = bias.to(torch.bfloat16)
+    rows = _rows(m, m * n + k)
+    out_ref, c_ref, q, s = linear.linear_ref(x.float().numpy(), w.q.numpy(), w.s.numpy(), bias=bias.float().numpy(),
+                                             rows=rows)
+    mass = tolerance.masses(q, s, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
+    announce("linear random shape", m, n, k, "fused" if bfp8.linear_fuses(m, n, k) else "two launches")
+    got = bfp8.linear(x.to(gpu), bfp8.pad_k(w.q.to(gpu)), w.s.to(gpu), bias.to(gpu))
+    torch.cuda.synchronize()
+    tolerance.compare_linear(bits(got)[rows], out_ref, c_ref, mass, k, f"linear random {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("groups,tokens,n,k", SHAPES_GROUPED)
+def test_grouped_random_shape(gpu, groups, tokens, n, k):
+    """Random expert counts (some experts empty), 128-row padding; padding rows stay untouched."""
+    counts = workloads.moe_counts(groups, tokens, seed=groups * 31 + tokens)
+    layout = workloads.moe_layout(counts)
+    x = workloads.act_normal_bf16(layout.size, k, seed=tokens + k)
+    x[torch.from_numpy(layout < 0)] = 0
+    weights = [workloads.weight(n, k, seed=n * 7 + k + g) for g in range(groups)]
+    bq = torch.stack([w.q for w in weights])
+    bs = torch.stack([w.s for w in weights])
+    q, s, q_ref, s_ref = quant_gpu_checked(x, gpu, f"grouped random {groups}x{tokens}x{n}x{k}")
+    out = torch.full((layout.size, n), 1536.0, dtype=torch.bfloat16, device=gpu)
+    announce("grouped random shape", groups, tokens, layout.size, n, k)
+    bfp8.grouped_gemm_contiguous(q, s, bfp8.pad_k(bq.to(gpu)), bs.to(gpu), torch.from_numpy(layout).to(gpu), out=out)
+    torch.cuda.synchronize()
+    assert (out[torch.from_numpy(layout < 0).to(gpu)].float() == 1536.0).all(), "padding rows were written"
+    cb = bits(out)
+    rng = np.random.default_rng(groups + n)
+    cols = np.arange(n) if n <= 512 else np.unique(np.concatenate([[0, n - 1], rng.choice(n, 400, replace=False)]))
+    for g in np.unique(layout[layout >= 0]):
+        rows = np.nonzero(layout == g)[0]
+        rows = np.unique(np.concatenate([rows[:1], rows[-1:], rng.choice(rows, min(4, rows.size), replace=False)]))
+        _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, bq[g].numpy(), bs[g].numpy(), rows=rows, cols=cols)
+        tolerance.compare(cb[np.ix_(rows, cols)], ref_bits, mass, k, f"grouped random expert {g} ({n}x{k})")
