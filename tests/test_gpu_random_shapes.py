@@ -1,8 +1,9 @@
 """GPU parity over seeded random shapes: the automatic schedule and tile choices (K-split or tiled;
 the tiled plans with their column splits and fewest-round shapes; the 1x64 kernel's three tile
-shapes; the linear layer's one-launch or two-launch path; the grouped GEMM over random expert
-counts) on ragged M, N and K, each against the oracle on sampled rows, with output rows padded
-(or padding rows preset) so that what must stay untouched can be checked."""
+shapes; the UE8M0 and fp16-output forms; the linear layer's one-launch or two-launch path; the
+grouped GEMM over random expert counts) on ragged M, N and K, each against the oracle on sampled
+rows, with output rows padded (or padding rows preset) so that what must stay untouched can be
+checked."""
 
 import numpy as np
 import pytest
@@ -10,7 +11,7 @@ import torch
 
 import block_scaled_fp8_bfp8_amd as bfp8
 import workloads
-from oracle import linear, quant
+from oracle import f16, gemm, linear, quant, ue8m0
 from tests import tolerance
 from tests.gpu_util import announce, bits, quant_gpu_checked
 
@@ -138,3 +139,46 @@ def test_grouped_random_shape(gpu, groups, tokens, n, k):
         rows = np.unique(np.concatenate([rows[:1], rows[-1:], rng.choice(rows, min(4, rows.size), replace=False)]))
         _, _, ref_bits, mass = tolerance.reference(q_ref, s_ref, bq[g].numpy(), bs[g].numpy(), rows=rows, cols=cols)
         tolerance.compare(cb[np.ix_(rows, cols)], ref_bits, mass, k, f"grouped random expert {g} ({n}x{k})")
+
+
+SHAPES_E8 = [(int(_RNG.choice([_RNG.integers(1, 257), _RNG.integers(257, 4300)])), int(_RNG.integers(1, 4300)),
+              int(_RNG.integers(1, 33)) * 128) for _ in range(6)]
+SHAPES_F16 = _shapes(6)
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES_E8)
+def test_gemm_ue8m0_random_shape(gpu, m, n, k):
+    """UE8M0 scales applied by the hardware-scaled MFMA (K a multiple of 128)."""
+    x = workloads.act_normal_bf16(m, k, seed=m * 19 + k)
+    q, e = bfp8.quant_act_ue8m0(x.to(gpu))
+    q_ref, e_ref = ue8m0.quant_act_ue8m0_ref(x.float().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(e.cpu().contiguous().numpy(), e_ref)
+    w = workloads.weight_ue8m0(n, k, seed=n * 23 + k)
+    buf, out = _padded_out(m, n, gpu)
+    announce("gemm_ue8m0 random shape", m, n, k, "->", bfp8.schedule_for(m, n, k))
+    bfp8.gemm_ue8m0(q, e, w.q.to(gpu), bfp8.ue8m0_scales(w.s.to(gpu)), out=out)
+    torch.cuda.synchronize()
+    assert (buf[:, n:] == -3.0).all(), "columns past N were written"
+    rows = _rows(m, m + n * 3 + k)
+    _, _, ref_bits, mass = tolerance.reference_e8(q_ref, e_ref, w.q.numpy(), w.s.numpy(), rows=rows)
+    tolerance.compare_e8(bits(out)[rows], ref_bits, mass, k, f"gemm_ue8m0 random {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES_F16)
+def test_gemm_f16_random_shape(gpu, m, n, k):
+    """fp16 output."""
+    x = workloads.act_normal_bf16(m, k, seed=m * 29 + k)
+    q, s = bfp8.quant_act(x.to(gpu))
+    q_ref, s_ref = quant.quant_act_ref(x.float().numpy())
+    w = workloads.weight(n, k, seed=n * 37 + k)
+    buf = torch.full((m, n + 5), -3.0, dtype=torch.float16, device=gpu)
+    announce("gemm_f16 random shape", m, n, k, "->", bfp8.schedule_for(m, n, k))
+    bfp8.gemm_f16(q, s, bfp8.pad_k(w.q.to(gpu)), w.s.to(gpu), out=buf[:, :n])
+    torch.cuda.synchronize()
+    assert (buf[:, n:] == -3.0).all(), "columns past N were written"
+    rows = _rows(m, m + n * 5 + k)
+    acc, _ = gemm.gemm_acc_ref(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows=rows)
+    mass = tolerance.masses(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
+    got = buf[:, :n].detach().cpu().view(torch.int16).numpy().view(np.uint16)[rows]
+    tolerance.compare_f16(got, f16.to_bits(acc), mass, k, f"gemm_f16 random {m}x{n}x{k}")
