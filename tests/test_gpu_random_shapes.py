@@ -182,3 +182,35 @@ def test_gemm_f16_random_shape(gpu, m, n, k):
     mass = tolerance.masses(q_ref, s_ref, w.q.numpy(), w.s.numpy(), rows, np.arange(n))
     got = buf[:, :n].detach().cpu().view(torch.int16).numpy().view(np.uint16)[rows]
     tolerance.compare_f16(got, f16.to_bits(acc), mass, k, f"gemm_f16 random {m}x{n}x{k}")
+
+
+def _moe_shapes(count):
+    return [(int(_RNG.integers(1, 300)), int(_RNG.integers(1, 9)), int(_RNG.integers(1, 25)),
+             int(_RNG.integers(1, 5)) * 128, int(_RNG.integers(1, 5)) * 128, float(_RNG.choice([0.0, 0.1])))
+            for _ in range(count)]
+
+
+SHAPES_MOE = _moe_shapes(6)
+
+
+@pytest.mark.parametrize("t,top_k,e,h,i,sent", SHAPES_MOE)
+def test_moe_forward_random_shape(gpu, t, top_k, e, h, i, sent):
+    """The experts forward (dispatch, tokens quantized once, grouped up projection, SwiGLU +
+    quantization, grouped down projection, weighted combine) on random routing (top_k drawn up to
+    8 and clipped to the expert count; with sentinels for experts held elsewhere) against the
+    oracle's forward, with the end-to-end bound of the benchmark-size test: 2^-2 of the down
+    product's absolute mass plus 2 bf16 ulp per element, mean relative error within 2e-3 (the
+    second quantization re-decides codes from up-projection outputs that differ by rounding)."""
+    from tests.test_gpu_moe import _check_forward, _down_mass
+    from oracle import moe
+
+    top_k = min(top_k, e)
+    x = workloads.act_normal_bf16(t, h, seed=t * 41 + h)
+    ids, w = workloads.moe_routing(t, top_k, e, seed=t + e + i, sentinel_frac=sent)
+    wts = workloads.moe_experts(e, h, i, seed=e * 43 + i)
+    announce("moe_forward random shape", t, top_k, e, h, i, sent)
+    y = bfp8.moe_forward(x.to(gpu), ids.to(gpu), w.to(gpu), *(a.to(gpu) for a in wts))
+    torch.cuda.synchronize()
+    ref = moe.moe_forward_ref(x.float().numpy(), ids.numpy(), w.numpy(), *(a.numpy() for a in wts))
+    _check_forward(bits(y), ref, _down_mass(x, ids, w, wts), f"moe random {t}x{top_k}of{e} h{h} i{i}",
+                   mean_bound=2e-3)
