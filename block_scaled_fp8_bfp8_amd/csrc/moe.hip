@@ -80,31 +80,31 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__
     for (int b = 0; b < nblocks; ++b) block_counts[(int64_t)b * E + e] += start[e];
 }
 
-// Row r's expert (-1 on padding and past the last block); every pair_of_row entry starts at -1.
-__global__ __launch_bounds__(256) void moe_fill_kernel(const int32_t* __restrict__ expert_start,
-                                                       const int32_t* __restrict__ expert_count, int E, int64_t rows,
-                                                       int32_t* __restrict__ layout,
-                                                       int32_t* __restrict__ pair_of_row) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  int e = -1;
-  if (r < expert_start[E]) {
-    int lo = 0, hi = E;  // largest lo with expert_start[lo] <= r (expert_start[0] = 0 <= r < expert_start[E])
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (expert_start[mid] <= r) lo = mid;
-      else hi = mid;
+// Workgroup b of the placement: rows [1024 b, 1024 b + 1024) of the layout get their expert (-1 on
+// padding and past the last expert's rows), and the padding rows' pair_of_row entries -1; then, if
+// b < nblocks, the pairs [1024 b, 1024 b + 1024) are placed, each writing its row's pair_of_row
+// entry. A real row's entry is written by its pair alone and a padding row's by the row fill
+// alone, so the two parts need no ordering between workgroups.
+__global__ __launch_bounds__(kPairsPerBlock) void moe_fill_place_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int nblocks, const int32_t* __restrict__ block_base,
+    const int32_t* __restrict__ expert_start, const int32_t* __restrict__ expert_count, int64_t rows,
+    int32_t* __restrict__ layout, int32_t* __restrict__ row_of_pair, int32_t* __restrict__ pair_of_row) {
+  const int64_t r = (int64_t)blockIdx.x * kPairsPerBlock + threadIdx.x;
+  if (r < rows) {
+    int e = -1;
+    if (r < expert_start[E]) {
+      int lo = 0, hi = E;  // largest lo with expert_start[lo] <= r (expert_start[0] = 0 <= r < expert_start[E])
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (expert_start[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      if (r - expert_start[lo] < expert_count[lo]) e = lo;
     }
-    if (r - expert_start[lo] < expert_count[lo]) e = lo;
+    layout[r] = e;
+    if (e < 0) pair_of_row[r] = -1;
   }
-  layout[r] = e;
-  pair_of_row[r] = -1;
-}
-
-__global__ __launch_bounds__(kPairsPerBlock) void moe_place_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
-                                                                    const int32_t* __restrict__ block_base,
-                                                                    int32_t* __restrict__ row_of_pair,
-                                                                    int32_t* __restrict__ pair_of_row) {
+  if ((int)blockIdx.x >= nblocks) return;  // uniform: no pairs here
   extern __shared__ int wave_cnt[];  // kWavesPerBlock x E
   for (int i = threadIdx.x; i < kWavesPerBlock * E; i += kPairsPerBlock) wave_cnt[i] = 0;
   __syncthreads();
@@ -364,13 +364,12 @@ hipError_t launch_moe_dispatch(const int32_t* ids, int64_t S, int E, int align, 
   }
   hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), (size_t)(E + 1) * 4, stream, block_counts,
                      (int)nblocks, E, align, expert_start, expert_count);
-  if (rows > 0) {
-    hipLaunchKernelGGL(moe_fill_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, expert_start,
-                       expert_count, E, rows, layout, pair_of_row);
-  }
-  if (nblocks > 0) {
-    hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)nblocks), dim3(kPairsPerBlock),
-                       (size_t)kWavesPerBlock * E * 4, stream, ids, S, E, block_counts, row_of_pair, pair_of_row);
+  const int64_t row_blocks = (rows + kPairsPerBlock - 1) / kPairsPerBlock;
+  const int64_t grid = nblocks > row_blocks ? nblocks : row_blocks;
+  if (grid > 0) {
+    hipLaunchKernelGGL(moe_fill_place_kernel, dim3((unsigned)grid), dim3(kPairsPerBlock),
+                       (size_t)kWavesPerBlock * E * 4, stream, ids, S, E, (int)nblocks, block_counts, expert_start,
+                       expert_count, rows, layout, row_of_pair, pair_of_row);
   }
   return hipGetLastError();
 }
