@@ -320,13 +320,17 @@ __global__ __launch_bounds__(kSwigluThreads) void swiglu_kernel(const uint16_t* 
 
 // y[t, c .. c+7] = bf16( sum_j bf16(out[row(t, j), c ..] * bf16(w[t, j])) ), float32 sum in
 // order j; a pair without a row adds zero.
+// kWaveToken: the row's chunk count is a multiple of 64, so all lanes of a wave sum for one token;
+// its pair rows and weights are then read once per wave, through the scalar cache.
+template <bool kWaveToken>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ out, int64_t ldo,
                                                           const int32_t* __restrict__ row_of_pair,
                                                           const float* __restrict__ w, int64_t T, int top_k,
                                                           int chunks_per_row, uint16_t* __restrict__ y, int64_t ldy) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= T * chunks_per_row) return;
-  const int64_t t = i / chunks_per_row;
+  int64_t t = i / chunks_per_row;
+  if constexpr (kWaveToken) t = (int64_t)__builtin_amdgcn_readfirstlane((int)t);
   const int c = (int)(i - t * chunks_per_row) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < top_k; ++j) {
@@ -398,8 +402,13 @@ hipError_t launch_moe_combine(const uint16_t* out, int64_t ldo, const int32_t* r
                               int top_k, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int chunks = (int)(H / 8);
   const int64_t n = T * chunks;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out, ldo,
-                     row_of_pair, w, T, top_k, chunks, y, ldy);
+  if (chunks % 64 == 0) {
+    hipLaunchKernelGGL(moe_combine_kernel<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out, ldo,
+                       row_of_pair, w, T, top_k, chunks, y, ldy);
+  } else {
+    hipLaunchKernelGGL(moe_combine_kernel<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out, ldo,
+                       row_of_pair, w, T, top_k, chunks, y, ldy);
+  }
   return hipGetLastError();
 }
 
