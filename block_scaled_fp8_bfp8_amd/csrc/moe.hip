@@ -80,6 +80,51 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__
     for (int b = 0; b < nblocks; ++b) block_counts[(int64_t)b * E + e] += start[e];
 }
 
+// Small dispatches (kMergedMaxBlocks blocks of pairs or fewer, their counters within
+// kMergedMaxCounters) in one workgroup: the per-block histograms in LDS, then the per-block bases,
+// the aligned starts and the totals exactly as moe_count_kernel and moe_offsets_kernel give them.
+constexpr int kMergedMaxBlocks = 16;
+constexpr int kMergedMaxCounters = 8192;
+__global__ __launch_bounds__(1024) void moe_count_offsets_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                                 int nblocks, int align,
+                                                                 int32_t* __restrict__ block_base,
+                                                                 int32_t* __restrict__ expert_start,
+                                                                 int32_t* __restrict__ expert_count) {
+  extern __shared__ int sh[];  // nblocks x E counters, then E + 1 starts
+  int* cnt = sh;
+  int* start = sh + nblocks * E;
+  for (int i = threadIdx.x; i < nblocks * E; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  for (int64_t p = threadIdx.x; p < S; p += blockDim.x) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[(int)(p / kPairsPerBlock) * E + e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nblocks; ++b) {
+      const int c = cnt[b * E + e];
+      cnt[b * E + e] = run;
+      run += c;
+    }
+    expert_count[e] = run;
+    start[e] = (run + align - 1) / align * align;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      const int a = start[e];
+      start[e] = acc;
+      acc += a;
+    }
+    start[E] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) expert_start[e] = start[e];
+  for (int i = threadIdx.x; i < nblocks * E; i += blockDim.x) block_base[i] = cnt[i] + start[i % E];
+}
+
 // Workgroup b of the placement: rows [1024 b, 1024 b + 1024) of the layout get their expert (-1 on
 // padding and past the last expert's rows), and the padding rows' pair_of_row entries -1; then, if
 // b < nblocks, the pairs [1024 b, 1024 b + 1024) are placed, each writing its row's pair_of_row
@@ -362,12 +407,15 @@ hipError_t launch_moe_dispatch(const int32_t* ids, int64_t S, int E, int align, 
                                int32_t* pair_of_row, int32_t* layout, int32_t* expert_start, int32_t* expert_count,
                                int32_t* block_counts, hipStream_t stream) {
   const int64_t nblocks = moe_dispatch_blocks(S);
-  if (nblocks > 0) {
-    hipLaunchKernelGGL(moe_count_kernel, dim3((unsigned)nblocks), dim3(kPairsPerBlock), (size_t)E * 4, stream, ids, S,
-                       E, block_counts);
+  if (nblocks <= kMergedMaxBlocks && nblocks * E <= kMergedMaxCounters) {
+    hipLaunchKernelGGL(moe_count_offsets_kernel, dim3(1), dim3(1024), (size_t)(nblocks * E + E + 1) * 4, stream, ids,
+                       S, E, (int)nblocks, align, block_counts, expert_start, expert_count);
+  } else {
+    hipLaunchKernelGGL(moe_count_kernel, dim3((unsigned)nblocks), dim3(kPairsPerBlock), (size_t)E * 4, stream, ids,
+                       S, E, block_counts);
+    hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), (size_t)(E + 1) * 4, stream, block_counts,
+                       (int)nblocks, E, align, expert_start, expert_count);
   }
-  hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), (size_t)(E + 1) * 4, stream, block_counts,
-                     (int)nblocks, E, align, expert_start, expert_count);
   const int64_t row_blocks = (rows + kPairsPerBlock - 1) / kPairsPerBlock;
   const int64_t grid = nblocks > row_blocks ? nblocks : row_blocks;
   if (grid > 0) {

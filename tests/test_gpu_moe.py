@@ -14,8 +14,12 @@ from tests.gpu_util import announce, bits
 pytestmark = pytest.mark.gpu
 
 
+# Up to 16 blocks of 1024 pairs with at most 8192 block counters the histograms and offsets take one
+# workgroup; (5000, 4, 32) (20 blocks) and (1100, 8, 1024) (9 blocks x 1024 experts) take the
+# two-kernel form, (900, 8, 1024) sits at the counter limit.
 @pytest.mark.parametrize("t,k,e,sent", [(512, 8, 16, 0.0), (700, 6, 64, 0.05), (3, 1, 1, 0.0), (2000, 1, 1024, 0.0),
-                                        (1, 4, 5, 0.5)])
+                                        (1, 4, 5, 0.5), (5000, 4, 32, 0.1), (900, 8, 1024, 0.0),
+                                        (1100, 8, 1024, 0.0)])
 def test_dispatch_layout(gpu, t, k, e, sent):
     ids, _ = workloads.moe_routing(t, k, e, seed=t + e, sentinel_frac=sent)
     announce("moe_dispatch", t, k, e, sent)
