@@ -229,7 +229,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        log(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
+        log(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the library has no multi-GPU path; "
             "run with --gpus 1.")
         return 2
     if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
