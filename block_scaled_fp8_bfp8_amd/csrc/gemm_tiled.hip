@@ -595,9 +595,11 @@ double plan_us(const TiledPlan& p, int64_t K) { return (double)((p.tiles + kCUs 
 
 // Base tile shape: the largest that still gives every CU a workgroup, which trades bytes copied
 // per MFMA (fewer with big tiles) against parallelism. On the N = K = 4096 sweep: 256x256 from
-// M = 4096 (8 waves of 128x64, two LDS stages), 256x128 at M = 2048 (three stages), 128x128 at
-// M = 1024 and 128x64 at M = 512 (8 waves of 64x32 or 32x32, four stages: the fourth stage took
-// M = 512 from 20.1 to 18.2 us, and 8 waves instead of 4 a further 3-6 % at M = 512-1536).
+// M = 4096 (8 waves of 128x64, two LDS stages), 256x128 at M = 2048 (three stages, 16 waves of
+// 64x32: 3 % under 8 waves of 64x64 at M = 2048, 1.6 % at M = 3072), 128x128 at M = 1024 and
+// 128x64 at M = 512 (8 waves of 64x32 or 32x32, four stages: the fourth stage took M = 512 from
+// 20.1 to 18.2 us, and 8 waves instead of 4 a further 3-6 % at M = 512-1536; 16 waves of 32x32 on
+// 128x128 lost 1-3 %).
 TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K) {
   (void)K;
   auto tiles = [&](int bn, int bm) { return (int)(((N + bn - 1) / bn) * ((M + bm - 1) / bm)); };
@@ -637,7 +639,7 @@ hipError_t launch_planned(const GemmArgs& args, const TiledPlan& p, hipStream_t 
     return launch_tiled_cfg<128, 64, 2, 2, 3, 1, false, true>(args, stream);
   }
   if (p.bn == 256 && p.bm == 256) return launch_tiled_cfg<256, 256, 2, 4, 2, 1, false, false>(args, stream);
-  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, false, false>(args, stream);
+  if (p.bn == 256) return launch_tiled_cfg<256, 128, 4, 4, 3, 1, false, false>(args, stream);
   if (p.bm == 128) return launch_tiled_cfg<128, 128, 2, 4, 4, 1, false, false>(args, stream);
   return launch_tiled_cfg<128, 64, 4, 2, 4, 1, false, false>(args, stream);
 }
@@ -716,10 +718,11 @@ hipError_t launch_gemm_tiled(const GemmArgs& args, void* workspace, hipStream_t 
   return launch_planned(a2, l.tail, stream, persistent);
 }
 
-// Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 8 waves of 64 x 64.
+// Grouped: a workgroup stays inside one 128-row block, so 256 x 128 with 16 waves of 64 x 32
+// (8 waves of 64 x 64 with a partial last K block).
 hipError_t launch_grouped_tiled(const GemmArgs& args, hipStream_t stream) {
   if (args.K % kBlock) return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true, true>(args, stream);
-  return launch_tiled_cfg<256, 128, 4, 2, 3, 1, true, false>(args, stream);
+  return launch_tiled_cfg<256, 128, 4, 4, 3, 1, true, false>(args, stream);
 }
 
 }  // namespace bfp8
