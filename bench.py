@@ -127,7 +127,7 @@ def cpu_baseline(rows_cap: int = 8192):
 
 def measure_ceilings(torch, np, dev, stream, graph_time_us) -> dict:
     """Ceilings measured on this device in this run (libbfp8_probes.so):
-      * fp8_mfma_loop_tflops: 256 workgroups of 8 waves (the GEMMs' occupancy, 2 waves per SIMD)
+      * fp8_mfma_loop_tflops: 256 workgroups of 8 waves (the 256x256 GEMM's occupancy, 2 waves per SIMD)
         issuing independent 16x16x128 FP8 MFMAs from registers; fp8_mfma_promote_tflops: the same
         with the four promotion FMAs per MFMA of the float-scale method; fp8_mfma32_loop_tflops and
         fp8_mfma32_promote_tflops: the 32x32x64 MFMA (one 1x64 group) accumulating, or promoted
